@@ -1,0 +1,171 @@
+"""CPU fp64 oracle for absorbed MLA decode (TEST INFRASTRUCTURE).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package. The GPU library never calls it and shares no code with it.
+
+All arrays are numpy. bf16 tensors are passed as their uint16 bit patterns; the C code
+widens them exactly to fp64 and does every step in fp64 (see ``mla_oracle.c`` for the
+steps and the passages of the pages each one follows).
+
+Pins (what each function is checked against) live in ``tests/test_oracle_*.py``.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIBS = {}
+
+_U16P = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+_I32P = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+_F64P = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+
+
+def _lib(mutant=0, path=None):
+    key = (mutant, path)
+    if key in _LIBS:
+        return _LIBS[key]
+    if path is None:
+        path = _build.LIB if mutant == 0 else os.path.join(
+            _build.HERE, "libmla_oracle_mutant%d.so" % mutant)
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build(out=path, mutant=mutant)
+    L = ctypes.CDLL(path)
+    i = ctypes.c_int
+    vp = ctypes.c_void_p
+    L.oracle_decode_absorbed.restype = i
+    L.oracle_decode_absorbed.argtypes = [i] * 8 + [_U16P] * 5 + [_I32P, _I32P, ctypes.c_double,
+                                                                 vp, i, i, _F64P, vp, i]
+    L.oracle_decode_naive.restype = i
+    L.oracle_decode_naive.argtypes = [i] * 8 + [_U16P] * 5 + [_I32P, _I32P, ctypes.c_double,
+                                                              _F64P, vp, i]
+    L.oracle_probs.restype = i
+    L.oracle_probs.argtypes = [i] * 8 + [_U16P] * 4 + [_I32P, _I32P, ctypes.c_double, i, i,
+                                                       _F64P]
+    L.oracle_gather_pages.restype = i
+    L.oracle_gather_pages.argtypes = [i] * 5 + [_U16P, _I32P, _I32P, i, _U16P]
+    L.oracle_mutant.restype = i
+    _LIBS[key] = L
+    return L
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 inputs are passed as uint16 bit patterns, got %s" % a.dtype)
+    return a
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table):
+    B, H, d_n = q_nope.shape
+    d_R = q_rope.shape[2]
+    d_c = W_UK.shape[2]
+    d_v = W_UV.shape[2]
+    page_size = kv_pages.shape[1]
+    if q_rope.shape[:2] != (B, H) or W_UK.shape != (H, d_n, d_c) or W_UV.shape != (H, d_c, d_v) \
+            or kv_pages.shape[2] != d_c + d_R or page_table.shape[0] != B:
+        raise ValueError("inconsistent shapes")
+    return B, H, d_n, d_c, d_R, d_v, page_size, page_table.shape[1]
+
+
+class Oracle:
+    """Handle on one build of the oracle (mutant=0 is the real one)."""
+
+    def __init__(self, mutant=0, path=None):
+        self.L = _lib(mutant, path)
+        self.mutant = self.L.oracle_mutant()
+
+    def decode(self, q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, scale=0.0,
+               pairs=None, n_split=1, threads=0):
+        """Absorbed decode. Returns (out, lse): out [B,H,d_v] fp64 and lse [B,H] fp64, or
+        for an explicit ``pairs`` list of (b,h): out [n,d_v] and lse [n]."""
+        args = [_u16(q_nope), _u16(q_rope), _u16(W_UK), _u16(W_UV), _u16(kv_pages)]
+        dims = _dims(*args, page_table)
+        B, H, d_v = dims[0], dims[1], dims[5]
+        pt, sl = _i32(page_table), _i32(seq_lens)
+        if pairs is None:
+            n, pp = B * H, None
+            out = np.zeros((B, H, d_v))
+            lse = np.zeros((B, H))
+        else:
+            pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+            n, pp = pairs.shape[0], pairs.ctypes.data
+            out = np.zeros((n, d_v))
+            lse = np.zeros((n,))
+        rc = self.L.oracle_decode_absorbed(*dims, *args, pt, sl, float(scale), pp, n,
+                                           int(n_split), out, lse.ctypes.data, int(threads))
+        if rc != 0:
+            raise ValueError("oracle_decode_absorbed failed (%d)" % rc)
+        return out, lse
+
+    def decode_naive(self, q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens,
+                     scale=0.0, threads=0):
+        """Naive decompressed decode (K and V materialised per head). Returns (out, lse)."""
+        args = [_u16(q_nope), _u16(q_rope), _u16(W_UK), _u16(W_UV), _u16(kv_pages)]
+        dims = _dims(*args, page_table)
+        B, H, d_v = dims[0], dims[1], dims[5]
+        out = np.zeros((B, H, d_v))
+        lse = np.zeros((B, H))
+        rc = self.L.oracle_decode_naive(*dims, *args, _i32(page_table), _i32(seq_lens),
+                                        float(scale), out, lse.ctypes.data, int(threads))
+        if rc != 0:
+            raise ValueError("oracle_decode_naive failed (%d)" % rc)
+        return out, lse
+
+    def probs(self, q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, b, h,
+              scale=0.0):
+        """Softmax weights p_t, t < S_b, of one (b,h)."""
+        args = [_u16(q_nope), _u16(q_rope), _u16(W_UK), _u16(W_UV), _u16(kv_pages)]
+        dims = _dims(*args, page_table)
+        sl = _i32(seq_lens)
+        p = np.zeros((int(sl[b]),))
+        rc = self.L.oracle_probs(*dims, args[0], args[1], args[2], args[4], _i32(page_table), sl,
+                                 float(scale), int(b), int(h), p)
+        if rc != 0:
+            raise ValueError("oracle_probs failed (%d)" % rc)
+        return p
+
+    def gather_pages(self, kv_pages, page_table, seq_lens, S_max, d_c):
+        """Logical copy of the paged cache: [B, S_max, d_c+d_R] uint16, zero past S_b."""
+        kv = _u16(kv_pages)
+        pt, sl = _i32(page_table), _i32(seq_lens)
+        B = pt.shape[0]
+        w = kv.shape[2]
+        dst = np.zeros((B, int(S_max), w), dtype=np.uint16)
+        rc = self.L.oracle_gather_pages(B, int(d_c), w - int(d_c), kv.shape[1], pt.shape[1], kv,
+                                        pt, sl, int(S_max), dst)
+        if rc != 0:
+            raise ValueError("oracle_gather_pages failed (%d)" % rc)
+        return dst
+
+
+_DEFAULT = None
+
+
+def default():
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle()
+    return _DEFAULT
+
+
+def decode(*a, **k):
+    return default().decode(*a, **k)
+
+
+def decode_naive(*a, **k):
+    return default().decode_naive(*a, **k)
+
+
+def probs(*a, **k):
+    return default().probs(*a, **k)
+
+
+def gather_pages(*a, **k):
+    return default().gather_pages(*a, **k)
