@@ -1,0 +1,124 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) absorbed MLA decode library, libmla_decode.so.
+ *
+ * The operation (one query token per sequence, one layer):
+ *   For every sequence b and head h, with the sequence's S_b cached tokens t, each stored once
+ *   as [c_KV (d_latent) | k_R (d_rope)] in 64-token pages
+ *     (bhfrc.com/news/60867 S1 cache format, S3 page size 64),
+ *     q_abs[c]   = sum_d q_nope[b,h,d] * W_UK[h,d,c]                    (absorbed query,
+ *                  lpnh.cn/news/2494972 S2.1; bhfrc.com/news/60867 S4 path B)
+ *     s_t        = scale * (q_abs . c_KV[t] + q_rope[b,h] . k_R[t])      (NoPE + RoPE logits)
+ *     p_t        = softmax_t(s_t),  lse = ln sum_t exp(s_t)
+ *     o_lat[c]   = sum_t p_t * c_KV[t][c]                               (values in latent space)
+ *     out[b,h,e] = sum_c o_lat[c] * W_UV[h,c,e]                         (up-projection,
+ *                  lpnh.cn/news/2494972 S2.1 v = c_kv W_uv)
+ *   K and V are never decompressed. k_R is shared by all heads; q_rope and k_R arrive already
+ *   rotated. The default scale is 1/sqrt(d_nope + d_rope) (bhfrc.com/news/60867 S4).
+ *
+ * Supported shapes: (num_heads, d_nope, d_latent, d_rope, d_v) = (128, 128, 512, 64, 128),
+ * the DeepSeek-V2/V3 widths (bhfrc.com/news/60867 S3), and (32, 120, 64, 8, 128), the MHA2MLA
+ * Llama-2-7B attention config (lpnh.cn/news/2494972 S3.2). page_size must be 64.
+ *
+ * Conventions for every entry point:
+ *   - tensors are dense row-major, in device memory, 16-byte aligned; bf16 is stored as its
+ *     16-bit pattern; int32 is native.
+ *   - the caller allocates and owns every buffer, including the workspace. The library
+ *     allocates no device memory, keeps no per-call state, and never synchronises the stream.
+ *     Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *     returns; results are valid once the stream reaches that point.
+ *   - argument errors are reported by the return value before anything is enqueued; a HIP
+ *     launch failure returns MLA_ERR_HIP (details: mla_last_hip_error()).
+ *   - device-resident values are clamped, never trusted: seq_lens[b] is clamped to
+ *     [0, max_pages_per_seq * 64] and page ids to [0, num_pages - 1], so a bad table gives
+ *     wrong numbers, not a memory fault. A sequence with S_b <= 0 gets out = 0, lse = -inf.
+ *   - page-table entries at or past ceil(S_b / 64) and cache slots at or past S_b are never
+ *     read into the result (they may hold anything, including NaN).
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_NULL_ARG = 1,    /* a required pointer is NULL                                */
+    MLA_ERR_BAD_DIMS = 2,    /* a size is out of range or sizes disagree with each other  */
+    MLA_ERR_MISALIGNED = 3,  /* a tensor pointer is not 16-byte aligned                   */
+    MLA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than mla_decode_workspace_bytes */
+    MLA_ERR_UNSUPPORTED = 5, /* head/width combination or page size not built             */
+    MLA_ERR_HIP = 6          /* the HIP runtime reported an error while enqueueing        */
+} mla_status_t;
+
+typedef struct {
+    int32_t batch;             /* B >= 1 sequences, one query token each                    */
+    int32_t num_heads;         /* H                                                        */
+    int32_t d_nope;            /* d_n: NoPE width of a query head                          */
+    int32_t d_latent;          /* d_c: latent width of the cache (c_KV)                    */
+    int32_t d_rope;            /* d_R: decoupled RoPE width (k_R shared by all heads)      */
+    int32_t d_v;               /* value width of a head after W_UV                         */
+    int32_t page_size;         /* tokens per cache page; must be 64                        */
+    int32_t max_pages_per_seq; /* row stride of page_table (>= 1)                          */
+    int32_t num_pages;         /* pages in the kv_pages pool (>= 1)                        */
+    int32_t max_seq_len;       /* host-side bound on every S_b, used to size the work plan;
+                                  <= 0 means max_pages_per_seq * 64                         */
+    float softmax_scale;       /* <= 0 means 1/sqrt(d_nope + d_rope)                        */
+    int32_t num_units;         /* independent streams over the cache (the split plan): the
+                                  tiles of all sequences are dealt to this many units in
+                                  order. 0 = automatic (fills the 256 compute units: 128 for
+                                  the DeepSeek widths, one unit = two work groups; 1024 for
+                                  MHA2MLA, one unit = one wave). At most 65536.            */
+} mla_dims_t;
+
+/* Bytes of scratch a call with these dims needs (pure function of the dims, host only).
+ * Returns 0 when the dims are invalid or unsupported. */
+size_t mla_decode_workspace_bytes(const mla_dims_t* dims);
+
+/*
+ * Absorbed MLA decode (the operation above).
+ *   q_nope     bf16 [B, H, d_nope]
+ *   q_rope     bf16 [B, H, d_rope]                       already rotated
+ *   W_UK       bf16 [H, d_nope, d_latent]
+ *   W_UV       bf16 [H, d_latent, d_v]
+ *   kv_pages   bf16 [num_pages, 64, d_latent + d_rope]   token = [c_KV | k_R]
+ *   page_table int32 [B, max_pages_per_seq]              logical page j of b -> pool page
+ *   seq_lens   int32 [B]                                 S_b, 1 <= S_b <= max_seq_len
+ *   out        bf16 [B, H, d_v]                          written
+ *   lse_out    fp32 [B, H] natural-log LSE of the logits, or NULL
+ *   workspace  device scratch, 256-byte aligned, of at least mla_decode_workspace_bytes(dims)
+ *              bytes; its contents need no initialisation and are garbage afterwards
+ * Inputs are read only; out, lse_out and workspace are the only memory written. Calls that
+ * share a workspace must be ordered on one stream.
+ */
+mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                        const void* W_UK, const void* W_UV, const void* kv_pages,
+                        const int32_t* page_table, const int32_t* seq_lens, void* out,
+                        float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Logical copy of the paged cache, through the same page addressing and LDS staging the
+ * attention kernel uses (a bit-exact test of the page loads).
+ *   dst bf16 [B, S_max, d_latent + d_rope]; row t of sequence b is token t for t < S_b and
+ *   zero for S_b <= t < S_max, where S_max = max_seq_len (or max_pages_per_seq * 64).
+ * Only batch, d_latent, d_rope, page_size, max_pages_per_seq, num_pages and max_seq_len of
+ * dims are used.
+ */
+mla_status_t mla_gather_pages(const mla_dims_t* dims, const void* kv_pages,
+                              const int32_t* page_table, const int32_t* seq_lens, void* dst,
+                              void* stream);
+
+/* Static description of a status code. */
+const char* mla_status_str(mla_status_t status);
+
+/* Text of the last HIP error this library saw on the calling thread ("" if none). */
+const char* mla_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,192 @@
+"""ctypes binding of libmla_decode.so (argument marshalling only).
+
+Every step of the decode runs in the library's HIP kernels; this module checks tensor
+dtypes/shapes/devices, allocates outputs and workspace with torch, and passes raw device
+pointers plus the current HIP stream. If the library is missing the calls raise.
+"""
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_decode.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "mla_decode.h")
+
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL_ARG", 2: "MLA_ERR_BAD_DIMS", 3: "MLA_ERR_MISALIGNED",
+          4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_UNSUPPORTED", 6: "MLA_ERR_HIP"}
+STATUS_CODE = {v: k for k, v in STATUS.items()}
+
+
+class Dims(ctypes.Structure):
+    """Mirror of mla_dims_t."""
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("d_nope", ctypes.c_int32), ("d_latent", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("num_units", ctypes.c_int32)]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, code, text):
+        super().__init__("%s: %s" % (STATUS.get(code, code), text))
+        self.code = code
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded library (loads it on first use; raises if it was not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmla_decode.so is not built (run __graft_entry__.build() or "
+                              "python -m mla_latent_kv_14_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, c_int, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        dp = ctypes.POINTER(Dims)
+        L.mla_decode_workspace_bytes.restype = sz
+        L.mla_decode_workspace_bytes.argtypes = [dp]
+        L.mla_decode.restype = c_int
+        L.mla_decode.argtypes = [dp] + [vp] * 10 + [sz, vp]
+        L.mla_gather_pages.restype = c_int
+        L.mla_gather_pages.argtypes = [dp, vp, vp, vp, vp, vp]
+        L.mla_status_str.restype = ctypes.c_char_p
+        L.mla_status_str.argtypes = [c_int]
+        L.mla_last_hip_error.restype = ctypes.c_char_p
+        L.mla_last_hip_error.argtypes = []
+        _LIB = L
+    return _LIB
+
+
+def header_symbols():
+    """Names of the functions include/mla_decode.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(code):
+    if code != 0:
+        L = lib()
+        text = L.mla_status_str(code).decode()
+        if code == STATUS_CODE["MLA_ERR_HIP"]:
+            text += " (" + L.mla_last_hip_error().decode() + ")"
+        raise MlaError(code, text)
+
+
+def make_dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, max_seq_len=None,
+              softmax_scale=None, num_units=0):
+    B, H, d_n = q_nope.shape
+    d = Dims()
+    d.batch, d.num_heads, d.d_nope = B, H, d_n
+    d.d_latent = W_UK.shape[2]
+    d.d_rope = q_rope.shape[2]
+    d.d_v = W_UV.shape[2]
+    d.page_size = kv_pages.shape[1]
+    d.max_pages_per_seq = page_table.shape[1]
+    d.num_pages = kv_pages.shape[0]
+    d.max_seq_len = int(max_seq_len) if max_seq_len else 0
+    d.softmax_scale = float(softmax_scale) if softmax_scale else 0.0
+    d.num_units = int(num_units)
+    return d
+
+
+def workspace_bytes(dims):
+    return int(lib().mla_decode_workspace_bytes(ctypes.byref(dims)))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _want(t, name, dtype, ndim, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None, lse=None,
+           max_seq_len=None, softmax_scale=None, num_units=0, workspace=None, stream=None,
+           return_lse=False):
+    """Absorbed MLA decode through mla_decode(). Tensors live on one HIP device.
+
+    q_nope bf16 [B,H,d_n], q_rope bf16 [B,H,d_R], W_UK bf16 [H,d_n,d_c], W_UV bf16 [H,d_c,d_v],
+    kv_pages bf16 [P,64,d_c+d_R], page_table int32 [B,max_pages], seq_lens int32 [B].
+    Returns out bf16 [B,H,d_v] (and lse fp32 [B,H] when return_lse).
+    """
+    dev = q_nope.device
+    if dev.type != "cuda":
+        raise ValueError("mla decode runs on a HIP device; got %s" % dev)
+    bf, i32 = torch.bfloat16, torch.int32
+    for t, n, dt, nd in ((q_nope, "q_nope", bf, 3), (q_rope, "q_rope", bf, 3),
+                         (W_UK, "W_UK", bf, 3), (W_UV, "W_UV", bf, 3),
+                         (kv_pages, "kv_pages", bf, 3), (page_table, "page_table", i32, 2),
+                         (seq_lens, "seq_lens", i32, 1)):
+        _want(t, n, dt, nd, dev)
+    dims = make_dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, max_seq_len,
+                     softmax_scale, num_units)
+    B, H, d_v = dims.batch, dims.num_heads, dims.d_v
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=bf, device=dev)
+    else:
+        _want(out, "out", bf, 3, dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _want(lse, "lse", torch.float32, 2, dev)
+    nbytes = workspace_bytes(dims)
+    if nbytes == 0:
+        _check(lib().mla_decode(ctypes.byref(dims), *([ctypes.c_void_p(0)] * 10), 0,
+                                ctypes.c_void_p(0)))
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    code = lib().mla_decode(ctypes.byref(dims), _ptr(q_nope), _ptr(q_rope), _ptr(W_UK),
+                            _ptr(W_UV), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
+                            _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                            _stream(stream, dev))
+    _check(code)
+    return (out, lse) if return_lse else out
+
+
+def gather_pages(kv_pages, page_table, seq_lens, d_latent, max_seq_len=None, stream=None):
+    """Logical copy of the paged cache through the attention kernels' loader (mla_gather_pages).
+    Returns bf16 [B, S_max, d_latent + d_rope], zero past each S_b."""
+    dev = kv_pages.device
+    _want(kv_pages, "kv_pages", torch.bfloat16, 3, dev)
+    _want(page_table, "page_table", torch.int32, 2, dev)
+    _want(seq_lens, "seq_lens", torch.int32, 1, dev)
+    d = Dims()
+    d.batch = page_table.shape[0]
+    d.d_latent = int(d_latent)
+    d.d_rope = kv_pages.shape[2] - int(d_latent)
+    d.page_size = kv_pages.shape[1]
+    d.max_pages_per_seq = page_table.shape[1]
+    d.num_pages = kv_pages.shape[0]
+    d.max_seq_len = int(max_seq_len) if max_seq_len else 0
+    S_max = d.max_seq_len or d.max_pages_per_seq * d.page_size
+    dst = torch.empty((d.batch, S_max, kv_pages.shape[2]), dtype=torch.bfloat16, device=dev)
+    _check(lib().mla_gather_pages(ctypes.byref(d), _ptr(kv_pages), _ptr(page_table),
+                                  _ptr(seq_lens), _ptr(dst), _stream(stream, dev)))
+    return dst
+
+
+def default_scale(d_nope, d_rope):
+    return 1.0 / math.sqrt(d_nope + d_rope)

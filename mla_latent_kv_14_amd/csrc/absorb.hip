@@ -1,0 +1,143 @@
+// K1: absorbed query, q_abs[b,h,c] = sum_d q_nope[b,h,d] * W_UK[h,d,c]
+// (lpnh.cn/news/2494972 S2.1: W_uk folds into the query side; bhfrc.com/news/60867 S4 path B).
+//
+// One work group per (head h, block of CB latent columns). The W_UK block [d_n x CB] is copied
+// to LDS with direct global->LDS loads (32-byte units XOR-swizzled by row so that the
+// transposing reads of four consecutive rows hit distinct banks), then
+//   q_abs^T[c, b] = W_UK[h]^T[c, d] * q_nope^T[d, b]
+// runs on 16x16x32 bf16 MFMA: the W operand comes from transposing LDS reads, the q_nope operand
+// straight from global memory (8 consecutive d per lane), fp32 accumulation, bf16 (RNE) out.
+// The kernel streams 2*H*d_n*d_c bytes of weight once; it is HBM-bound.
+//
+// Block 0 also writes the work plan for the attention kernel (see Plan in device.h).
+#include "device.h"
+#include "kernels.h"
+
+namespace mla {
+
+// off[b] = sum_{b' < b} ceil(S_b' / TT) with S clamped; header {total, per, groups}.
+__device__ void build_plan(const int32_t* __restrict__ seq_lens, int B, int max_pages, int G,
+                           int TT, Plan* __restrict__ plan) {
+  __shared__ int32_t wave_tot[4];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  int32_t* off = plan_off(plan);
+  for (int base = 0; base < B; base += 256) {
+    const int b = base + tid;
+    int n = 0;
+    if (b < B) n = (clamp_len(seq_lens[b], max_pages) + TT - 1) / TT;
+    int x = n;  // inclusive wave scan
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wave; ++w) before += wave_tot[w];
+    if (b < B) off[b] = before + x - n;
+    __syncthreads();
+    if (tid == 0) carry += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int total = carry;
+    int g = G < 1 ? 1 : G;
+    plan->total = total;
+    plan->per = (total + g - 1) / g;
+    plan->groups = g;
+    plan->pad = 0;
+  }
+}
+
+template <int DN, int DC, int CB>
+__global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
+                                                     const uint16_t* __restrict__ W_UK,
+                                                     uint16_t* __restrict__ q_abs, int B, int H,
+                                                     const int32_t* __restrict__ seq_lens,
+                                                     int max_pages, int G, int TT, Plan* plan) {
+  constexpr int DNP = (DN + 31) / 32 * 32;  // contraction padded to the MFMA K of 32
+  constexpr int ROWB = CB * 2;              // LDS bytes per W row
+  constexpr int UNITS = ROWB / 32;          // 32-byte units per row (swizzle period)
+  constexpr int NCHUNK = DN * ROWB / 16;    // 16-byte pieces of the W block
+  static_assert(NCHUNK % 64 == 0, "W block must be whole KiB");
+  static_assert(DN % 8 == 0 && CB % 16 == 0 && DC % CB == 0, "shape");
+  __shared__ __attribute__((aligned(16))) char wt[DNP * ROWB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = DC / CB;
+  const int h = blockIdx.x / nblk, cblk = blockIdx.x % nblk;
+  if (blockIdx.x == 0) build_plan(seq_lens, B, max_pages, G, TT, plan);
+
+  // ---- stage W_UK[h][0:DN][cblk*CB : +CB] in LDS
+  const char* Wg = reinterpret_cast<const char*>(W_UK + (size_t)h * DN * DC + (size_t)cblk * CB);
+  MLA_LDS char* wl = (MLA_LDS char*)wt;
+  for (int k = wave; k < NCHUNK / 64; k += 4) {
+    const int q = k * 64 + lane;
+    const int row = q / (ROWB / 16), p = q % (ROWB / 16);
+    const int lunit = (p >> 1) ^ (row % UNITS);
+    const char* src = Wg + (size_t)row * DC * 2 + lunit * 32 + (p & 1) * 16;
+    load_lds_16(src, wl + k * 1024);
+  }
+  for (int i = DN * ROWB / 16 + tid; i < DNP * ROWB / 16; i += 256)  // zero pad rows
+    *reinterpret_cast<MLA_LDS u32x4*>(wl + i * 16) = u32x4{0, 0, 0, 0};
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // ---- q_abs^T block [CB x B] = W^T [CB x DNP] * q_nope^T [DNP x B]
+  const int G16 = lane >> 4, q16 = lane & 15;
+  const int mblocks = CB / 16, nblocks = (B + 15) / 16;
+  const uint16_t* qn = q_nope + (size_t)h * DN;
+  for (int pair = wave; pair < mblocks * nblocks; pair += 4) {
+    const int mb = pair % mblocks, nb = pair / mblocks;
+    const int b = nb * 16 + q16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DNP / 32; ++ks) {
+      bf16x4 a0, a1;
+      {
+        const int row0 = ks * 32 + 8 * G16 + (q16 >> 2);
+        const int row1 = row0 + 4;
+        const uint32_t o0 = row0 * ROWB + ((mb ^ (row0 % UNITS)) * 32) + 8 * (q16 & 3);
+        const uint32_t o1 = row1 * ROWB + ((mb ^ (row1 % UNITS)) * 32) + 8 * (q16 & 3);
+        a0 = lds_read_tr16(wl, o0);
+        a1 = lds_read_tr16(wl, o1);
+      }
+      bf16x8 bq;
+      const int d0 = ks * 32 + 8 * G16;
+      if (b < B && d0 < DN) {
+        bq = *reinterpret_cast<const bf16x8*>(qn + (size_t)b * H * DN + d0);
+      } else {
+        bq = bf16x8{};
+      }
+      acc = mfma_16x16x32(cat4(a0, a1), bq, acc);
+    }
+    if (b < B) {
+      const int c0 = cblk * CB + mb * 16 + 4 * G16;
+      bf16x4 o = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+      *reinterpret_cast<bf16x4*>(q_abs + ((size_t)b * H + h) * DC + c0) = o;
+    }
+  }
+}
+
+hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* q_abs, int B,
+                         int H, const int32_t* seq_lens, int max_pages, int G, void* plan,
+                         hipStream_t stream) {
+  if (shape == kShapeDeepSeek) {
+    constexpr int DN = 128, DC = 512, CB = 128;
+    absorb_kernel<DN, DC, CB><<<H * (DC / CB), 256, 0, stream>>>(
+        (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H, seq_lens,
+        max_pages, G, kSub, (Plan*)plan);
+  } else {
+    constexpr int DN = 120, DC = 64, CB = 64;
+    absorb_kernel<DN, DC, CB><<<H * (DC / CB), 256, 0, stream>>>(
+        (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H, seq_lens,
+        max_pages, G, kPage, (Plan*)plan);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,171 @@
+// C ABI of libmla_decode.so: argument checks, workspace layout, work plan size and the three
+// launches (absorb -> attention -> combine) on the caller's stream. No allocation, no sync.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "mla_decode.h"
+#include "device.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_hip_err[256] = "";
+
+struct ShapeInfo {
+  int shape, H, DN, DC, DR, DV, TT;  // TT: tokens per plan tile
+};
+
+bool shape_of(const mla_dims_t* d, ShapeInfo* s) {
+  if (d->num_heads == 128 && d->d_nope == 128 && d->d_latent == 512 && d->d_rope == 64 &&
+      d->d_v == 128) {
+    *s = {mla::kShapeDeepSeek, 128, 128, 512, 64, 128, mla::kSub};
+    return true;
+  }
+  if (d->num_heads == 32 && d->d_nope == 120 && d->d_latent == 64 && d->d_rope == 8 &&
+      d->d_v == 128) {
+    *s = {mla::kShapeMha2Mla, 32, 120, 64, 8, 128, mla::kPage};
+    return true;
+  }
+  return false;
+}
+
+// Validates the sizes; fills the shape on success.
+mla_status_t check_dims(const mla_dims_t* d, ShapeInfo* s) {
+  if (!d) return MLA_ERR_NULL_ARG;
+  if (d->batch < 1 || d->batch > (1 << 20) || d->max_pages_per_seq < 1 || d->num_pages < 1 ||
+      d->num_units < 0 || d->num_units > 65536 || d->num_heads < 1 || d->d_nope < 1 ||
+      d->d_latent < 1 || d->d_rope < 1 || d->d_v < 1 || d->page_size < 1)
+    return MLA_ERR_BAD_DIMS;
+  if ((int64_t)d->batch * d->max_pages_per_seq > (int64_t)1 << 29) return MLA_ERR_BAD_DIMS;
+  if ((int64_t)d->max_seq_len > (int64_t)d->max_pages_per_seq * d->page_size)
+    return MLA_ERR_BAD_DIMS;
+  if (d->page_size != mla::kPage) return MLA_ERR_UNSUPPORTED;
+  if (!shape_of(d, s)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+int max_len(const mla_dims_t* d) {
+  return d->max_seq_len > 0 ? d->max_seq_len : d->max_pages_per_seq * d->page_size;
+}
+
+// Plan units sharing the cache stream: tile streams served by two work groups (DeepSeek
+// widths) or single waves (MHA2MLA). The automatic count fills 256 compute units; it is capped
+// by the tiles that can exist so that no unit is sure to be idle.
+int plan_units(const mla_dims_t* d, const ShapeInfo& s) {
+  const int64_t upper = (int64_t)d->batch * ((max_len(d) + s.TT - 1) / s.TT);
+  int64_t g = d->num_units;
+  if (g == 0) g = s.shape == mla::kShapeDeepSeek ? 128 : 256 * mla::kAttnWavesMha2Mla;
+  if (g > upper) g = upper;
+  return g < 1 ? 1 : (int)g;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t plan, q_abs, part_lse, part_o, total;
+};
+
+Layout layout(const mla_dims_t* d, const ShapeInfo& s) {
+  const size_t B = (size_t)d->batch, slots = (size_t)plan_units(d, s) + B;
+  Layout L;
+  L.plan = 0;
+  L.q_abs = align256(sizeof(mla::Plan) + 4 * B);
+  L.part_lse = L.q_abs + align256(B * s.H * s.DC * 2);
+  L.part_o = L.part_lse + align256(slots * s.H * 4);
+  L.total = L.part_o + align256(slots * s.H * s.DC * 2);
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+mla_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  snprintf(g_hip_err, sizeof g_hip_err, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_decode_workspace_bytes(const mla_dims_t* dims) {
+  ShapeInfo s;
+  if (check_dims(dims, &s) != MLA_OK) return 0;
+  return layout(dims, s).total;
+}
+
+mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                        const void* W_UK, const void* W_UV, const void* kv_pages,
+                        const int32_t* page_table, const int32_t* seq_lens, void* out,
+                        float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  ShapeInfo s;
+  mla_status_t st = check_dims(dims, &s);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !q_rope || !W_UK || !W_UV || !kv_pages || !page_table || !seq_lens || !out)
+    return MLA_ERR_NULL_ARG;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(W_UK) || !aligned16(W_UV) ||
+      !aligned16(kv_pages) || !aligned16(page_table) || !aligned16(seq_lens) ||
+      !aligned16(out) || (lse_out && !aligned16(lse_out)) ||
+      (workspace && ((uintptr_t)workspace & 255) != 0))
+    return MLA_ERR_MISALIGNED;
+  const Layout L = layout(dims, s);
+  if (!workspace || workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+
+  const hipStream_t hs = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int B = dims->batch, mp = dims->max_pages_per_seq;
+  const int G = plan_units(dims, s);
+  const float scale = dims->softmax_scale > 0.f ? dims->softmax_scale
+                                                : 1.0f / sqrtf((float)(s.DN + s.DR));
+  const float scale_log2 = scale * mla::kLog2e;
+
+  st = hip_status(mla::launch_absorb(s.shape, q_nope, W_UK, ws + L.q_abs, B, s.H, seq_lens, mp,
+                                     G, ws + L.plan, hs));
+  if (st != MLA_OK) return st;
+  st = hip_status(mla::launch_attention(s.shape, ws + L.q_abs, q_rope, kv_pages, page_table,
+                                        seq_lens, B, mp, dims->num_pages, ws + L.plan, G,
+                                        scale_log2, ws + L.part_o, (float*)(ws + L.part_lse), hs));
+  if (st != MLA_OK) return st;
+  return hip_status(mla::launch_combine(s.shape, ws + L.part_o, (const float*)(ws + L.part_lse),
+                                        ws + L.plan, seq_lens, W_UV, out, lse_out, B, s.H, mp,
+                                        hs));
+}
+
+mla_status_t mla_gather_pages(const mla_dims_t* dims, const void* kv_pages,
+                              const int32_t* page_table, const int32_t* seq_lens, void* dst,
+                              void* stream) {
+  if (!dims) return MLA_ERR_NULL_ARG;
+  if (dims->batch < 1 || dims->max_pages_per_seq < 1 || dims->num_pages < 1 ||
+      (int64_t)dims->batch * dims->max_pages_per_seq > (int64_t)1 << 29 ||
+      (int64_t)dims->max_seq_len > (int64_t)dims->max_pages_per_seq * dims->page_size)
+    return MLA_ERR_BAD_DIMS;
+  if (dims->page_size != mla::kPage) return MLA_ERR_UNSUPPORTED;
+  if (!((dims->d_latent == 512 && dims->d_rope == 64) ||
+        (dims->d_latent == 64 && dims->d_rope == 8)))
+    return MLA_ERR_UNSUPPORTED;
+  if (!kv_pages || !page_table || !seq_lens || !dst) return MLA_ERR_NULL_ARG;
+  if (!aligned16(kv_pages) || !aligned16(page_table) || !aligned16(seq_lens) || !aligned16(dst))
+    return MLA_ERR_MISALIGNED;
+  return hip_status(mla::launch_gather(dims->d_latent, dims->d_rope, kv_pages, page_table,
+                                       seq_lens, dims->batch, dims->max_pages_per_seq,
+                                       dims->num_pages, max_len(dims), dst,
+                                       (hipStream_t)stream));
+}
+
+const char* mla_status_str(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case MLA_ERR_BAD_DIMS: return "sizes out of range or inconsistent";
+    case MLA_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned (workspace: 256)";
+    case MLA_ERR_WORKSPACE: return "workspace missing or smaller than mla_decode_workspace_bytes";
+    case MLA_ERR_UNSUPPORTED: return "head/width combination or page size not supported";
+    case MLA_ERR_HIP: return "HIP runtime error while enqueueing";
+  }
+  return "unknown status";
+}
+
+const char* mla_last_hip_error(void) { return g_hip_err; }
+
+}  // extern "C"

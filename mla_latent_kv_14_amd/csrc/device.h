@@ -1,0 +1,120 @@
+// Device helpers shared by the gfx950 kernels: vector types, MFMA wrappers, LDS access,
+// direct global->LDS loads, and the work plan that spreads the paged cache over work groups.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr int kPage = 64;   // tokens per cache page
+constexpr int kSub = 32;    // tokens per attention sub-tile (half a page)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- MFMA (bf16 in, fp32 acc)
+// 32x32x16: lane l holds A[l%32][8*(l/32)+j], B[8*(l/32)+j][l%32] (j < 8) and
+//           D[8*(r/4) + 4*(l/32) + r%4][l%32] (r < 16).
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x32: lane l holds A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16] (j < 8) and
+//           D[4*(l/16) + r][l%16] (r < 4).
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 32x32x8: lane l holds A[l%32][4*(l/32)+j], B[4*(l/32)+j][l%32] (j < 4), D as 32x32x16.
+__device__ __forceinline__ f32x16 mfma_32x32x8(i16x4 a, i16x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- LDS access
+__device__ __forceinline__ bf16x8 lds_read_b128(const MLA_LDS char* base, uint32_t byte_off) {
+  return *reinterpret_cast<const MLA_LDS bf16x8*>(base + byte_off);
+}
+// Transposing LDS read: within each 16-lane group, lane i receives column i of a 4x16 block of
+// 16-bit values whose row j is given by the 8-byte addresses of lanes 4j..4j+3 of the group.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const MLA_LDS char* base, uint32_t byte_off) {
+  typedef MLA_LDS bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + byte_off));
+}
+__device__ __forceinline__ bf16x8 cat4(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16*l (the whole
+// wave writes one contiguous KiB; the LDS base goes in M0); the global address is per lane.
+// Issued as inline assembly so that the compiler does not guard later LDS reads with a full
+// vmcnt(0) drain: completion is tracked explicitly with wait_vmcnt<N>() before a block_sync().
+__device__ __forceinline__ void load_lds_16(const void* gptr, MLA_LDS void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
+}
+
+// Work-group barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// outstanding global loads (the prefetched tiles stay in flight across the barrier).
+__device__ __forceinline__ void block_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Read of a value that is the same for the whole wave from memory the kernel never writes:
+// through the constant address space it becomes a scalar load (lgkmcnt, not vmcnt).
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Marks a register as used here, so the compiler completes the load that produced it at this
+// point (and knows it is complete afterwards) instead of at its later uses.
+template <typename T>
+__device__ __forceinline__ void settle(const T& v) {
+  asm volatile("" ::"v"(v));
+}
+
+__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2f_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ uint16_t bf16_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+
+// ---------------------------------------------------------------- work plan
+// The cache of all sequences is viewed as one stream of tiles of TT tokens (32 for the DeepSeek
+// widths, 64 for MHA2MLA), sequence after sequence, each sequence starting a new tile. Plan
+// unit g of G owns tiles [g*per, min((g+1)*per, total)). The part of a sequence b that falls in
+// unit g is a segment; its partial result goes to slot b + g, which is unique because the
+// units that touch sequence b form a contiguous range that can share at most its first unit
+// with sequence b-1. So a call needs at most G + B partial slots.
+struct Plan {
+  int32_t total;  // tiles over all sequences
+  int32_t per;    // tiles per plan unit
+  int32_t groups; // G
+  int32_t pad;
+  // followed by int32_t off[B]: first tile of sequence b
+};
+__device__ __forceinline__ const int32_t* plan_off(const Plan* p) {
+  return reinterpret_cast<const int32_t*>(p + 1);
+}
+__device__ __forceinline__ int32_t* plan_off(Plan* p) { return reinterpret_cast<int32_t*>(p + 1); }
+
+// Effective S_b: clamped to what the page table row can address.
+__device__ __forceinline__ int clamp_len(int s, int max_pages) {
+  s = s < 0 ? 0 : s;
+  int cap = max_pages * kPage;
+  return s > cap ? cap : s;
+}
+
+}  // namespace mla

@@ -1,0 +1,35 @@
+// Host-side launch entry points of the gfx950 kernels (implemented in the .hip files).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// The two head/width families the kernels are built for.
+enum Shape : int {
+  kShapeDeepSeek = 0,  // H=128, d_nope=128, d_latent=512, d_rope=64, d_v=128
+  kShapeMha2Mla = 1,   // H=32,  d_nope=120, d_latent=64,  d_rope=8,  d_v=128
+};
+
+// MHA2MLA attention: waves per work group; each wave is one plan unit. (DeepSeek widths: one
+// plan unit is served by two work groups, one per half of the heads.)
+constexpr int kAttnWavesMha2Mla = 4;
+
+hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* q_abs, int B,
+                         int H, const int32_t* seq_lens, int max_pages, int G, void* plan,
+                         hipStream_t stream);
+
+hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, const void* kv,
+                            const int32_t* page_table, const int32_t* seq_lens, int B,
+                            int max_pages, int num_pages, const void* plan, int G,
+                            float scale_log2, void* part_o, float* part_lse, hipStream_t stream);
+
+hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, const void* plan,
+                          const int32_t* seq_lens, const void* W_UV, void* out, float* lse_out,
+                          int B, int H, int max_pages, hipStream_t stream);
+
+hipError_t launch_gather(int d_latent, int d_rope, const void* kv, const int32_t* page_table,
+                         const int32_t* seq_lens, int B, int max_pages, int num_pages, int S_max,
+                         void* dst, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,135 @@
+"""The C-ABI library loads, exports what include/mla_decode.h declares, and rejects bad
+arguments before it enqueues anything. No call here passes validation, so nothing touches a GPU
+(the pointers are placeholders, never dereferenced)."""
+import ctypes
+
+import pytest
+
+import mla_latent_kv_14_amd as M
+from mla_latent_kv_14_amd.binding import STATUS_CODE
+
+EXPECTED = ["mla_decode", "mla_decode_workspace_bytes", "mla_gather_pages",
+            "mla_last_hip_error", "mla_status_str"]
+
+
+def test_header_declares_the_boundary():
+    assert M.header_symbols() == EXPECTED
+
+
+def test_library_exports_every_declared_symbol():
+    L = M.lib()
+    for name in M.header_symbols():
+        assert getattr(L, name) is not None
+
+
+def ds_dims(B=16, max_pages=64, num_pages=1024, max_seq_len=4096, units=0):
+    d = M.Dims()
+    d.batch, d.num_heads, d.d_nope, d.d_latent, d.d_rope, d.d_v = B, 128, 128, 512, 64, 128
+    d.page_size, d.max_pages_per_seq, d.num_pages = 64, max_pages, num_pages
+    d.max_seq_len, d.softmax_scale, d.num_units = max_seq_len, 0.0, units
+    return d
+
+
+def m2_dims(B=32, max_pages=512, num_pages=16384, max_seq_len=32768, units=0):
+    d = ds_dims(B, max_pages, num_pages, max_seq_len, units)
+    d.num_heads, d.d_nope, d.d_latent, d.d_rope, d.d_v = 32, 120, 64, 8, 128
+    return d
+
+
+def _al(n=1):
+    return ctypes.c_void_p(0x100000 * n)  # 256-aligned placeholder, never dereferenced
+
+
+def call(d, ptrs=None, ws=None, ws_bytes=None, lse=None):
+    p = ptrs or [_al(i + 1) for i in range(8)]
+    if ws is None:
+        ws = _al(9)
+    if ws_bytes is None:
+        ws_bytes = M.workspace_bytes(d) if M.workspace_bytes(d) else 1 << 40
+    return M.lib().mla_decode(ctypes.byref(d), *p, lse or ctypes.c_void_p(0), ws, ws_bytes,
+                              ctypes.c_void_p(0))
+
+
+def test_workspace_bytes_closed_form():
+    # plan header + offsets, q_abs, per-slot lse, per-slot bf16 partials (slots = units + B)
+    def al(x):
+        return (x + 255) // 256 * 256
+    d = ds_dims()
+    slots = 128 + 16
+    assert M.workspace_bytes(d) == (al(16 + 4 * 16) + al(16 * 128 * 512 * 2) + al(slots * 128 * 4)
+                                    + al(slots * 128 * 512 * 2))
+    d = m2_dims()
+    slots = 1024 + 32
+    assert M.workspace_bytes(d) == (al(16 + 4 * 32) + al(32 * 32 * 64 * 2) + al(slots * 32 * 4)
+                                    + al(slots * 32 * 64 * 2))
+    # units are capped by the tiles that can exist: B=1, S=512 -> 16 tiles of 32 tokens
+    d = ds_dims(B=1, max_pages=8, num_pages=8, max_seq_len=512)
+    assert M.workspace_bytes(d) == al(16 + 4) + al(128 * 512 * 2) + al(17 * 128 * 4) + \
+        al(17 * 128 * 512 * 2)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_heads", 64, "MLA_ERR_UNSUPPORTED"), ("d_latent", 256, "MLA_ERR_UNSUPPORTED"),
+    ("page_size", 16, "MLA_ERR_UNSUPPORTED"), ("batch", 0, "MLA_ERR_BAD_DIMS"),
+    ("max_pages_per_seq", 0, "MLA_ERR_BAD_DIMS"), ("num_pages", 0, "MLA_ERR_BAD_DIMS"),
+    ("max_seq_len", 64 * 64 + 1, "MLA_ERR_BAD_DIMS"), ("num_units", -1, "MLA_ERR_BAD_DIMS"),
+    ("num_units", 65537, "MLA_ERR_BAD_DIMS")])
+def test_bad_dims(field, value, status):
+    d = ds_dims(max_seq_len=0)  # 0: bounded by the page table alone
+    setattr(d, field, value)
+    assert M.workspace_bytes(d) == 0
+    assert call(d) == STATUS_CODE[status]
+
+
+def test_null_dims_and_pointers():
+    assert M.lib().mla_decode(None, *([_al()] * 10), 1 << 30, None) == STATUS_CODE["MLA_ERR_NULL_ARG"]
+    for i in range(8):
+        p = [_al(k + 1) for k in range(8)]
+        p[i] = ctypes.c_void_p(0)
+        assert call(ds_dims(), ptrs=p) == STATUS_CODE["MLA_ERR_NULL_ARG"], i
+
+
+def test_misaligned():
+    for i in range(8):
+        p = [_al(k + 1) for k in range(8)]
+        p[i] = ctypes.c_void_p(0x100008)
+        assert call(ds_dims(), ptrs=p) == STATUS_CODE["MLA_ERR_MISALIGNED"], i
+    assert call(ds_dims(), lse=ctypes.c_void_p(0x100004)) == STATUS_CODE["MLA_ERR_MISALIGNED"]
+    assert call(ds_dims(), ws=ctypes.c_void_p(0x100010)) == STATUS_CODE["MLA_ERR_MISALIGNED"]
+
+
+def test_workspace_too_small_or_missing():
+    d = ds_dims()
+    need = M.workspace_bytes(d)
+    assert call(d, ws_bytes=need - 1) == STATUS_CODE["MLA_ERR_WORKSPACE"]
+    assert call(d, ws=ctypes.c_void_p(0)) == STATUS_CODE["MLA_ERR_WORKSPACE"]
+    d = m2_dims()
+    assert call(d, ws_bytes=M.workspace_bytes(d) - 256) == STATUS_CODE["MLA_ERR_WORKSPACE"]
+
+
+def test_gather_rejects_bad_args():
+    L = M.lib()
+    d = ds_dims()
+    args = [_al(1), _al(2), _al(3), _al(4), ctypes.c_void_p(0)]
+    assert L.mla_gather_pages(None, *args) == STATUS_CODE["MLA_ERR_NULL_ARG"]
+    d.d_latent = 128
+    assert L.mla_gather_pages(ctypes.byref(d), *args) == STATUS_CODE["MLA_ERR_UNSUPPORTED"]
+    d = ds_dims()
+    assert L.mla_gather_pages(ctypes.byref(d), _al(1), _al(2), ctypes.c_void_p(0), _al(4),
+                              ctypes.c_void_p(0)) == STATUS_CODE["MLA_ERR_NULL_ARG"]
+    assert L.mla_gather_pages(ctypes.byref(d), ctypes.c_void_p(0x100002), _al(2), _al(3), _al(4),
+                              ctypes.c_void_p(0)) == STATUS_CODE["MLA_ERR_MISALIGNED"]
+
+
+def test_status_strings():
+    for code in range(7):
+        assert M.lib().mla_status_str(code)
+    assert M.lib().mla_last_hip_error() is not None
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 128, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        M.decode(x, x, x, x, x, torch.zeros(1, 1, dtype=torch.int32),
+                 torch.ones(1, dtype=torch.int32))
