@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark: absorbed MLA decode over a paged latent cache on one MI355X.
+
+A step is one full mla_decode call (absorb -> paged split-KV attention -> combine + W_UV) over
+one batch of synthetic inputs already resident in HBM. The default workload is DeepSeek widths
+(128 heads, 512-d latent + 64-d RoPE, d_nope 128, d_v 128), B = 16 sequences of 4096 tokens in
+64-token pages under a shuffled page table. Distinct input sets (each a full set of queries,
+weights and cache) are rotated so that the working set of consecutive steps exceeds the
+256 MiB Infinity Cache: the timed steps read from HBM ("cold"). A single-set run is reported
+as "warm" next to it.
+
+Prints one JSON line (the contract): metric/value (KV tokens per second), TFLOP/s, GB/s, the
+roofline object of the dominant kernel (paged attention; HIP events recorded on the library's
+stream around that kernel in every timed step) and the fp64 CPU oracle's throughput on the
+host cores (a reported baseline).
+
+Algorithmic work of one call (what the method must move or compute; partials and the
+decompression it avoids excluded):
+  F = 2 B H d_n d_c + 2 H (d_c + d_R) sumS + 2 H d_c sumS + 2 B H d_c d_v
+  Bytes = sumS (d_c + d_R) 2 + 2 H d_c (d_n + d_v) + 2 B H (d_n + d_R) + 2 B H d_v
+          + 4 (B max_pages + B)
+Attention kernel alone: sumS (d_c + d_R) 2 bytes of cache (1152 B per token) plus
+2 B H (d_c + d_R) bytes of queries and 4 (B max_pages + B) bytes of page table and lengths.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode KV-tokens/s + TFLOP/s at B=16 S=4096; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
+MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
+ATTN_SOURCES = ["attn.hip", "paged_tile.h", "device.h"]
+
+
+def algorithmic(inp):
+    B, H = inp["B"], inp["H"]
+    d_n, d_c, d_R, d_v = inp["d_n"], inp["d_c"], inp["d_R"], inp["d_v"]
+    S = int(inp["seq_lens"].sum())
+    mp = inp["max_pages"]
+    flops = 2 * B * H * d_n * d_c + 2 * H * (d_c + d_R) * S + 2 * H * d_c * S + 2 * B * H * d_c * d_v
+    nbytes = (S * (d_c + d_R) * 2 + 2 * H * d_c * (d_n + d_v) + 2 * B * H * (d_n + d_R)
+              + 2 * B * H * d_v + 4 * (B * mp + B))
+    attn_bytes = S * (d_c + d_R) * 2 + 2 * B * H * (d_c + d_R) + 4 * (B * mp + B)
+    attn_flops = 2 * H * (d_c + d_R) * S + 2 * H * d_c * S
+    return dict(sumS=S, flops=flops, bytes=nbytes, attn_bytes=attn_bytes, attn_flops=attn_flops)
+
+
+class Hip:
+    """HIP runtime events via ctypes (timing on the stream the library launches on)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.L.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(t), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(e)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "mla_latent_kv_14_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or None
+    if there is none for this workload or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(workload_name)
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def run(args):
+    import torch
+    import mla_latent_kv_14_amd as M
+    import workloads as W
+
+    lib = M.lib()
+    cfg = W.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = W.config_inputs(args.workload)
+    alg = algorithmic(base)
+    n_sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / alg["bytes"]))
+    sets = []
+    for i in range(n_sets):
+        inp = base if i == 0 else W.config_inputs(args.workload, seed=cfg["seed"] + 1000 * i)
+        sets.append({k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()})
+    d0 = sets[0]
+    dims = M.make_dims(d0["q_nope"], d0["q_rope"], d0["W_UK"], d0["W_UV"], d0["kv_pages"],
+                       d0["page_table"])
+    ws_bytes = M.workspace_bytes(dims)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = [torch.empty((d["B"], d["H"], d["d_v"]), dtype=torch.bfloat16, device=dev)
+            for d in sets]
+    stream = torch.cuda.current_stream(dev)
+    vp = ctypes.c_void_p
+
+    def argv(i):
+        d = sets[i]
+        return [vp(d[k].data_ptr()) for k in ("q_nope", "q_rope", "W_UK", "W_UV", "kv_pages",
+                                               "page_table", "seq_lens")] + \
+            [vp(outs[i].data_ptr()), vp(0), vp(ws.data_ptr()), ctypes.c_size_t(ws_bytes),
+             vp(stream.cuda_stream)]
+    call_args = [argv(i) for i in range(n_sets)]
+    dref = ctypes.byref(dims)
+    hip = Hip()
+    K, Wu = args.steps, args.warmup
+    ev = [[hip.event() for _ in range(4)] for _ in range(K)]
+    ev_arr = [(vp * 4)(*e) for e in ev]
+    nullev = ctypes.POINTER(vp)()
+
+    def step(i, events=nullev):
+        rc = lib.mla_decode_timed(dref, *call_args[i % n_sets], events)
+        if rc != 0:
+            raise RuntimeError("mla_decode failed: %s" % lib.mla_status_str(rc).decode())
+
+    def timed(rotate):
+        for i in range(Wu):
+            step(i if rotate else 0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(i if rotate else 0, ev_arr[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stages = [[hip.ms(e[j], e[j + 1]) for e in ev] for j in range(3)]
+        busy = [hip.ms(e[0], e[3]) for e in ev]
+        return (t1 - t0) / K, [sum(s) / K for s in stages], sum(busy) / K
+
+    sec, stage_ms, busy_ms = timed(rotate=True)
+    warm_sec, warm_stage_ms, warm_busy = timed(rotate=False) if not args.cold_only else (None, None, None)
+
+    attn_s = stage_ms[1] * 1e-3
+    achieved = alg["attn_bytes"] / attn_s / 1e9
+    traffic = measured_traffic(cfg["name"])
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "attn_deepseek_kernel" if cfg["H"] == 128
+                else "attn_mha2mla_kernel", "avg_us": round(stage_ms[1] * 1e3, 2)}
+    call_frac = max(alg["bytes"] / (HBM_PEAK_GBS * 1e9), alg["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / sec
+    res = {
+        "metric": METRIC, "value": round(alg["sumS"] / sec, 1), "unit": "KV-tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wu, "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "batch": cfg["B"], "seq_len": base["seq_lens"].tolist()[0]
+                   if cfg["seq"][0] == "fixed" else "ragged", "kv_tokens": alg["sumS"],
+                   "heads": cfg["H"], "d_nope": cfg["d_n"], "d_latent": cfg["d_c"],
+                   "d_rope": cfg["d_R"], "d_v": cfg["d_v"], "page_size": 64,
+                   "page_table": cfg["layout"], "input_sets_rotated": n_sets},
+        "tflops": round(alg["flops"] / sec / 1e12, 2),
+        "gbps": round(alg["bytes"] / sec / 1e9, 1),
+        "roofline_frac_call": round(call_frac, 4),
+        "gpu_busy_us": round(busy_ms * 1e3, 2),
+        "kernels_us": {"absorb": round(stage_ms[0] * 1e3, 2), "attention": round(stage_ms[1] * 1e3, 2),
+                       "combine": round(stage_ms[2] * 1e3, 2)},
+        "roofline": roofline,
+    }
+    if warm_sec is not None:
+        res["warm"] = {"ms_per_step": round(warm_sec * 1e3, 5),
+                       "value": round(alg["sumS"] / warm_sec, 1),
+                       "kernels_us": {"absorb": round(warm_stage_ms[0] * 1e3, 2),
+                                      "attention": round(warm_stage_ms[1] * 1e3, 2),
+                                      "combine": round(warm_stage_ms[2] * 1e3, 2)}}
+    for e in ev:
+        for x in e:
+            hip.destroy(x)
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(base, alg)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def cpu_baseline(inp, alg):
+    """The fp64 oracle, as it stands, on the host cores: every (b, h) of one input set."""
+    import oracle
+    import workloads as W
+    cores = len(os.sched_getaffinity(0))
+    args = W.oracle_args(inp)
+    t0 = time.perf_counter()
+    oracle.decode(*args, threads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": round(alg["sumS"] / dt, 1), "unit": "KV-tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "all %d (b,h) pairs of one input set of this workload (%d KV tokens), "
+                      "fp64, OpenMP over (b,h); %.2f s wall" % (inp["B"] * inp["H"],
+                                                              alg["sumS"], dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="which workload (2 = B=16, S=4096, the headline)")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = enough to "
+                    "exceed twice the Infinity Cache)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cold-only", action="store_true", help="skip the single-set warm run")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs the decode on a single MI355X and has "
+              "no multi-GPU path (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    print(json.dumps(run(args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

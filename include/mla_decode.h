@@ -100,6 +100,19 @@ mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* 
                         float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode with stage timing: identical work and results, and, when stage_events is not NULL,
+ * records stage_events[i] (hipEvent_t, each may be NULL) on `stream` before the absorb kernel
+ * (i = 0), after it (1), after the attention kernel (2) and after the combine kernel (3), so
+ * the caller can time each kernel with hipEventElapsedTime on the stream the kernels run on.
+ * The events are owned by the caller. Used by the benchmark's roofline measurement.
+ */
+mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                              const void* W_UK, const void* W_UV, const void* kv_pages,
+                              const int32_t* page_table, const int32_t* seq_lens, void* out,
+                              float* lse_out, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* stage_events);
+
+/*
  * Logical copy of the paged cache, through the same page addressing and LDS staging the
  * attention kernel uses (a bit-exact test of the page loads).
  *   dst bf16 [B, S_max, d_latent + d_rope]; row t of sequence b is token t for t < S_b and

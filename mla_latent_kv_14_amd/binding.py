@@ -53,6 +53,8 @@ def lib():
         L.mla_decode_workspace_bytes.argtypes = [dp]
         L.mla_decode.restype = c_int
         L.mla_decode.argtypes = [dp] + [vp] * 10 + [sz, vp]
+        L.mla_decode_timed.restype = c_int
+        L.mla_decode_timed.argtypes = [dp] + [vp] * 10 + [sz, vp, ctypes.POINTER(vp)]
         L.mla_gather_pages.restype = c_int
         L.mla_gather_pages.argtypes = [dp, vp, vp, vp, vp, vp]
         L.mla_status_str.restype = ctypes.c_char_p

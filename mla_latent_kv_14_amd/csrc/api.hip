@@ -95,10 +95,11 @@ size_t mla_decode_workspace_bytes(const mla_dims_t* dims) {
   return layout(dims, s).total;
 }
 
-mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
-                        const void* W_UK, const void* W_UV, const void* kv_pages,
-                        const int32_t* page_table, const int32_t* seq_lens, void* out,
-                        float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                              const void* W_UK, const void* W_UV, const void* kv_pages,
+                              const int32_t* page_table, const int32_t* seq_lens, void* out,
+                              float* lse_out, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* stage_events) {
   ShapeInfo s;
   mla_status_t st = check_dims(dims, &s);
   if (st != MLA_OK) return st;
@@ -119,17 +120,31 @@ mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* 
   const float scale = dims->softmax_scale > 0.f ? dims->softmax_scale
                                                 : 1.0f / sqrtf((float)(s.DN + s.DR));
   const float scale_log2 = scale * mla::kLog2e;
+  auto mark = [&](int i) -> mla_status_t {
+    if (!stage_events || !stage_events[i]) return MLA_OK;
+    return hip_status(hipEventRecord((hipEvent_t)stage_events[i], hs));
+  };
 
+  if ((st = mark(0)) != MLA_OK) return st;
   st = hip_status(mla::launch_absorb(s.shape, q_nope, W_UK, ws + L.q_abs, B, s.H, seq_lens, mp,
                                      G, ws + L.plan, hs));
-  if (st != MLA_OK) return st;
+  if (st != MLA_OK || (st = mark(1)) != MLA_OK) return st;
   st = hip_status(mla::launch_attention(s.shape, ws + L.q_abs, q_rope, kv_pages, page_table,
                                         seq_lens, B, mp, dims->num_pages, ws + L.plan, G,
                                         scale_log2, ws + L.part_o, (float*)(ws + L.part_lse), hs));
+  if (st != MLA_OK || (st = mark(2)) != MLA_OK) return st;
+  st = hip_status(mla::launch_combine(s.shape, ws + L.part_o, (const float*)(ws + L.part_lse),
+                                      ws + L.plan, seq_lens, W_UV, out, lse_out, B, s.H, mp, hs));
   if (st != MLA_OK) return st;
-  return hip_status(mla::launch_combine(s.shape, ws + L.part_o, (const float*)(ws + L.part_lse),
-                                        ws + L.plan, seq_lens, W_UV, out, lse_out, B, s.H, mp,
-                                        hs));
+  return mark(3);
+}
+
+mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                        const void* W_UK, const void* W_UV, const void* kv_pages,
+                        const int32_t* page_table, const int32_t* seq_lens, void* out,
+                        float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode_timed(dims, q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out,
+                          lse_out, workspace, workspace_bytes, stream, nullptr);
 }
 
 mla_status_t mla_gather_pages(const mla_dims_t* dims, const void* kv_pages,

@@ -8,7 +8,7 @@ import pytest
 import mla_latent_kv_14_amd as M
 from mla_latent_kv_14_amd.binding import STATUS_CODE
 
-EXPECTED = ["mla_decode", "mla_decode_workspace_bytes", "mla_gather_pages",
+EXPECTED = ["mla_decode", "mla_decode_timed", "mla_decode_workspace_bytes", "mla_gather_pages",
             "mla_last_hip_error", "mla_status_str"]
 
 
