@@ -233,7 +233,20 @@ def main():
                     "exceed twice the Infinity Cache)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-only", action="store_true", help="skip the single-set warm run")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the decode, run 5 device copies of MIB MiB (a plain copy "
+                         "kernel of known size, used to scale the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the decode on a single MI355X and has "
               "no multi-GPU path (got --gpus %d)" % args.gpus, file=sys.stderr)

@@ -16,8 +16,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmla_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# -amdgpu-mfma-vgpr-form=1: MFMA accumulators live in arch VGPRs, so the attention kernels'
+# loop-carried accumulators are not shuttled between AGPRs and VGPRs around every tile.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -79,8 +79,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
     const int q = k * 64 + lane;
     const int row = q / (ROWB / 16), p = q % (ROWB / 16);
     const int lunit = (p >> 1) ^ (row % UNITS);
-    const char* src = Wg + (size_t)row * DC * 2 + lunit * 32 + (p & 1) * 16;
-    load_lds_16(src, wl + k * 1024);
+    load_lds_16(Wg, (uint32_t)(row * DC * 2 + lunit * 32 + (p & 1) * 16), wl + k * 1024);
   }
   for (int i = DN * ROWB / 16 + tid; i < DNP * ROWB / 16; i += 256)  // zero pad rows
     *reinterpret_cast<MLA_LDS u32x4*>(wl + i * 16) = u32x4{0, 0, 0, 0};

@@ -67,25 +67,39 @@ __device__ __forceinline__ int find_seq(const int32_t* off, int B, int total, in
 // placed 8 ids apart): the cache crosses HBM once and the second read hits that XCD's L2.
 // A work group (4 waves, one per SIMD) streams 32-token tiles (36 KiB) through 4 LDS buffers,
 // 3 in flight, and for its 64 heads computes per tile:
-//   scores  S^T[32 tok x 32 heads] per head block hb (2 per group); the 576-wide contraction is
-//           split between two waves (kh = 0: latent 0..287, kh = 1: latent 288..511 + RoPE),
-//           18 MFMA 32x32x16 each, with the wave's query slice (72 VGPRs) held in registers for
-//           the whole segment. The kh = 1 wave passes its partial scores through LDS.
-//   softmax the kh = 0 wave of a head block finishes the scores (lane = one head x 16 tokens;
-//           one exchange with lane^32 completes the tile max) and writes P (bf16) to LDS.
+//   scores  S^T[32 tok x 32 heads] per head block hb (2 per group). The 576-wide contraction is
+//           split between two waves on 8-chunk boundaries (kh = 0: latent 0..255 + RoPE 0..31,
+//           kh = 1: latent 256..511 + RoPE 32..63): 18 MFMA 32x32x16 each, all 18 operand reads
+//           issued first; the wave's query slice (72 VGPRs) stays in registers for the segment.
+//           The two waves of a head block swap the partial scores of each other's tokens
+//           through LDS.
+//   softmax each wave finishes the scores of 16 of the 32 tokens (lane = one head x 8 tokens)
+//           and writes its half of P (bf16) to LDS. The pair shares a per-head reference max
+//           fixed by the segment's first tile, so no per-tile max exchange is needed; only when
+//           a tile beats the reference by more than 2^64 do the waves agree on a new one and
+//           rescale the accumulator.
 //   values  O[64 heads x 128 latent cols of this wave] += P[64 x 32] * tile[32 x 128 cols],
 //           16 MFMA 32x32x16; the tile is read with transposing LDS reads (contraction over
 //           tokens). Each wave reads only its quarter of the value columns.
+// Two work-group barriers per tile: after the scores (partial scores and a free buffer for the
+// next prefetch) and after the softmax (P and the next tile visible).
 namespace ds {
 constexpr int H = 128, HG = 64, DC = 512, DR = 64, DK = DC + DR, ROWB = DK * 2;
 constexpr int NBUF = 4;
-constexpr int PPITCH = 80;      // bytes per head row of P (32 bf16 + 16 pad: conflict-free reads)
-constexpr int KHALF = DK / 2;   // 288: contraction share of one wave
-constexpr int KSTEPS = KHALF / 16;
+constexpr int PPITCH = 80;   // bytes per head row of P (32 bf16 + 16 pad: conflict-free reads)
+constexpr int KSTEPS = 18;   // score MFMA steps per wave: half of the 576-wide contraction
 using Tile = PagedTile<kSub, ROWB>;
 constexpr int IPW = Tile::INSTR / 4;  // load instructions per wave per tile
-constexpr float kRescale = 8.f;
+constexpr float kRescale = 64.f;      // log2 headroom before the running max must move
 }  // namespace ds
+
+template <int N>
+__device__ __forceinline__ void wait_tiles_after(int tiles_after) {
+  // tile loads complete in order: at most `tiles_after` later tiles (N instructions each) pending
+  if (tiles_after >= 2) wait_vmcnt<2 * N>();
+  else if (tiles_after == 1) wait_vmcnt<N>();
+  else wait_vmcnt<0>();
+}
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
@@ -94,12 +108,16 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
                      const Plan* __restrict__ plan, float scale_log2,
                      uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   using namespace ds;
+  static_assert(NBUF == 4, "wait_tiles_after covers up to 2 later tiles");
   __shared__ __attribute__((aligned(1024))) char lds_tiles[NBUF * Tile::BYTES];
-  __shared__ __attribute__((aligned(16))) float lds_x[2][16][64];  // kh=1 partial scores
+  // partial scores handed to the partner wave: [head block][owner kh][float4 k][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 lds_x[2][2][2][64];
   __shared__ __attribute__((aligned(16))) char lds_p[HG * PPITCH];
   __shared__ __attribute__((aligned(16))) float lds_alpha[HG];
   __shared__ __attribute__((aligned(16))) float lds_invl[HG];
-  __shared__ __attribute__((aligned(16))) int lds_flag[4];
+  __shared__ __attribute__((aligned(16))) float lds_m[2][2][32];  // [hb][kh][head] tile maxima
+  __shared__ __attribute__((aligned(16))) float lds_l[2][32];     // [hb][head] kh=1 row sums
+  __shared__ int lds_flag[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -113,194 +131,243 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
   const int32_t* off = plan_off(plan);
   const int n = u1 - u0;
 
-  Cursor lc;
-  {
-    const int b0 = find_seq(off, B, total, u0);
-    cursor_at(lc, b0, u0 - ld_uniform(off + b0), off, seq_lens, B, total, max_pages);
-  }
-  Cursor cc = lc;
-
   MLA_LDS char* tiles = (MLA_LDS char*)lds_tiles;
   MLA_LDS char* pbuf = (MLA_LDS char*)lds_p;
 
-  auto issue = [&](const Cursor& c, int buf) {
-    const char* base =
-        Tile::tile_base(kv, page_table + (size_t)c.b * max_pages, c.j, num_pages);
-    const int valid = min(kSub, c.S - c.j * kSub);
-    Tile::issue<4>(base, valid, tiles + buf * Tile::BYTES, wave, lane);
-  };
-
   const int t32 = lane & 31, hi = lane >> 5;
   const int hb = wave & 1, kh = wave >> 1;
-  const int hloc = 32 * hb + t32;       // local head (0..63) whose scores this lane holds
-  const int head = HG * hh + hloc;      // global head
+  const int hloc = 32 * hb + t32;   // local head (0..63) whose scores this lane holds
+  const int head = HG * hh + hloc;  // global head
   const int G16 = lane >> 4, q16 = lane & 15;
 
-  bf16x8 qf[KSTEPS];
-  f32x16 acc[2][4];
-  float m_used = -INFINITY, l_lane = 0.f;
-  // this wave's query slice for sequence b, loads completed here; state reset
-  auto start_segment = [&](int b) {
-    const uint16_t* qa = q_abs + ((size_t)b * H + head) * DC + 8 * hi;
-    const uint16_t* qr = q_rope + ((size_t)b * H + head) * DR + 8 * hi;
+  // lane offsets of this wave's share of a full tile load (instructions wave, wave + 4, ...)
+  uint32_t dmo[IPW];
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) {
-      const int c = KHALF * kh + 16 * st;  // first latent/RoPE index of the step
-      qf[st] = c < DC ? *reinterpret_cast<const bf16x8*>(qa + c)
-                      : *reinterpret_cast<const bf16x8*>(qr + (c - DC));
+  for (int k = 0; k < IPW; ++k) dmo[k] = Tile::src_off(wave + 4 * k, lane, kSub);
+  // score operand: row t32, logical chunk 32*kh + 2*st + hi (st < 16) or 64 + 4*kh + 2*s + hi
+  const int fs = Tile::swz(t32);
+  uint32_t oq[4], orp[2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) oq[s] = t32 * ROWB + 16 * (32 * kh + ((2 * s + hi) ^ fs));
+#pragma unroll
+  for (int s = 0; s < 2; ++s) orp[s] = t32 * ROWB + 16 * (64 + ((4 * kh + 2 * s + hi) ^ fs));
+  // value operand (transposing reads): rows 16*ks + 8*(G16/2) + 4*hf + q16/4, latent columns
+  // 128*wave + 32*nb + 16*(G16%2) + 4*(q16%4); the swizzle of those rows does not depend on ks
+  uint32_t ov[2][2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int n1 = 0; n1 < 2; ++n1) {
+      const int t = 8 * (G16 >> 1) + 4 * hf + (q16 >> 2);
+      const int low = 4 * n1 + 2 * (G16 & 1) + ((q16 >> 1) & 1);
+      ov[hf][n1] = t * ROWB + 16 * (16 * wave + (low ^ Tile::swz(t))) + 8 * (q16 & 1);
     }
+  const uint32_t pw = hloc * PPITCH + 8 * hi;  // P write: + 16*r4
+  const uint32_t pr = t32 * PPITCH + 16 * hi;  // P read: + 32*PPITCH*mb + 32*ks
+
+  auto issue_tile = [&](const Cursor& c, int buf) {
+    const char* base =
+        Tile::tile_base(kv, page_table + (size_t)c.b * max_pages, c.j, num_pages);
+    Tile::issue<4>(base, min(kSub, c.S - c.j * kSub), dmo, tiles + buf * Tile::BYTES, wave, lane);
+  };
+
+  bf16x8 qf[KSTEPS];
+  auto load_queries = [&](int b) {  // this wave's query slice, loads completed here
+    const uint16_t* qa = q_abs + ((size_t)b * H + head) * DC + 256 * kh + 8 * hi;
+    const uint16_t* qr = q_rope + ((size_t)b * H + head) * DR + 32 * kh + 8 * hi;
+#pragma unroll
+    for (int st = 0; st < 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qa + 16 * st);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) qf[16 + s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) settle(qf[st]);
+  };
+
+  Cursor cc;
+  {
+    const int b0 = find_seq(off, B, total, u0);
+    cursor_at(cc, b0, u0 - ld_uniform(off + b0), off, seq_lens, B, total, max_pages);
+  }
+  load_queries(cc.b);
+  Cursor lc = cc;
+  int issued = 0;
+  for (; issued < NBUF - 1 && issued < n; ++issued) {
+    issue_tile(lc, issued);
+    cursor_next(lc, off, seq_lens, B, total, max_pages);
+  }
+  wait_tiles_after<IPW>(issued - 1);
+  block_sync();
+
+  f32x16 acc[2][4];
+  int it = 0;
+  bool first_segment = true;
+  while (it < n) {
+    const int j0 = cc.j, S = cc.S;
+    const int seg = min(cc.nj - cc.j, n - it);
+    if (!first_segment) load_queries(cc.b);
+    first_segment = false;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
-    m_used = -INFINITY;
-    l_lane = 0.f;
-  };
-  start_segment(cc.b);
-  bool seg_start = false;
+    float m_ref = -INFINITY, l_lane = 0.f;
 
-  int issued = 0;
-  for (; issued < NBUF - 1 && issued < n; ++issued) {
-    issue(lc, issued % NBUF);
-    cursor_next(lc, off, seq_lens, B, total, max_pages);
-  }
-
-  for (int it = 0; it < n; ++it) {
-    if (seg_start) {
-      start_segment(cc.b);
-      seg_start = false;
-    }
-    // tile `it` has landed once at most the later tiles' loads are outstanding
-    const int after = issued - it - 1;
-    if (after >= 2) wait_vmcnt<2 * IPW>();
-    else if (after == 1) wait_vmcnt<IPW>();
-    else wait_vmcnt<0>();
-    block_sync();
-    if (issued < n) {
-      issue(lc, issued % NBUF);
-      cursor_next(lc, off, seq_lens, B, total, max_pages);
-      ++issued;
-    }
-    const MLA_LDS char* kb = tiles + (it % NBUF) * Tile::BYTES;
-
-    // ---- partial scores over this wave's half of the contraction
-    f32x16 s = {};
+    for (int k = 0; k < seg; ++k, ++it) {
+      const MLA_LDS char* kb = tiles + (it % NBUF) * Tile::BYTES;
+      // ---- partial scores over this wave's half of the contraction; operand reads run
+      //      4 steps ahead of the MFMAs
+      auto rd = [&](int st) {
+        return st < 16 ? lds_read_b128(kb, oq[st & 3] + 128 * (st >> 2))
+                       : lds_read_b128(kb, orp[st - 16]);
+      };
+      bf16x8 win[4];
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st)
-      s = mfma_32x32x16(lds_read_b128(kb, Tile::lds_off(t32, 2 * (KSTEPS * kh + st) + hi)),
-                        qf[st], s);
-    if (kh == 1) {
+      for (int st = 0; st < 4; ++st) win[st] = rd(st);
+      f32x16 sc = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) lds_x[hb][r][lane] = s[r];
-    }
-    block_sync();
-
-    // ---- online softmax (log2 domain) by the kh = 0 waves; lane = one head x 16 tokens
-    int need = 0;
-    float alpha = 1.f;
-    if (kh == 0) {
-      const int valid = min(kSub, cc.S - cc.j * kSub);
-      float mt = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 8 * (r >> 2) + 4 * hi + (r & 3);
-        const float v = t < valid ? (s[r] + lds_x[hb][r][lane]) * scale_log2 : -INFINITY;
-        s[r] = v;
-        mt = fmaxf(mt, v);
+      for (int st = 0; st < KSTEPS; ++st) {
+        const bf16x8 cur = win[st & 3];
+        if (st + 4 < KSTEPS) win[st & 3] = rd(st + 4);
+        sc = mfma_32x32x16(cur, qf[st], sc);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      if (m_used == -INFINITY) {
-        m_used = mt;
-      } else if (mt > m_used + kRescale) {
-        alpha = exp2f_fast(m_used - mt);
-        m_used = mt;
-        need = 1;
+      // hand the partner wave the partial scores of its 8 rows (rows 8*kh' .. 8*kh' + 7)
+      {
+        const int o = 8 * (1 - kh);
+        lds_x[hb][1 - kh][0][lane] = f32x4{sc[o + 0], sc[o + 1], sc[o + 2], sc[o + 3]};
+        lds_x[hb][1 - kh][1][lane] = f32x4{sc[o + 4], sc[o + 5], sc[o + 6], sc[o + 7]};
       }
+      block_sync();  // partial scores visible; every wave is done with tile it-1
+      if (issued < n) {
+        issue_tile(lc, issued % NBUF);
+        cursor_next(lc, off, seq_lens, B, total, max_pages);
+        ++issued;
+      }
+      // ---- this wave's 8 rows: r = 8*kh + i, token 16*kh + 8*(i/4) + 4*hi + i%4
+      float v[8];
+      {
+        const f32x4 x0 = lds_x[hb][kh][0][lane], x1 = lds_x[hb][kh][1][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = (sc[8 * kh + i] + x0[i]) * scale_log2;
+          v[4 + i] = (sc[8 * kh + 4 + i] + x1[i]) * scale_log2;
+        }
+      }
+      const int valid = min(kSub, S - (j0 + k) * kSub);
+      if (valid < kSub) {  // last tile of the sequence: slots past its end get no weight
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (16 * kh + 8 * (i >> 2) + 4 * hi + (i & 3) >= valid) v[i] = -INFINITY;
+      }
+      float lm = v[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) lm = fmaxf(lm, v[i]);
+      lm = fmaxf(lm, __shfl_xor(lm, 32, 64));  // this wave's 16 tokens of the head
+      if (k == 0) {  // segment start: the pair agrees on the reference max
+        if (hi == 0) lds_m[hb][kh][t32] = lm;
+        block_sync();
+        m_ref = fmaxf(lds_m[hb][0][t32], lds_m[hb][1][t32]);
+      }
+      const int need = lm > m_ref + kRescale;  // a running max must move (rare)
+      if (lane == 0) lds_flag[wave] = __ballot(need) != 0;
       float lsum = 0.f;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
+      for (int h4 = 0; h4 < 2; ++h4) {
         bf16x4 pv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const __bf16 pb = (__bf16)exp2f_fast(s[4 * r4 + e] - m_used);
+          const __bf16 pb = (__bf16)exp2f_fast(v[4 * h4 + e] - m_ref);
           pv[e] = pb;
           lsum += (float)pb;
         }
-        *reinterpret_cast<MLA_LDS bf16x4*>(pbuf + hloc * PPITCH + (8 * r4 + 4 * hi) * 2) = pv;
+        *reinterpret_cast<MLA_LDS bf16x4*>(pbuf + pw + 32 * kh + 16 * h4) = pv;
       }
-      l_lane = l_lane * alpha + lsum;
-      if (hi == 0) lds_alpha[hloc] = alpha;
-    }
-    if (lane == 0) lds_flag[wave] = __ballot(need) != 0;
-    block_sync();
-    const int any = lds_flag[0] | lds_flag[1] | lds_flag[2] | lds_flag[3];
+      if (it + 1 < n) wait_tiles_after<IPW>(issued - it - 2);  // tile it+1 has landed
+      block_sync();  // P, flags and tile it+1 visible
+      if (lds_flag[0] | lds_flag[1] | lds_flag[2] | lds_flag[3]) {
+        // rare: agree on new reference maxima, recompute this tile's P, rescale accumulators
+        if (hi == 0) lds_m[hb][kh][t32] = lm;
+        block_sync();
+        const float m_new = fmaxf(m_ref, fmaxf(lds_m[hb][0][t32], lds_m[hb][1][t32]));
+        const float alpha = exp2f_fast(m_ref - m_new);
+        m_ref = m_new;
+        lsum = 0.f;
+#pragma unroll
+        for (int h4 = 0; h4 < 2; ++h4) {
+          bf16x4 pv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const __bf16 pb = (__bf16)exp2f_fast(v[4 * h4 + e] - m_ref);
+            pv[e] = pb;
+            lsum += (float)pb;
+          }
+          *reinterpret_cast<MLA_LDS bf16x4*>(pbuf + pw + 32 * kh + 16 * h4) = pv;
+        }
+        l_lane *= alpha;
+        if (kh == 0 && hi == 0) lds_alpha[hloc] = alpha;
+        block_sync();
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 a4 = *reinterpret_cast<const MLA_LDS f32x4*>(
+                (const MLA_LDS char*)lds_alpha + (32 * mb + 8 * r4 + 4 * hi) * 4);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[mb][nb][4 * r4 + e] *= a4[e];
+          }
+        if (lane == 0) lds_flag[wave] = 0;
+        block_sync();
+      }
+      l_lane += lsum;
 
-    // ---- values: O[64 heads][this wave's 128 columns] += P * V
-    if (any) {
+      // ---- values: O[64 heads][this wave's 128 columns] += P * V
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 pa[2], vb[4];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 a4 = *reinterpret_cast<const MLA_LDS f32x4*>(
-              (const MLA_LDS char*)lds_alpha + (32 * mb + 8 * r4 + 4 * hi) * 4);
+        for (int mb = 0; mb < 2; ++mb) pa[mb] = lds_read_b128(pbuf, pr + 32 * PPITCH * mb + 32 * ks);
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[mb][nb][4 * r4 + e] *= a4[e];
+        for (int nb = 0; nb < 4; ++nb) {
+          const uint32_t o = ks * 16 * ROWB + (nb >> 1) * 128;
+          vb[nb] = cat4(lds_read_tr16(kb, ov[0][nb & 1] + o), lds_read_tr16(kb, ov[1][nb & 1] + o));
         }
-    }
 #pragma unroll
-    for (int ks = 0; ks < kSub / 16; ++ks) {
-      bf16x8 pa[2];
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        pa[mb] = lds_read_b128(pbuf, (32 * mb + t32) * PPITCH + (16 * ks + 8 * hi) * 2);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        bf16x4 v2[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int t = 16 * ks + 8 * (G16 >> 1) + 4 * hf + (q16 >> 2);
-          const int c0 = 128 * wave + 32 * nb + 16 * (G16 & 1) + 4 * (q16 & 3);
-          v2[hf] = lds_read_tr16(kb, Tile::lds_off(t, c0 >> 3) + (c0 & 7) * 2);
-        }
-        const bf16x8 vb = cat4(v2[0], v2[1]);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma_32x32x16(pa[mb], vb, acc[mb][nb]);
+          for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma_32x32x16(pa[mb], vb[nb], acc[mb][nb]);
       }
     }
 
     // ---- end of segment: normalised partial and its lse
-    if (it == n - 1 || cc.j == cc.nj - 1) {
-      const int slot = cc.b + g;
-      if (kh == 0) {
-        const float lt = l_lane + __shfl_xor(l_lane, 32, 64);
-        if (hi == 0) {
-          lds_invl[hloc] = 1.f / lt;
-          part_lse[(size_t)slot * H + head] = (m_used + log2f_fast(lt)) * kLn2;
-        }
-      }
-      block_sync();
-      uint16_t* po = part_o + ((size_t)slot * H + HG * hh) * DC;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 il = *reinterpret_cast<const MLA_LDS f32x4*>(
-              (const MLA_LDS char*)lds_invl + (32 * mb + 8 * r4 + 4 * hi) * 4);
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int h = 32 * mb + 8 * r4 + 4 * hi + e;
-              const int c = 128 * wave + 32 * nb + t32;
-              po[(size_t)h * DC + c] = bf16_bits((__bf16)(acc[mb][nb][4 * r4 + e] * il[e]));
-            }
-        }
-      seg_start = true;
+    const int slot = cc.b + g;
+    const float lw = l_lane + __shfl_xor(l_lane, 32, 64);  // this wave's 16 tokens per tile
+    if (kh == 1 && hi == 0) lds_l[hb][t32] = lw;
+    block_sync();
+    if (kh == 0 && hi == 0) {
+      const float lt = lw + lds_l[hb][t32];
+      lds_invl[hloc] = 1.f / lt;
+      part_lse[(size_t)slot * H + head] = (m_ref + log2f_fast(lt)) * kLn2;
     }
+    block_sync();
+    uint16_t* po = part_o + ((size_t)slot * H + HG * hh) * DC;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 il = *reinterpret_cast<const MLA_LDS f32x4*>(
+            (const MLA_LDS char*)lds_invl + (32 * mb + 8 * r4 + 4 * hi) * 4);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int h = 32 * mb + 8 * r4 + 4 * hi + e;
+            const int c = 128 * wave + 32 * nb + t32;
+            po[(size_t)h * DC + c] = bf16_bits((__bf16)(acc[mb][nb][4 * r4 + e] * il[e]));
+          }
+      }
+    // next sequence (the loop ends when the unit's range is used up)
+    cc.j += seg - 1;
     cursor_next(cc, off, seq_lens, B, total, max_pages);
   }
 }
@@ -319,7 +386,7 @@ constexpr int NBUF = 4;
 constexpr int TT = kPage;  // tokens per tile: one page
 using Tile = PagedTile<TT, ROWB>;
 constexpr int IPW = Tile::INSTR;  // the wave issues the whole tile
-constexpr float kRescale = 8.f;
+constexpr float kRescale = 64.f;  // log2 headroom before the running max must move
 }  // namespace m2
 
 __global__ void __launch_bounds__(256)
@@ -348,11 +415,13 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
     cursor_at(lc, b0, u0 - ld_uniform(off + b0), off, seq_lens, B, total, max_pages);
   }
   Cursor cc = lc;
+  uint32_t dmo[IPW];  // lane offsets of a full-tile load
+#pragma unroll
+  for (int k = 0; k < IPW; ++k) dmo[k] = Tile::src_off(k, lane, TT);
   auto issue = [&](const Cursor& c, int buf) {
     const char* base =
         Tile::tile_base(kv, page_table + (size_t)c.b * max_pages, c.j, num_pages);
-    const int valid = min(TT, c.S - c.j * TT);
-    Tile::issue<1>(base, valid, tiles + buf * Tile::BYTES, 0, lane);
+    Tile::issue<1>(base, min(TT, c.S - c.j * TT), dmo, tiles + buf * Tile::BYTES, 0, lane);
   };
 
   const int t32 = lane & 31, hi = lane >> 5;

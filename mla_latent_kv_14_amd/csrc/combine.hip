@@ -42,7 +42,7 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
     const int q = k * 64 + lane;
     const int row = q / (ROWB / 16), p = q % (ROWB / 16);
     const int lunit = (p >> 1) ^ (row % UNITS);
-    load_lds_16(Wg + (size_t)row * DV * 2 + lunit * 32 + (p & 1) * 16, wl + k * 1024);
+    load_lds_16(Wg, (uint32_t)(row * DV * 2 + lunit * 32 + (p & 1) * 16), wl + k * 1024);
   }
 
   const int total = plan->total, per = plan->per;

@@ -51,13 +51,14 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16*l (the whole
-// wave writes one contiguous KiB; the LDS base goes in M0); the global address is per lane.
-// Issued as inline assembly so that the compiler does not guard later LDS reads with a full
-// vmcnt(0) drain: completion is tracked explicitly with wait_vmcnt<N>() before a block_sync().
-__device__ __forceinline__ void load_lds_16(const void* gptr, MLA_LDS void* lds) {
+// Direct global->LDS copy of 16 bytes per lane: lane l reads base + off_l (base uniform, in
+// SGPRs) and its bytes land at lds + 16*l, so the whole wave writes one contiguous KiB (the LDS
+// base goes in M0). Issued as inline assembly so that the compiler does not guard later LDS
+// reads with a full vmcnt(0) drain: completion is tracked explicitly with wait_vmcnt<N>()
+// before a block_sync().
+__device__ __forceinline__ void load_lds_16(const void* base, uint32_t off, MLA_LDS void* lds) {
   const uint32_t m0 = (uint32_t)(uintptr_t)lds;
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 
 // Work-group barrier for LDS traffic only: waits for this wave's LDS operations, not for its

@@ -23,7 +23,10 @@ gather_kernel(const char* __restrict__ kv, const int32_t* __restrict__ page_tabl
   const int valid = min(ROWS, S - j * ROWS);
   if (valid > 0) {
     const char* base = Tile::tile_base(kv, page_table + (size_t)b * max_pages, j, num_pages);
-    Tile::template issue<1>(base, valid, tl, 0, lane);
+    uint32_t offs[Tile::INSTR];
+#pragma unroll
+    for (int k = 0; k < Tile::INSTR; ++k) offs[k] = Tile::src_off(k, lane, ROWS);
+    Tile::template issue<1>(base, valid, offs, tl, 0, lane);
     wait_vmcnt<0>();
   }
   __syncthreads();

@@ -5,11 +5,13 @@
 // block of ROWS*ROWB bytes in global memory. It is copied to LDS with direct global->LDS loads:
 // one wave instruction moves 64 lanes x 16 bytes into one contiguous KiB of LDS, and each lane
 // picks its own global source, which is how the LDS copy gets its layout:
-//   LDS byte offset of 16-byte chunk ch of row r = r*ROWB + 16*swz(r, ch),
-//   swz(r, ch) = ch ^ (r & 7) for ch < SWZ (the whole groups of 8 chunks), ch otherwise.
-// The XOR spreads the same chunk of eight consecutive rows over eight different bank groups,
-// so column reads down a tile (the score MFMA operand) and 4-row transposing reads (the value
-// MFMA operand) do not pile onto one bank.
+//   LDS byte offset of 16-byte chunk ch of row r = r*ROWB + 16*s,
+//   s = (ch & ~7) | ((ch & 7) ^ swz(r)) inside the whole groups of 8 chunks, s = ch past them,
+//   swz(r): m = (r >> 1) & 7, swz = ((m & 3) << 1) | (m >> 2).
+// With 64 four-byte banks served 16 lanes per clock, the XOR makes two read patterns
+// conflict-free: 16 consecutive rows at the same chunk (16-byte reads of the score operand) and
+// 4 consecutive rows x 32 bytes (transposing 8-byte reads of the value operand). Rows of 1152
+// bytes start alternately at bank 0 and bank 32, which the pattern accounts for.
 // Rows at or past `valid` (cache slots past the end of the sequence) are loaded from row
 // valid-1 instead: they hold finite data and their softmax weight is forced to zero.
 #pragma once
@@ -26,9 +28,17 @@ struct PagedTile {
   static_assert(ROWB % 16 == 0 && BYTES % 1024 == 0, "tile must be whole KiB of 16B chunks");
   static_assert(kPage % ROWS == 0, "tile rows must divide the page");
 
+  __device__ static __forceinline__ int swz(int r) {
+    const int m = (r >> 1) & 7;
+    return ((m & 3) << 1) | (m >> 2);
+  }
+  // Position of logical chunk ch of row r (and, the XOR being an involution, the logical chunk
+  // kept at position ch).
+  __device__ static __forceinline__ int chunk_pos(int r, int ch) {
+    return ch < SWZ ? (ch ^ swz(r)) : ch;
+  }
   __device__ static __forceinline__ uint32_t lds_off(int r, int ch) {
-    const int s = ch < SWZ ? (ch ^ (r & 7)) : ch;
-    return (uint32_t)(r * ROWB + s * 16);
+    return (uint32_t)(r * ROWB + chunk_pos(r, ch) * 16);
   }
 
   // Global address of the tile holding logical sub-tile j (ROWS tokens) of a sequence.
@@ -41,19 +51,28 @@ struct PagedTile {
     return kv + (size_t)page * (kPage * ROWB) + (size_t)(j % TPP) * BYTES;
   }
 
-  // Issue this wave's share of the tile: instructions i0 + k*STEP for k < INSTR/STEP.
+  // Byte offset inside the tile that lane `lane` of load instruction i fetches.
+  __device__ static __forceinline__ uint32_t src_off(int i, int lane, int valid) {
+    const int q = i * 64 + lane;
+    const int r = q / NCH, s = q - r * NCH;
+    const int rr = r < valid ? r : valid - 1;
+    return (uint32_t)(rr * ROWB + chunk_pos(r, s) * 16);
+  }
+
+  // Issue this wave's share of the tile: instructions i0 + k*STEP for k < INSTR/STEP. Full tiles
+  // use the precomputed lane offsets `offs`; a tile with fewer valid rows computes them.
   template <int STEP>
-  __device__ static __forceinline__ void issue(const char* base, int valid, MLA_LDS char* lds,
-                                               int i0, int lane) {
+  __device__ static __forceinline__ void issue(const char* base, int valid, const uint32_t* offs,
+                                               MLA_LDS char* lds, int i0, int lane) {
     static_assert(INSTR % STEP == 0, "instructions must split evenly");
+    if (valid >= ROWS) {
 #pragma unroll
-    for (int k = 0; k < INSTR / STEP; ++k) {
-      const int i = i0 + k * STEP;
-      const int q = i * 64 + lane;
-      const int r = q / NCH, s = q - r * NCH;
-      const int ch = s < SWZ ? (s ^ (r & 7)) : s;  // logical chunk kept at LDS position s
-      const int rr = r < valid ? r : valid - 1;
-      load_lds_16(base + rr * ROWB + ch * 16, lds + i * 1024);
+      for (int k = 0; k < INSTR / STEP; ++k)
+        load_lds_16(base, offs[k], lds + (i0 + k * STEP) * 1024);
+    } else {
+#pragma unroll
+      for (int k = 0; k < INSTR / STEP; ++k)
+        load_lds_16(base, src_off(i0 + k * STEP, lane, valid), lds + (i0 + k * STEP) * 1024);
     }
   }
 };
