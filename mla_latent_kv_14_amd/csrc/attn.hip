@@ -65,59 +65,55 @@ __device__ __forceinline__ int find_seq(const int32_t* off, int B, int total, in
 // A tile stream (plan unit) is served by two work groups, one per half of the 128 heads, that
 // sit on the same XCD (work groups are dealt to the 8 XCDs round robin, so the pair is
 // placed 8 ids apart): the cache crosses HBM once and the second read hits that XCD's L2.
-// A work group (4 waves, one per SIMD) streams 32-token tiles (36 KiB) through 4 LDS buffers,
-// 3 in flight, and for its 64 heads computes per tile:
+// A work group has 8 waves (two per SIMD) and streams 32-token tiles (36 KiB) through 3 LDS
+// buffers (2 in flight). For its 64 heads, per tile:
 //   scores  S^T[32 tok x 32 heads] per head block hb (2 per group). The 576-wide contraction is
-//           split between two waves on 8-chunk boundaries (kh = 0: latent 0..255 + RoPE 0..31,
-//           kh = 1: latent 256..511 + RoPE 32..63): 18 MFMA 32x32x16 each, all 18 operand reads
-//           issued first; the wave's query slice (72 VGPRs) stays in registers for the segment.
-//           The two waves of a head block swap the partial scores of each other's tokens
-//           through LDS.
-//   softmax each wave finishes the scores of 16 of the 32 tokens (lane = one head x 8 tokens)
-//           and writes its half of P (bf16) to LDS. The pair shares a per-head reference max
-//           fixed by the segment's first tile, so no per-tile max exchange is needed; only when
-//           a tile beats the reference by more than 2^64 do the waves agree on a new one and
-//           rescale the accumulator.
-//   values  O[64 heads x 128 latent cols of this wave] += P[64 x 32] * tile[32 x 128 cols],
-//           16 MFMA 32x32x16; the tile is read with transposing LDS reads (contraction over
-//           tokens). Each wave reads only its quarter of the value columns.
-// Two work-group barriers per tile: after the scores (partial scores and a free buffer for the
-// next prefetch) and after the softmax (P and the next tile visible).
+//           split over four waves kq on 8-chunk boundaries (latent 128kq..128kq+127 plus RoPE
+//           16kq..16kq+15): 9 MFMA 32x32x16 each with the wave's query slice (36 VGPRs) held
+//           for the segment. Partial scores are summed through LDS: wave kq owns tokens
+//           8kq..8kq+7 and receives the other three partials for them.
+//   softmax each wave turns its 8 tokens of a head (4 per lane) into bf16 weights P in LDS.
+//           The four waves share a per-head reference max fixed on the segment's first tile;
+//           only when a tile beats it by more than 2^64 do they agree on a new one and rescale.
+//   values  O[64 heads x 64 latent cols of this wave] += P[64 x 32] * tile[32 x 64 cols],
+//           8 MFMA 32x32x16, value operand by transposing LDS reads.
+// Two work-group barriers per tile: after the scores (partials visible, the oldest buffer free
+// for the next prefetch) and after the softmax (P and the next tile visible).
 namespace ds {
 constexpr int H = 128, HG = 64, DC = 512, DR = 64, DK = DC + DR, ROWB = DK * 2;
-constexpr int NBUF = 4;
+constexpr int NBUF = 3;
+constexpr int NW = 8;        // waves per work group
 constexpr int PPITCH = 80;   // bytes per head row of P (32 bf16 + 16 pad: conflict-free reads)
-constexpr int KSTEPS = 18;   // score MFMA steps per wave: half of the 576-wide contraction
+constexpr int KSTEPS = 9;    // score MFMA steps per wave: a quarter of the 576-wide contraction
 using Tile = PagedTile<kSub, ROWB>;
-constexpr int IPW = Tile::INSTR / 4;  // load instructions per wave per tile
+constexpr int IPW = Tile::INSTR / 4;  // load instructions per loading wave (waves 0..3)
 constexpr float kRescale = 64.f;      // log2 headroom before the running max must move
 }  // namespace ds
 
 template <int N>
 __device__ __forceinline__ void wait_tiles_after(int tiles_after) {
   // tile loads complete in order: at most `tiles_after` later tiles (N instructions each) pending
-  if (tiles_after >= 2) wait_vmcnt<2 * N>();
-  else if (tiles_after == 1) wait_vmcnt<N>();
+  if (tiles_after >= 1) wait_vmcnt<N>();
   else wait_vmcnt<0>();
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
                      const char* __restrict__ kv, const int32_t* __restrict__ page_table,
                      const int32_t* __restrict__ seq_lens, int B, int max_pages, int num_pages,
                      const Plan* __restrict__ plan, float scale_log2,
                      uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   using namespace ds;
-  static_assert(NBUF == 4, "wait_tiles_after covers up to 2 later tiles");
+  static_assert(NBUF == 3, "wait_tiles_after covers one later tile");
   __shared__ __attribute__((aligned(1024))) char lds_tiles[NBUF * Tile::BYTES];
-  // partial scores handed to the partner wave: [head block][owner kh][float4 k][lane]
-  __shared__ __attribute__((aligned(16))) f32x4 lds_x[2][2][2][64];
+  // partial scores: [head block][owner kq][slot (source kq skipping the owner)][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 lds_x[2][4][3][64];
   __shared__ __attribute__((aligned(16))) char lds_p[HG * PPITCH];
   __shared__ __attribute__((aligned(16))) float lds_alpha[HG];
   __shared__ __attribute__((aligned(16))) float lds_invl[HG];
-  __shared__ __attribute__((aligned(16))) float lds_m[2][2][32];  // [hb][kh][head] tile maxima
-  __shared__ __attribute__((aligned(16))) float lds_l[2][32];     // [hb][head] kh=1 row sums
-  __shared__ int lds_flag[4];
+  __shared__ __attribute__((aligned(16))) float lds_m[2][4][32];  // [hb][kq][head] maxima
+  __shared__ __attribute__((aligned(16))) float lds_l[2][4][32];  // [hb][kq][head] row sums
+  __shared__ int lds_flag[NW];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -135,50 +131,50 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
   MLA_LDS char* pbuf = (MLA_LDS char*)lds_p;
 
   const int t32 = lane & 31, hi = lane >> 5;
-  const int hb = wave & 1, kh = wave >> 1;
+  const int hb = wave & 1, kq = wave >> 1;
   const int hloc = 32 * hb + t32;   // local head (0..63) whose scores this lane holds
   const int head = HG * hh + hloc;  // global head
   const int G16 = lane >> 4, q16 = lane & 15;
+  const bool loader = wave < 4;     // waves 0..3 issue the tile loads, 9 instructions each
 
-  // lane offsets of this wave's share of a full tile load (instructions wave, wave + 4, ...)
   uint32_t dmo[IPW];
 #pragma unroll
-  for (int k = 0; k < IPW; ++k) dmo[k] = Tile::src_off(wave + 4 * k, lane, kSub);
-  // score operand: row t32, logical chunk 32*kh + 2*st + hi (st < 16) or 64 + 4*kh + 2*s + hi
+  for (int k = 0; k < IPW; ++k) dmo[k] = Tile::src_off((wave & 3) + 4 * k, lane, kSub);
+  // score operand: row t32, latent chunks 16kq + 2st + hi (st < 8), RoPE chunk 64 + 2kq + hi
   const int fs = Tile::swz(t32);
-  uint32_t oq[4], orp[2];
+  uint32_t oq[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) oq[s] = t32 * ROWB + 16 * (32 * kh + ((2 * s + hi) ^ fs));
-#pragma unroll
-  for (int s = 0; s < 2; ++s) orp[s] = t32 * ROWB + 16 * (64 + ((4 * kh + 2 * s + hi) ^ fs));
+  for (int s = 0; s < 4; ++s) oq[s] = t32 * ROWB + 16 * (16 * kq + ((2 * s + hi) ^ fs));
+  const uint32_t orp = t32 * ROWB + 16 * (64 + ((2 * kq + hi) ^ fs));
   // value operand (transposing reads): rows 16*ks + 8*(G16/2) + 4*hf + q16/4, latent columns
-  // 128*wave + 32*nb + 16*(G16%2) + 4*(q16%4); the swizzle of those rows does not depend on ks
+  // 64*wave + 32*nb + 16*(G16%2) + 4*(q16%4); the swizzle of those rows does not depend on ks
   uint32_t ov[2][2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int n1 = 0; n1 < 2; ++n1) {
+    for (int nb = 0; nb < 2; ++nb) {
       const int t = 8 * (G16 >> 1) + 4 * hf + (q16 >> 2);
-      const int low = 4 * n1 + 2 * (G16 & 1) + ((q16 >> 1) & 1);
-      ov[hf][n1] = t * ROWB + 16 * (16 * wave + (low ^ Tile::swz(t))) + 8 * (q16 & 1);
+      const int low = 4 * nb + 2 * (G16 & 1) + ((q16 >> 1) & 1);
+      ov[hf][nb] = t * ROWB + 16 * (8 * wave + (low ^ Tile::swz(t))) + 8 * (q16 & 1);
     }
-  const uint32_t pw = hloc * PPITCH + 8 * hi;  // P write: + 16*r4
-  const uint32_t pr = t32 * PPITCH + 16 * hi;  // P read: + 32*PPITCH*mb + 32*ks
+  const uint32_t pw = hloc * PPITCH + 16 * kq + 8 * hi;  // P write: this wave's 4 tokens
+  const uint32_t pr = t32 * PPITCH + 16 * hi;            // P read: + 32*PPITCH*mb + 32*ks
 
   auto issue_tile = [&](const Cursor& c, int buf) {
+    if (!loader) return;
     const char* base =
         Tile::tile_base(kv, page_table + (size_t)c.b * max_pages, c.j, num_pages);
-    Tile::issue<4>(base, min(kSub, c.S - c.j * kSub), dmo, tiles + buf * Tile::BYTES, wave, lane);
+    Tile::issue<4>(base, min(kSub, c.S - c.j * kSub), dmo, tiles + buf * Tile::BYTES,
+                   wave & 3, lane);
   };
 
   bf16x8 qf[KSTEPS];
   auto load_queries = [&](int b) {  // this wave's query slice, loads completed here
-    const uint16_t* qa = q_abs + ((size_t)b * H + head) * DC + 256 * kh + 8 * hi;
-    const uint16_t* qr = q_rope + ((size_t)b * H + head) * DR + 32 * kh + 8 * hi;
+    const uint16_t* qa = q_abs + ((size_t)b * H + head) * DC + 128 * kq + 8 * hi;
+    const uint16_t* qr = q_rope + ((size_t)b * H + head) * DR + 16 * kq + 8 * hi;
 #pragma unroll
-    for (int st = 0; st < 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qa + 16 * st);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) qf[16 + s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
+    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qa + 16 * st);
+    qf[8] = *reinterpret_cast<const bf16x8*>(qr);
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) settle(qf[st]);
   };
@@ -198,7 +194,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
   wait_tiles_after<IPW>(issued - 1);
   block_sync();
 
-  f32x16 acc[2][4];
+  f32x16 acc[2][2];
   int it = 0;
   bool first_segment = true;
   while (it < n) {
@@ -209,32 +205,25 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
     float m_ref = -INFINITY, l_lane = 0.f;
 
     for (int k = 0; k < seg; ++k, ++it) {
       const MLA_LDS char* kb = tiles + (it % NBUF) * Tile::BYTES;
-      // ---- partial scores over this wave's half of the contraction; operand reads run
-      //      4 steps ahead of the MFMAs
-      auto rd = [&](int st) {
-        return st < 16 ? lds_read_b128(kb, oq[st & 3] + 128 * (st >> 2))
-                       : lds_read_b128(kb, orp[st - 16]);
-      };
-      bf16x8 win[4];
+      // ---- partial scores over this wave's quarter of the contraction
+      bf16x8 a[KSTEPS];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) win[st] = rd(st);
+      for (int st = 0; st < 8; ++st) a[st] = lds_read_b128(kb, oq[st & 3] + 128 * (st >> 2));
+      a[8] = lds_read_b128(kb, orp);
       f32x16 sc = {};
 #pragma unroll
-      for (int st = 0; st < KSTEPS; ++st) {
-        const bf16x8 cur = win[st & 3];
-        if (st + 4 < KSTEPS) win[st & 3] = rd(st + 4);
-        sc = mfma_32x32x16(cur, qf[st], sc);
-      }
-      // hand the partner wave the partial scores of its 8 rows (rows 8*kh' .. 8*kh' + 7)
-      {
-        const int o = 8 * (1 - kh);
-        lds_x[hb][1 - kh][0][lane] = f32x4{sc[o + 0], sc[o + 1], sc[o + 2], sc[o + 3]};
-        lds_x[hb][1 - kh][1][lane] = f32x4{sc[o + 4], sc[o + 5], sc[o + 6], sc[o + 7]};
+      for (int st = 0; st < KSTEPS; ++st) sc = mfma_32x32x16(a[st], qf[st], sc);
+      // hand each other wave of the head block the partials of its 4 rows (rows 4q..4q+3)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q == kq) continue;
+        const int slot = q < kq ? kq - 1 : kq;  // this source's slot at owner q
+        lds_x[hb][q][slot][lane] = f32x4{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
       }
       block_sync();  // partial scores visible; every wave is done with tile it-1
       if (issued < n) {
@@ -242,68 +231,62 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         cursor_next(lc, off, seq_lens, B, total, max_pages);
         ++issued;
       }
-      // ---- this wave's 8 rows: r = 8*kh + i, token 16*kh + 8*(i/4) + 4*hi + i%4
-      float v[8];
+      // ---- this wave's rows r = 4kq + e: tokens 8kq + 4hi + e
+      float v[4];
       {
-        const f32x4 x0 = lds_x[hb][kh][0][lane], x1 = lds_x[hb][kh][1][lane];
+        f32x4 t4 = {sc[4 * kq], sc[4 * kq + 1], sc[4 * kq + 2], sc[4 * kq + 3]};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = (sc[8 * kh + i] + x0[i]) * scale_log2;
-          v[4 + i] = (sc[8 * kh + 4 + i] + x1[i]) * scale_log2;
-        }
+        for (int sl = 0; sl < 3; ++sl) t4 += lds_x[hb][kq][sl][lane];
+        const int valid = min(kSub, S - (j0 + k) * kSub);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = 8 * kq + 4 * hi + e < valid ? t4[e] * scale_log2 : -INFINITY;
       }
-      const int valid = min(kSub, S - (j0 + k) * kSub);
-      if (valid < kSub) {  // last tile of the sequence: slots past its end get no weight
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (16 * kh + 8 * (i >> 2) + 4 * hi + (i & 3) >= valid) v[i] = -INFINITY;
-      }
-      float lm = v[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) lm = fmaxf(lm, v[i]);
-      lm = fmaxf(lm, __shfl_xor(lm, 32, 64));  // this wave's 16 tokens of the head
-      if (k == 0) {  // segment start: the pair agrees on the reference max
-        if (hi == 0) lds_m[hb][kh][t32] = lm;
+      float lm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+      lm = fmaxf(lm, __shfl_xor(lm, 32, 64));  // this wave's 8 tokens of the head
+      if (k == 0) {  // segment start: the head block agrees on the reference max
+        if (hi == 0) lds_m[hb][kq][t32] = lm;
         block_sync();
-        m_ref = fmaxf(lds_m[hb][0][t32], lds_m[hb][1][t32]);
+        m_ref = fmaxf(fmaxf(lds_m[hb][0][t32], lds_m[hb][1][t32]),
+                      fmaxf(lds_m[hb][2][t32], lds_m[hb][3][t32]));
       }
       const int need = lm > m_ref + kRescale;  // a running max must move (rare)
       if (lane == 0) lds_flag[wave] = __ballot(need) != 0;
       float lsum = 0.f;
-#pragma unroll
-      for (int h4 = 0; h4 < 2; ++h4) {
+      {
         bf16x4 pv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const __bf16 pb = (__bf16)exp2f_fast(v[4 * h4 + e] - m_ref);
+          const __bf16 pb = (__bf16)exp2f_fast(v[e] - m_ref);
           pv[e] = pb;
           lsum += (float)pb;
         }
-        *reinterpret_cast<MLA_LDS bf16x4*>(pbuf + pw + 32 * kh + 16 * h4) = pv;
+        *reinterpret_cast<MLA_LDS bf16x4*>(pbuf + pw) = pv;
       }
       if (it + 1 < n) wait_tiles_after<IPW>(issued - it - 2);  // tile it+1 has landed
       block_sync();  // P, flags and tile it+1 visible
-      if (lds_flag[0] | lds_flag[1] | lds_flag[2] | lds_flag[3]) {
+      int any = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) any |= lds_flag[w];
+      if (any) {
         // rare: agree on new reference maxima, recompute this tile's P, rescale accumulators
-        if (hi == 0) lds_m[hb][kh][t32] = lm;
+        if (hi == 0) lds_m[hb][kq][t32] = lm;
         block_sync();
-        const float m_new = fmaxf(m_ref, fmaxf(lds_m[hb][0][t32], lds_m[hb][1][t32]));
+        const float m_new = fmaxf(fmaxf(m_ref, fmaxf(lds_m[hb][0][t32], lds_m[hb][1][t32])),
+                                  fmaxf(lds_m[hb][2][t32], lds_m[hb][3][t32]));
         const float alpha = exp2f_fast(m_ref - m_new);
         m_ref = m_new;
         lsum = 0.f;
+        bf16x4 pv;
 #pragma unroll
-        for (int h4 = 0; h4 < 2; ++h4) {
-          bf16x4 pv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const __bf16 pb = (__bf16)exp2f_fast(v[4 * h4 + e] - m_ref);
-            pv[e] = pb;
-            lsum += (float)pb;
-          }
-          *reinterpret_cast<MLA_LDS bf16x4*>(pbuf + pw + 32 * kh + 16 * h4) = pv;
+        for (int e = 0; e < 4; ++e) {
+          const __bf16 pb = (__bf16)exp2f_fast(v[e] - m_ref);
+          pv[e] = pb;
+          lsum += (float)pb;
         }
+        *reinterpret_cast<MLA_LDS bf16x4*>(pbuf + pw) = pv;
         l_lane *= alpha;
-        if (kh == 0 && hi == 0) lds_alpha[hloc] = alpha;
+        if (kq == 0 && hi == 0) lds_alpha[hloc] = alpha;
         block_sync();
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -312,7 +295,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
             const f32x4 a4 = *reinterpret_cast<const MLA_LDS f32x4*>(
                 (const MLA_LDS char*)lds_alpha + (32 * mb + 8 * r4 + 4 * hi) * 4);
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
               for (int e = 0; e < 4; ++e) acc[mb][nb][4 * r4 + e] *= a4[e];
           }
@@ -321,19 +304,18 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
       }
       l_lane += lsum;
 
-      // ---- values: O[64 heads][this wave's 128 columns] += P * V
+      // ---- values: O[64 heads][this wave's 64 columns] += P * V
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 pa[2], vb[4];
+        bf16x8 pa[2], vb[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) pa[mb] = lds_read_b128(pbuf, pr + 32 * PPITCH * mb + 32 * ks);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const uint32_t o = ks * 16 * ROWB + (nb >> 1) * 128;
-          vb[nb] = cat4(lds_read_tr16(kb, ov[0][nb & 1] + o), lds_read_tr16(kb, ov[1][nb & 1] + o));
-        }
+        for (int nb = 0; nb < 2; ++nb)
+          vb[nb] = cat4(lds_read_tr16(kb, ov[0][nb] + ks * 16 * ROWB),
+                        lds_read_tr16(kb, ov[1][nb] + ks * 16 * ROWB));
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma_32x32x16(pa[mb], vb[nb], acc[mb][nb]);
       }
@@ -341,31 +323,47 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
 
     // ---- end of segment: normalised partial and its lse
     const int slot = cc.b + g;
-    const float lw = l_lane + __shfl_xor(l_lane, 32, 64);  // this wave's 16 tokens per tile
-    if (kh == 1 && hi == 0) lds_l[hb][t32] = lw;
+    const float lw = l_lane + __shfl_xor(l_lane, 32, 64);  // this wave's 8 tokens per tile
+    if (hi == 0) lds_l[hb][kq][t32] = lw;
     block_sync();
-    if (kh == 0 && hi == 0) {
-      const float lt = lw + lds_l[hb][t32];
+    if (kq == 0 && hi == 0) {
+      const float lt = lds_l[hb][0][t32] + lds_l[hb][1][t32] + lds_l[hb][2][t32] + lds_l[hb][3][t32];
       lds_invl[hloc] = 1.f / lt;
       part_lse[(size_t)slot * H + head] = (m_ref + log2f_fast(lt)) * kLn2;
     }
     block_sync();
-    uint16_t* po = part_o + ((size_t)slot * H + HG * hh) * DC;
+    // Stage the normalised bf16 partial, 32 heads at a time, in the buffer of the segment's
+    // last tile (no load targets it before the next tile's barrier), then write it out in
+    // 16-byte pieces: rows of 512 latent columns, pitch 1040 bytes.
+    {
+      constexpr int SPITCH = DC * 2 + 16;
+      static_assert(32 * SPITCH <= Tile::BYTES, "staging fits one tile buffer");
+      MLA_LDS char* stg = tiles + ((it - 1) % NBUF) * Tile::BYTES;
+      uint16_t* po = part_o + ((size_t)slot * H + HG * hh) * DC;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 il = *reinterpret_cast<const MLA_LDS f32x4*>(
-            (const MLA_LDS char*)lds_invl + (32 * mb + 8 * r4 + 4 * hi) * 4);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 il = *reinterpret_cast<const MLA_LDS f32x4*>(
+              (const MLA_LDS char*)lds_invl + (32 * mb + 8 * r4 + 4 * hi) * 4);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+          for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int h = 32 * mb + 8 * r4 + 4 * hi + e;
-            const int c = 128 * wave + 32 * nb + t32;
-            po[(size_t)h * DC + c] = bf16_bits((__bf16)(acc[mb][nb][4 * r4 + e] * il[e]));
-          }
+            for (int e = 0; e < 4; ++e)
+              *reinterpret_cast<MLA_LDS __bf16*>(
+                  stg + (8 * r4 + 4 * hi + e) * SPITCH + (64 * wave + 32 * nb + t32) * 2) =
+                  (__bf16)(acc[mb][nb][4 * r4 + e] * il[e]);
+        }
+        block_sync();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {  // 32 rows x 64 pieces of 16 bytes over 512 threads
+          const int q = k * 512 + tid, row = q >> 6, piece = q & 63;
+          *reinterpret_cast<u32x4*>(po + (size_t)(32 * mb + row) * DC + piece * 8) =
+              *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * SPITCH + piece * 16);
+        }
+        block_sync();
       }
+    }
     // next sequence (the loop ends when the unit's range is used up)
     cc.j += seg - 1;
     cursor_next(cc, off, seq_lens, B, total, max_pages);
@@ -570,7 +568,7 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
   if (shape == kShapeDeepSeek) {
     // two head halves per tile stream, paired 8 ids apart; ids padded to whole groups of 16
     const int blocks = 16 * ((G + 7) / 8);
-    attn_deepseek_kernel<<<blocks, 256, 0, stream>>>(
+    attn_deepseek_kernel<<<blocks, 64 * ds::NW, 0, stream>>>(
         (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv, page_table, seq_lens,
         B, max_pages, num_pages, (const Plan*)plan, scale_log2, (uint16_t*)part_o, part_lse);
   } else {
