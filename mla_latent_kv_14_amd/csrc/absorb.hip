@@ -43,13 +43,21 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens, int B, int max_
     if (tid == 0) carry += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
     __syncthreads();
   }
+  const int g = G < 1 ? 1 : G;
+  const int total = carry;
+  const int per = (total + g - 1) / g;
   if (tid == 0) {
-    int total = carry;
-    int g = G < 1 ? 1 : G;
     plan->total = total;
-    plan->per = (total + g - 1) / g;
+    plan->per = per;
     plan->groups = g;
     plan->pad = 0;
+  }
+  // first[u] = b for every unit u whose first tile u*per falls in sequence b's tiles
+  int32_t* first = plan_first(plan, B);
+  for (int b = tid; b < B; b += 256) {
+    const int n = (clamp_len(seq_lens[b], max_pages) + TT - 1) / TT;
+    const int o = off[b];
+    for (int u = (o + per - 1) / per; u < g && (long long)u * per < o + n; ++u) first[u] = b;
   }
 }
 
@@ -83,41 +91,51 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
   }
   for (int i = DN * ROWB / 16 + tid; i < DNP * ROWB / 16; i += 256)  // zero pad rows
     *reinterpret_cast<MLA_LDS u32x4*>(wl + i * 16) = u32x4{0, 0, 0, 0};
+
+  // ---- q_abs^T block [CB x B] = W^T [CB x DNP] * q_nope^T [DNP x B]. Wave w takes sequence
+  // block nb and the m-blocks w, w+4, ...; its q_nope operand is loaded while W is in flight.
+  const int G16 = lane >> 4, q16 = lane & 15;
+  constexpr int KS = DNP / 32;
+  constexpr int MBLK = CB / 16;
+  const int nblocks = (B + 15) / 16;
+  const uint16_t* qn = q_nope + (size_t)h * DN;
+  auto load_q = [&](int nb, bf16x8* bq) {
+    // unconditional loads from clamped (in-bounds) addresses, zeroed afterwards where the
+    // sequence or the contraction index lies past the end
+    const int b = nb * 16 + q16, bc = b < B ? b : B - 1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = ks * 32 + 8 * G16, dc = d0 < DN ? d0 : DN - 8;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(qn + (size_t)bc * H * DN + dc);
+      const uint32_t keep = (b < B && d0 < DN) ? 0xffffffffu : 0u;
+      bq[ks] = __builtin_bit_cast(bf16x8, raw & keep);
+    }
+  };
+  bf16x8 bq[KS];
+  load_q(0, bq);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) settle(bq[ks]);  // issued here, with W still in flight
   wait_vmcnt<0>();
   __syncthreads();
 
-  // ---- q_abs^T block [CB x B] = W^T [CB x DNP] * q_nope^T [DNP x B]
-  const int G16 = lane >> 4, q16 = lane & 15;
-  const int mblocks = CB / 16, nblocks = (B + 15) / 16;
-  const uint16_t* qn = q_nope + (size_t)h * DN;
-  for (int pair = wave; pair < mblocks * nblocks; pair += 4) {
-    const int mb = pair % mblocks, nb = pair / mblocks;
+  for (int nb = 0; nb < nblocks; ++nb) {
+    if (nb > 0) load_q(nb, bq);
     const int b = nb * 16 + q16;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int mb = wave; mb < MBLK; mb += 4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < DNP / 32; ++ks) {
-      bf16x4 a0, a1;
-      {
+      for (int ks = 0; ks < KS; ++ks) {
         const int row0 = ks * 32 + 8 * G16 + (q16 >> 2);
         const int row1 = row0 + 4;
         const uint32_t o0 = row0 * ROWB + ((mb ^ (row0 % UNITS)) * 32) + 8 * (q16 & 3);
         const uint32_t o1 = row1 * ROWB + ((mb ^ (row1 % UNITS)) * 32) + 8 * (q16 & 3);
-        a0 = lds_read_tr16(wl, o0);
-        a1 = lds_read_tr16(wl, o1);
+        acc = mfma_16x16x32(cat4(lds_read_tr16(wl, o0), lds_read_tr16(wl, o1)), bq[ks], acc);
       }
-      bf16x8 bq;
-      const int d0 = ks * 32 + 8 * G16;
-      if (b < B && d0 < DN) {
-        bq = *reinterpret_cast<const bf16x8*>(qn + (size_t)b * H * DN + d0);
-      } else {
-        bq = bf16x8{};
+      if (b < B) {
+        const int c0 = cblk * CB + mb * 16 + 4 * G16;
+        bf16x4 o = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+        *reinterpret_cast<bf16x4*>(q_abs + ((size_t)b * H + h) * DC + c0) = o;
       }
-      acc = mfma_16x16x32(cat4(a0, a1), bq, acc);
-    }
-    if (b < B) {
-      const int c0 = cblk * CB + mb * 16 + 4 * G16;
-      bf16x4 o = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
-      *reinterpret_cast<bf16x4*>(q_abs + ((size_t)b * H + h) * DC + c0) = o;
     }
   }
 }

@@ -70,7 +70,7 @@ Layout layout(const mla_dims_t* d, const ShapeInfo& s) {
   const size_t B = (size_t)d->batch, slots = (size_t)plan_units(d, s) + B;
   Layout L;
   L.plan = 0;
-  L.q_abs = align256(sizeof(mla::Plan) + 4 * B);
+  L.q_abs = align256(sizeof(mla::Plan) + 4 * B + 4 * (size_t)plan_units(d, s));
   L.part_lse = L.q_abs + align256(B * s.H * s.DC * 2);
   L.part_o = L.part_lse + align256(slots * s.H * 4);
   L.total = L.part_o + align256(slots * s.H * s.DC * 2);

@@ -50,50 +50,43 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* off,
   if (b < B) cursor_at(c, b, 0, off, seq_lens, B, total, max_pages);
 }
 
-// Sequence holding plan tile u (the unique b with off[b] <= u < off[b+1]).
-__device__ __forceinline__ int find_seq(const int32_t* off, int B, int total, int u) {
-  int lo = 0, hi = B - 1;  // last b with off[b] <= u
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (ld_uniform(off + mid) <= u) lo = mid; else hi = mid - 1;
-  }
-  (void)total;
-  return lo;
-}
-
 // ================================================================ DeepSeek widths
 // A tile stream (plan unit) is served by two work groups, one per half of the 128 heads, that
-// sit on the same XCD (work groups are dealt to the 8 XCDs round robin, so the pair is
-// placed 8 ids apart): the cache crosses HBM once and the second read hits that XCD's L2.
-// A work group has 8 waves (two per SIMD) and streams 32-token tiles (36 KiB) through 3 LDS
-// buffers (2 in flight). For its 64 heads, per tile:
-//   scores  S^T[32 tok x 32 heads] per head block hb (2 per group). The 576-wide contraction is
-//           split over four waves kq on 8-chunk boundaries (latent 128kq..128kq+127 plus RoPE
-//           16kq..16kq+15): 9 MFMA 32x32x16 each with the wave's query slice (36 VGPRs) held
-//           for the segment. Partial scores are summed through LDS: wave kq owns tokens
-//           8kq..8kq+7 and receives the other three partials for them.
-//   softmax each wave turns its 8 tokens of a head (4 per lane) into bf16 weights P in LDS.
-//           The four waves share a per-head reference max fixed on the segment's first tile;
-//           only when a tile beats it by more than 2^64 do they agree on a new one and rescale.
-//   values  O[64 heads x 64 latent cols of this wave] += P[64 x 32] * tile[32 x 64 cols],
-//           8 MFMA 32x32x16, value operand by transposing LDS reads.
-// Two work-group barriers per tile: after the scores (partials visible, the oldest buffer free
-// for the next prefetch) and after the softmax (P and the next tile visible).
+// sit on the same XCD (work groups are dealt to the 8 XCDs round robin, so the pair is placed
+// 8 ids apart): the cache crosses HBM once and the second read hits that XCD's L2.
+//
+// Inside a work group the eight waves form two teams that run one 32-token tile apart, with a
+// single work-group barrier per tile:
+//   scores  (waves 0..3) wave a holds the whole 576-wide query of 16 heads (72 VGPRs) and
+//           computes S^T[32 tok x 16 heads] with 2 x 18 MFMA 16x16x32; the online softmax of
+//           those heads is then entirely its own (row maxima by two lane exchanges), and it
+//           writes the bf16 weights P, the per-head rescale factors and, at the end of a
+//           segment, 1/l and the lse.
+//   values  (waves 4..7) wave v accumulates O[64 heads x 128 latent columns] += P * V with
+//           16 MFMA 32x32x16 per tile (value operand by transposing LDS reads), and issues the
+//           tile loads; at the end of a segment it normalises, stages its block in the part of
+//           the finished tile that only it read, and writes whole rows.
+// In round r the score team works on tile r+1 while the value team works on tile r. The ring
+// has four 36 KiB buffers: tiles r and r+1 in use, r+2 and r+3 in flight, so a load has two
+// rounds to land. P, the rescale factors and 1/l are double buffered by tile parity.
+// The reference max of a head is fixed on the segment's first tile and only moves when a tile
+// beats it by more than 2^64 (log2 units); the value team then rescales its rows.
 namespace ds {
 constexpr int H = 128, HG = 64, DC = 512, DR = 64, DK = DC + DR, ROWB = DK * 2;
-constexpr int NBUF = 3;
-constexpr int NW = 8;        // waves per work group
+constexpr int NBUF = 4;
+constexpr int NW = 8;        // waves per work group: 4 score waves, 4 value waves
 constexpr int PPITCH = 80;   // bytes per head row of P (32 bf16 + 16 pad: conflict-free reads)
-constexpr int KSTEPS = 9;    // score MFMA steps per wave: a quarter of the 576-wide contraction
+constexpr int KST = DK / 32; // score MFMA steps (16x16x32) per token block
 using Tile = PagedTile<kSub, ROWB>;
-constexpr int IPW = Tile::INSTR / 4;  // load instructions per loading wave (waves 0..3)
+constexpr int IPW = Tile::INSTR / 4;  // load instructions per value wave per tile
 constexpr float kRescale = 64.f;      // log2 headroom before the running max must move
 }  // namespace ds
 
+// Waits until at most `after` (0..2) tiles of N instructions each are still in flight.
 template <int N>
-__device__ __forceinline__ void wait_tiles_after(int tiles_after) {
-  // tile loads complete in order: at most `tiles_after` later tiles (N instructions each) pending
-  if (tiles_after >= 1) wait_vmcnt<N>();
+__device__ __forceinline__ void wait_tiles_after(int after) {
+  if (after >= 2) wait_vmcnt<2 * N>();
+  else if (after == 1) wait_vmcnt<N>();
   else wait_vmcnt<0>();
 }
 
@@ -104,19 +97,14 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
                      const Plan* __restrict__ plan, float scale_log2,
                      uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   using namespace ds;
-  static_assert(NBUF == 3, "wait_tiles_after covers one later tile");
   __shared__ __attribute__((aligned(1024))) char lds_tiles[NBUF * Tile::BYTES];
-  // partial scores: [head block][owner kq][slot (source kq skipping the owner)][lane]
-  __shared__ __attribute__((aligned(16))) f32x4 lds_x[2][4][3][64];
-  __shared__ __attribute__((aligned(16))) char lds_p[HG * PPITCH];
-  __shared__ __attribute__((aligned(16))) float lds_alpha[HG];
-  __shared__ __attribute__((aligned(16))) float lds_invl[HG];
-  __shared__ __attribute__((aligned(16))) float lds_m[2][4][32];  // [hb][kq][head] maxima
-  __shared__ __attribute__((aligned(16))) float lds_l[2][4][32];  // [hb][kq][head] row sums
-  __shared__ int lds_flag[NW];
+  __shared__ __attribute__((aligned(16))) char lds_p[2][HG * PPITCH];
+  __shared__ __attribute__((aligned(16))) float lds_alpha[2][HG];  // rescale factor per head
+  __shared__ __attribute__((aligned(16))) float lds_invl[2][HG];   // 1/l at a segment's end
+  __shared__ __attribute__((aligned(16))) int lds_flag[2][4];      // score wave moved a max
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   // work group -> (tile stream g, head half hh); both halves of g share an XCD
   const int x = blockIdx.x;
   const int g = 8 * (x >> 4) + (x & 7), hh = (x >> 3) & 1;
@@ -126,247 +114,246 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
   if (u0 >= u1) return;
   const int32_t* off = plan_off(plan);
   const int n = u1 - u0;
-
   MLA_LDS char* tiles = (MLA_LDS char*)lds_tiles;
-  MLA_LDS char* pbuf = (MLA_LDS char*)lds_p;
 
-  const int t32 = lane & 31, hi = lane >> 5;
-  const int hb = wave & 1, kq = wave >> 1;
-  const int hloc = 32 * hb + t32;   // local head (0..63) whose scores this lane holds
-  const int head = HG * hh + hloc;  // global head
-  const int G16 = lane >> 4, q16 = lane & 15;
-  const bool loader = wave < 4;     // waves 0..3 issue the tile loads, 9 instructions each
-
-  uint32_t dmo[IPW];
-#pragma unroll
-  for (int k = 0; k < IPW; ++k) dmo[k] = Tile::src_off((wave & 3) + 4 * k, lane, kSub);
-  // score operand: row t32, latent chunks 16kq + 2st + hi (st < 8), RoPE chunk 64 + 2kq + hi
-  const int fs = Tile::swz(t32);
-  uint32_t oq[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) oq[s] = t32 * ROWB + 16 * (16 * kq + ((2 * s + hi) ^ fs));
-  const uint32_t orp = t32 * ROWB + 16 * (64 + ((2 * kq + hi) ^ fs));
-  // value operand (transposing reads): rows 16*ks + 8*(G16/2) + 4*hf + q16/4, latent columns
-  // 64*wave + 32*nb + 16*(G16%2) + 4*(q16%4); the swizzle of those rows does not depend on ks
-  uint32_t ov[2][2];
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int t = 8 * (G16 >> 1) + 4 * hf + (q16 >> 2);
-      const int low = 4 * nb + 2 * (G16 & 1) + ((q16 >> 1) & 1);
-      ov[hf][nb] = t * ROWB + 16 * (8 * wave + (low ^ Tile::swz(t))) + 8 * (q16 & 1);
-    }
-  const uint32_t pw = hloc * PPITCH + 16 * kq + 8 * hi;  // P write: this wave's 4 tokens
-  const uint32_t pr = t32 * PPITCH + 16 * hi;            // P read: + 32*PPITCH*mb + 32*ks
-
-  auto issue_tile = [&](const Cursor& c, int buf) {
-    if (!loader) return;
-    const char* base =
-        Tile::tile_base(kv, page_table + (size_t)c.b * max_pages, c.j, num_pages);
-    Tile::issue<4>(base, min(kSub, c.S - c.j * kSub), dmo, tiles + buf * Tile::BYTES,
-                   wave & 3, lane);
-  };
-
-  bf16x8 qf[KSTEPS];
-  auto load_queries = [&](int b) {  // this wave's query slice, loads completed here
-    const uint16_t* qa = q_abs + ((size_t)b * H + head) * DC + 128 * kq + 8 * hi;
-    const uint16_t* qr = q_rope + ((size_t)b * H + head) * DR + 16 * kq + 8 * hi;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qa + 16 * st);
-    qf[8] = *reinterpret_cast<const bf16x8*>(qr);
-#pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) settle(qf[st]);
-  };
-
-  Cursor cc;
+  Cursor c0;  // the unit's first tile
   {
-    const int b0 = find_seq(off, B, total, u0);
-    cursor_at(cc, b0, u0 - ld_uniform(off + b0), off, seq_lens, B, total, max_pages);
+    const int b0 = ld_uniform(plan_first(plan, B) + g);
+    cursor_at(c0, b0, u0 - ld_uniform(off + b0), off, seq_lens, B, total, max_pages);
   }
-  load_queries(cc.b);
-  Cursor lc = cc;
-  int issued = 0;
-  for (; issued < NBUF - 1 && issued < n; ++issued) {
-    issue_tile(lc, issued);
-    cursor_next(lc, off, seq_lens, B, total, max_pages);
-  }
-  wait_tiles_after<IPW>(issued - 1);
-  block_sync();
 
-  f32x16 acc[2][2];
-  int it = 0;
-  bool first_segment = true;
-  while (it < n) {
-    const int j0 = cc.j, S = cc.S;
-    const int seg = min(cc.nj - cc.j, n - it);
-    if (!first_segment) load_queries(cc.b);
-    first_segment = false;
+  if (wave < 4) {
+    // ================= score team: wave a owns local heads 16a .. 16a+15
+    const int a = wave;
+    const int hl = lane & 15, g4 = lane >> 4;
+    const int head = HG * hh + 16 * a + hl;
+    // score operand (16x16x32, A = tile rows): token row 16tb + hl, chunk 4s + g4 of step s;
+    // with the row swizzle, step s sits at ko[tb][s & 1] + 128 * (s >> 1) (RoPE steps included)
+    uint32_t ko[2][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int tb = 0; tb < 2; ++tb) {
+      const int r = 16 * tb + hl, sw = Tile::swz(r);
+      ko[tb][0] = r * ROWB + 16 * (g4 ^ sw);
+      ko[tb][1] = r * ROWB + 16 * ((4 + g4) ^ sw);
+    }
+    bf16x8 qf[KST];
+    auto load_queries = [&](int b) {  // this wave's 16 queries, loads completed here
+      const uint16_t* qa = q_abs + ((size_t)b * H + head) * DC + 8 * g4;
+      const uint16_t* qr = q_rope + ((size_t)b * H + head) * DR + 8 * g4;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
+      for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qa + 32 * s);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) qf[16 + s] = *reinterpret_cast<const bf16x8*>(qr + 32 * s);
+#pragma unroll
+      for (int s = 0; s < KST; ++s) settle(qf[s]);
+    };
+    load_queries(c0.b);
+    block_sync_tagged<0>();  // tile 0 landed
+
+    Cursor ca = c0;
     float m_ref = -INFINITY, l_lane = 0.f;
-
-    for (int k = 0; k < seg; ++k, ++it) {
-      const MLA_LDS char* kb = tiles + (it % NBUF) * Tile::BYTES;
-      // ---- partial scores over this wave's quarter of the contraction
-      bf16x8 a[KSTEPS];
+    for (int r = -1; r < n; ++r) {
+      const int t = r + 1;  // this round's tile
+      if (t < n) {
+        const bool seg_first = t == 0 || ca.j == 0;
+        const bool seg_last = t == n - 1 || ca.j == ca.nj - 1;
+        if (seg_first && t > 0) load_queries(ca.b);
+        const MLA_LDS char* kb = tiles + (t % NBUF) * Tile::BYTES;
+        f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int st = 0; st < 8; ++st) a[st] = lds_read_b128(kb, oq[st & 3] + 128 * (st >> 2));
-      a[8] = lds_read_b128(kb, orp);
-      f32x16 sc = {};
+        for (int s = 0; s < KST; ++s)
 #pragma unroll
-      for (int st = 0; st < KSTEPS; ++st) sc = mfma_32x32x16(a[st], qf[st], sc);
-      // hand each other wave of the head block the partials of its 4 rows (rows 4q..4q+3)
+          for (int tb = 0; tb < 2; ++tb)
+            sc[tb] = mfma_16x16x32(lds_read_b128(kb, ko[tb][s & 1] + 128 * (s >> 1)), qf[s], sc[tb]);
+        // lane: head hl, tokens 16tb + 4g4 + e
+        const int valid = min(kSub, ca.S - ca.j * kSub);
+        float v[2][4];
+        float mx = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (q == kq) continue;
-        const int slot = q < kq ? kq - 1 : kq;  // this source's slot at owner q
-        lds_x[hb][q][slot][lane] = f32x4{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
-      }
-      block_sync();  // partial scores visible; every wave is done with tile it-1
-      if (issued < n) {
-        issue_tile(lc, issued % NBUF);
-        cursor_next(lc, off, seq_lens, B, total, max_pages);
-        ++issued;
-      }
-      // ---- this wave's rows r = 4kq + e: tokens 8kq + 4hi + e
-      float v[4];
-      {
-        f32x4 t4 = {sc[4 * kq], sc[4 * kq + 1], sc[4 * kq + 2], sc[4 * kq + 3]};
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int sl = 0; sl < 3; ++sl) t4 += lds_x[hb][kq][sl][lane];
-        const int valid = min(kSub, S - (j0 + k) * kSub);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = 8 * kq + 4 * hi + e < valid ? t4[e] * scale_log2 : -INFINITY;
-      }
-      float lm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-      lm = fmaxf(lm, __shfl_xor(lm, 32, 64));  // this wave's 8 tokens of the head
-      if (k == 0) {  // segment start: the head block agrees on the reference max
-        if (hi == 0) lds_m[hb][kq][t32] = lm;
-        block_sync();
-        m_ref = fmaxf(fmaxf(lds_m[hb][0][t32], lds_m[hb][1][t32]),
-                      fmaxf(lds_m[hb][2][t32], lds_m[hb][3][t32]));
-      }
-      const int need = lm > m_ref + kRescale;  // a running max must move (rare)
-      if (lane == 0) lds_flag[wave] = __ballot(need) != 0;
-      float lsum = 0.f;
-      {
-        bf16x4 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const __bf16 pb = (__bf16)exp2f_fast(v[e] - m_ref);
-          pv[e] = pb;
-          lsum += (float)pb;
-        }
-        *reinterpret_cast<MLA_LDS bf16x4*>(pbuf + pw) = pv;
-      }
-      if (it + 1 < n) wait_tiles_after<IPW>(issued - it - 2);  // tile it+1 has landed
-      block_sync();  // P, flags and tile it+1 visible
-      int any = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) any |= lds_flag[w];
-      if (any) {
-        // rare: agree on new reference maxima, recompute this tile's P, rescale accumulators
-        if (hi == 0) lds_m[hb][kq][t32] = lm;
-        block_sync();
-        const float m_new = fmaxf(fmaxf(m_ref, fmaxf(lds_m[hb][0][t32], lds_m[hb][1][t32])),
-                                  fmaxf(lds_m[hb][2][t32], lds_m[hb][3][t32]));
-        const float alpha = exp2f_fast(m_ref - m_new);
-        m_ref = m_new;
-        lsum = 0.f;
-        bf16x4 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const __bf16 pb = (__bf16)exp2f_fast(v[e] - m_ref);
-          pv[e] = pb;
-          lsum += (float)pb;
-        }
-        *reinterpret_cast<MLA_LDS bf16x4*>(pbuf + pw) = pv;
-        l_lane *= alpha;
-        if (kq == 0 && hi == 0) lds_alpha[hloc] = alpha;
-        block_sync();
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 a4 = *reinterpret_cast<const MLA_LDS f32x4*>(
-                (const MLA_LDS char*)lds_alpha + (32 * mb + 8 * r4 + 4 * hi) * 4);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[mb][nb][4 * r4 + e] *= a4[e];
+          for (int e = 0; e < 4; ++e) {
+            v[tb][e] = 16 * tb + 4 * g4 + e < valid ? sc[tb][e] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, v[tb][e]);
           }
-        if (lane == 0) lds_flag[wave] = 0;
-        block_sync();
-      }
-      l_lane += lsum;
-
-      // ---- values: O[64 heads][this wave's 64 columns] += P * V
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 pa[2], vb[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) pa[mb] = lds_read_b128(pbuf, pr + 32 * PPITCH * mb + 32 * ks);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          vb[nb] = cat4(lds_read_tr16(kb, ov[0][nb] + ks * 16 * ROWB),
-                        lds_read_tr16(kb, ov[1][nb] + ks * 16 * ROWB));
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma_32x32x16(pa[mb], vb[nb], acc[mb][nb]);
-      }
-    }
-
-    // ---- end of segment: normalised partial and its lse
-    const int slot = cc.b + g;
-    const float lw = l_lane + __shfl_xor(l_lane, 32, 64);  // this wave's 8 tokens per tile
-    if (hi == 0) lds_l[hb][kq][t32] = lw;
-    block_sync();
-    if (kq == 0 && hi == 0) {
-      const float lt = lds_l[hb][0][t32] + lds_l[hb][1][t32] + lds_l[hb][2][t32] + lds_l[hb][3][t32];
-      lds_invl[hloc] = 1.f / lt;
-      part_lse[(size_t)slot * H + head] = (m_ref + log2f_fast(lt)) * kLn2;
-    }
-    block_sync();
-    // Stage the normalised bf16 partial, 32 heads at a time, in the buffer of the segment's
-    // last tile (no load targets it before the next tile's barrier), then write it out in
-    // 16-byte pieces: rows of 512 latent columns, pitch 1040 bytes.
-    {
-      constexpr int SPITCH = DC * 2 + 16;
-      static_assert(32 * SPITCH <= Tile::BYTES, "staging fits one tile buffer");
-      MLA_LDS char* stg = tiles + ((it - 1) % NBUF) * Tile::BYTES;
-      uint16_t* po = part_o + ((size_t)slot * H + HG * hh) * DC;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 il = *reinterpret_cast<const MLA_LDS f32x4*>(
-              (const MLA_LDS char*)lds_invl + (32 * mb + 8 * r4 + 4 * hi) * 4);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              *reinterpret_cast<MLA_LDS __bf16*>(
-                  stg + (8 * r4 + 4 * hi + e) * SPITCH + (64 * wave + 32 * nb + t32) * 2) =
-                  (__bf16)(acc[mb][nb][4 * r4 + e] * il[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float alpha = 1.f;
+        int need = 0;
+        if (seg_first) {
+          m_ref = mx;
+          l_lane = 0.f;
+        } else if (mx > m_ref + kRescale) {  // rare: the head's reference max moves
+          alpha = exp2f_fast(m_ref - mx);
+          m_ref = mx;
+          l_lane *= alpha;
+          need = 1;
         }
-        block_sync();
+        const int pb = t & 1;
+        if (lane == 0) lds_flag[pb][a] = __ballot(need) != 0;
+        if (g4 == 0) lds_alpha[pb][16 * a + hl] = alpha;
+        float lsum = 0.f;
+        MLA_LDS char* prow = (MLA_LDS char*)lds_p[pb] + (16 * a + hl) * PPITCH + 8 * g4;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {  // 32 rows x 64 pieces of 16 bytes over 512 threads
-          const int q = k * 512 + tid, row = q >> 6, piece = q & 63;
-          *reinterpret_cast<u32x4*>(po + (size_t)(32 * mb + row) * DC + piece * 8) =
-              *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * SPITCH + piece * 16);
+        for (int tb = 0; tb < 2; ++tb) {
+          bf16x4 pv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const __bf16 pbf = (__bf16)exp2f_fast(v[tb][e] - m_ref);
+            pv[e] = pbf;
+            lsum += (float)pbf;
+          }
+          *reinterpret_cast<MLA_LDS bf16x4*>(prow + 32 * tb) = pv;
         }
-        block_sync();
+        l_lane += lsum;
+        if (seg_last) {  // the head's row sum over the segment, its lse and 1/l
+          float lt = l_lane + __shfl_xor(l_lane, 16, 64);
+          lt += __shfl_xor(lt, 32, 64);
+          if (g4 == 0) {
+            lds_invl[pb][16 * a + hl] = 1.f / lt;
+            part_lse[(size_t)(ca.b + g) * H + head] = (m_ref + log2f_fast(lt)) * kLn2;
+          }
+        }
+        cursor_next(ca, off, seq_lens, B, total, max_pages);
       }
+      block_sync_tagged<0>();
     }
-    // next sequence (the loop ends when the unit's range is used up)
-    cc.j += seg - 1;
-    cursor_next(cc, off, seq_lens, B, total, max_pages);
+  } else {
+    // ================= value team: wave vw owns latent columns 128vw .. 128vw+127
+    const int vw = wave - 4;
+    const int t32 = lane & 31, hi = lane >> 5;
+    const int G16 = lane >> 4, q16 = lane & 15;
+    uint32_t dmo[IPW];
+#pragma unroll
+    for (int k = 0; k < IPW; ++k) dmo[k] = Tile::src_off(vw + 4 * k, lane, kSub);
+    // value operand (transposing reads): rows 16ks + 8(G16/2) + 4hf + q16/4, latent columns
+    // 128vw + 32nb + 16(G16%2) + 4(q16%4); column block nb >= 2 is 128 bytes further on
+    uint32_t ov[2][2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int t = 8 * (G16 >> 1) + 4 * hf + (q16 >> 2);
+        const int low = 4 * nb + 2 * (G16 & 1) + ((q16 >> 1) & 1);
+        ov[hf][nb] = t * ROWB + 16 * (16 * vw + (low ^ Tile::swz(t))) + 8 * (q16 & 1);
+      }
+    const uint32_t pr = t32 * PPITCH + 16 * hi;  // P read: + 32*PPITCH*mb + 32*ks
+
+    // tile loads. A loading wave keeps 64 page-table entries of the current sequence in one
+    // VGPR (lane l: entry pw_base + l) and picks entries with readlane, so the loop issues no
+    // scalar loads (the barrier would wait for them).
+    Cursor lc = c0;
+    int issued = 0;
+    int pw_v = 0, pw_b = -1, pw_base = 0;
+    auto issue_next = [&]() {
+      const int p = lc.j / Tile::TPP;
+      if (lc.b != pw_b || p < pw_base || p >= pw_base + 64) {  // refill (waits for earlier loads)
+        pw_b = lc.b;
+        pw_base = p;
+        const int idx = p + lane;
+        pw_v = idx < max_pages ? page_table[(size_t)lc.b * max_pages + idx] : 0;
+      }
+      const char* base =
+          Tile::base_of(kv, __builtin_amdgcn_readlane(pw_v, p - pw_base), lc.j, num_pages);
+      Tile::issue<4>(base, min(kSub, lc.S - lc.j * kSub), dmo,
+                     tiles + (issued % NBUF) * Tile::BYTES, vw, lane);
+      ++issued;
+      cursor_next(lc, off, seq_lens, B, total, max_pages);
+    };
+    while (issued < 3 && issued < n) issue_next();
+    wait_tiles_after<IPW>(issued - 1);  // tile 0 landed
+    block_sync_tagged<1>();
+
+    // round -1: the score team works on tile 0
+    if (1 < n) wait_tiles_after<IPW>(issued - 2);  // tile 1 landed
+    block_sync_tagged<1>();
+
+    Cursor cb = c0;
+    f32x16 acc[2][4];
+    int r = 0;
+    while (r < n) {  // one segment (a run of one sequence's tiles) per pass
+      const int seg = min(cb.nj - cb.j, n - r);
+      const int slot = cb.b + g;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
+      for (int k = 0; k < seg; ++k, ++r) {
+        // tile r+3 goes into the buffer tile r-1 left (read before the last barrier)
+        if (issued < n) issue_next();
+        const int pb = r & 1;
+        const MLA_LDS char* kb = tiles + (r % NBUF) * Tile::BYTES;
+        const MLA_LDS char* pbuf = (const MLA_LDS char*)lds_p[pb];
+        if (k > 0) {
+          const u32x4 fl =
+              *reinterpret_cast<const MLA_LDS u32x4*>((const MLA_LDS char*)lds_flag[pb]);
+          if (fl[0] | fl[1] | fl[2] | fl[3]) {  // rare: some reference maxima moved
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 a4 = *reinterpret_cast<const MLA_LDS f32x4*>(
+                    (const MLA_LDS char*)lds_alpha[pb] + (32 * mb + 8 * r4 + 4 * hi) * 4);
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) acc[mb][nb][4 * r4 + e] *= a4[e];
+              }
+          }
+        }
+        // O[64 heads][128 columns] += P * V
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 pa[2], vb[4];
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            pa[mb] = lds_read_b128(pbuf, pr + 32 * PPITCH * mb + 32 * ks);
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            vb[nb] = cat4(lds_read_tr16(kb, ov[0][nb & 1] + 128 * (nb >> 1) + ks * 16 * ROWB),
+                          lds_read_tr16(kb, ov[1][nb & 1] + 128 * (nb >> 1) + ks * 16 * ROWB));
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+              acc[mb][nb] = mfma_32x32x16(pa[mb], vb[nb], acc[mb][nb]);
+        }
+        if (k == seg - 1) {
+          // Normalise and write this wave's block of the segment's partial. It is staged, 32
+          // heads at a time, in the bytes of tile r that only this wave read (its own columns
+          // of every row: 256 bytes at 256vw of each 1152-byte row), then written as whole
+          // 256-byte rows.
+          MLA_LDS char* stg = tiles + (r % NBUF) * Tile::BYTES + 256 * vw;
+          uint16_t* po = part_o + ((size_t)slot * H + HG * hh) * DC + 128 * vw;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 il = *reinterpret_cast<const MLA_LDS f32x4*>(
+                  (const MLA_LDS char*)lds_invl[pb] + (32 * mb + 8 * r4 + 4 * hi) * 4);
+#pragma unroll
+              for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  *reinterpret_cast<MLA_LDS __bf16*>(
+                      stg + (8 * r4 + 4 * hi + e) * ROWB + (32 * nb + t32) * 2) =
+                      (__bf16)(acc[mb][nb][4 * r4 + e] * il[e]);
+            }
+#pragma unroll
+            for (int q8 = 0; q8 < 8; ++q8) {  // 32 rows x 16 pieces of 16 bytes
+              const int q = q8 * 64 + lane, row = q >> 4, piece = q & 15;
+              *reinterpret_cast<u32x4*>(po + (size_t)(32 * mb + row) * DC + piece * 8) =
+                  *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * ROWB + piece * 16);
+            }
+          }
+        }
+        if (r + 2 < n) wait_tiles_after<IPW>(issued - (r + 3));  // tile r+2 landed
+        block_sync_tagged<1>();  // P of tile r+1 visible; tile r free
+      }
+      cb.j += seg - 1;
+      cursor_next(cb, off, seq_lens, B, total, max_pages);
+    }
+    wait_vmcnt<0>();
   }
 }
 
@@ -409,7 +396,7 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
 
   Cursor lc;
   {
-    const int b0 = find_seq(off, B, total, u0);
+    const int b0 = ld_uniform(plan_first(plan, B) + g);
     cursor_at(lc, b0, u0 - ld_uniform(off + b0), off, seq_lens, B, total, max_pages);
   }
   Cursor cc = lc;

@@ -4,134 +4,205 @@
 //   o_lat[c]   = sum_s exp(lse_s - lse_b) * o_s[c]         (fp32; o_s are normalised partials)
 //   out[b,h,e] = sum_c o_lat[c] * W_UV[h,c,e]              (lpnh.cn/news/2494972 S2.1, v = c_kv W_uv)
 //
-// One work group per (head h, block of EB output columns). The W_UV block [d_latent x EB] is
-// staged in LDS by direct loads (32-byte units XOR-swizzled by row); the merged latent rows of
-// 16 sequences at a time go to LDS as bf16; then out^T[e, b] = W^T[e, c] * o_lat^T[c, b] runs on
-// 16x16x32 bf16 MFMA with transposing reads for the W operand. A sequence with no tokens gets
-// out = 0 and lse = -inf.
+// One work group per (head h, group of 16 sequences, half of the d_v output columns). The two
+// halves of a (head, group) get block ids 8 apart, which places them on the same XCD: the
+// second read of the head's partials is served by that XCD's L2.
+//
+// The W_UV block [d_latent x 64] goes to LDS by direct loads (32-byte units XOR-swizzled by
+// row) and stays in flight while the partials are merged. For the merge every thread owns one
+// 16-byte column chunk of a sequence's latent row (or a quarter of its slots, when the rows are
+// short); it issues the loads of all its slots (rows and their lse values) at once, forms the
+// merged lse from the values it holds, and sums the weighted rows in fp32. The merged rows are
+// rounded once to bf16 in LDS, then out^T[e, b] = W^T[e, c] * o_lat^T[c, b] runs on 16x16x32
+// bf16 MFMA with transposing reads for the W operand. A sequence with no tokens gets out = 0
+// and lse = -inf.
 #include "device.h"
 #include "kernels.h"
 
 namespace mla {
 
-template <int H, int DC, int DV, int EB>
-__global__ void __launch_bounds__(256)
+namespace comb {
+constexpr int NT = 512;   // threads per work group
+constexpr int SEQ = 16;   // sequences per work group (the MFMA N)
+constexpr int EB = 64;    // output columns per work group
+constexpr int CAP = 8;    // slots per thread whose loads are issued together
+}  // namespace comb
+
+template <int H, int DC, int DV>
+__global__ void __launch_bounds__(comb::NT)
 combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
-               const Plan* __restrict__ plan, const int32_t* __restrict__ seq_lens,
-               const uint16_t* __restrict__ W_UV, uint16_t* __restrict__ out,
-               float* __restrict__ lse_out, int B, int max_pages) {
+               const Plan* __restrict__ plan, const uint16_t* __restrict__ W_UV,
+               uint16_t* __restrict__ out, float* __restrict__ lse_out, int B, int groups) {
+  using namespace comb;
   constexpr int ROWB = EB * 2;        // LDS bytes per W row
   constexpr int UNITS = ROWB / 32;    // swizzle period (32-byte units per row)
   constexpr int NCHUNK = DC * ROWB / 16;
   constexpr int OPITCH = DC * 2 + 16; // bytes per merged latent row in LDS
-  static_assert(NCHUNK % 64 == 0 && DC % 32 == 0 && EB == 64, "shape");
+  constexpr int NCH = DC / 8;         // 16-byte chunks of a latent row
+  constexpr int ITEMS = SEQ * NCH;    // (sequence, chunk) items of a work group
+  constexpr int J = ITEMS >= NT ? 1 : NT / ITEMS;  // threads sharing one item (split by slot)
+  constexpr int IPT = ITEMS >= NT ? ITEMS / NT : 1; // items per thread
+  static_assert(DV == 2 * EB, "two column halves per head");
+  static_assert(NCHUNK % 64 == 0 && DC % 32 == 0, "shape");
+  static_assert(ITEMS * J == NT * IPT && (J & (J - 1)) == 0 && J <= 64, "item split");
   __shared__ __attribute__((aligned(16))) char lds_w[DC * ROWB];
-  __shared__ __attribute__((aligned(16))) char lds_o[16 * OPITCH];
-  __shared__ float lds_lse[16];
-  __shared__ int lds_first[16], lds_count[16];
+  __shared__ __attribute__((aligned(16))) char lds_o[SEQ * OPITCH];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nblk = DV / EB;
-  const int h = blockIdx.x / nblk, eblk = blockIdx.x % nblk;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int x = blockIdx.x;
+  const int eblk = (x >> 3) & 1;
+  const int grp = ((x >> 4) << 3) | (x & 7);  // (sequence group, head)
+  if (grp >= groups) return;                  // padding block: leaves before any barrier
+  const int h = grp % H, b0 = (grp / H) * SEQ;
   MLA_LDS char* wl = (MLA_LDS char*)lds_w;
   MLA_LDS char* ol = (MLA_LDS char*)lds_o;
 
-  // ---- stage W_UV[h][:, eblk*EB : +EB]
+  // ---- stage W_UV[h][:, eblk*EB : +EB] (completes during the merge)
   const char* Wg = reinterpret_cast<const char*>(W_UV + (size_t)h * DC * DV + (size_t)eblk * EB);
-  for (int k = wave; k < NCHUNK / 64; k += 4) {
+  for (int k = wave; k < NCHUNK / 64; k += NT / 64) {
     const int q = k * 64 + lane;
     const int row = q / (ROWB / 16), p = q % (ROWB / 16);
     const int lunit = (p >> 1) ^ (row % UNITS);
     load_lds_16(Wg, (uint32_t)(row * DV * 2 + lunit * 32 + (p & 1) * 16), wl + k * 1024);
   }
 
-  const int total = plan->total, per = plan->per;
+  // ---- merge. The plan is read with scalar loads (lane l of every wave gets sequence b0+l's
+  // first slot and slot count), so that waiting for it never waits for the W block.
+  const int total = ld_uniform(&plan->total), per = ld_uniform(&plan->per);
   const int32_t* off = plan_off(plan);
-  const int G16 = lane >> 4, q16 = lane & 15;
-
-  for (int b0 = 0; b0 < B; b0 += 16) {
-    // ---- per-sequence slot range and merged lse
-    if (tid < 16) {
-      const int b = b0 + tid;
-      int first = 0, count = 0;
-      float L = -INFINITY;
-      if (b < B) {
-        const int nt = (b + 1 < B ? off[b + 1] : total) - off[b];
-        if (nt > 0) {
-          const int g0 = off[b] / per, g1 = (off[b] + nt - 1) / per;
-          first = g0 + b;
-          count = g1 - g0 + 1;
-          float m = -INFINITY;
-          for (int s = 0; s < count; ++s) m = fmaxf(m, part_lse[(size_t)(first + s) * H + h]);
-          float z = 0.f;
-          for (int s = 0; s < count; ++s) z += __expf(part_lse[(size_t)(first + s) * H + h] - m);
-          L = m + __logf(z);
-        }
-      }
-      lds_first[tid] = first;
-      lds_count[tid] = count;
-      lds_lse[tid] = L;
-      if (b < B && eblk == 0 && lse_out) lse_out[(size_t)b * H + h] = L;
-    }
-    __syncthreads();
-    // ---- merged latent rows, 8 columns per thread-item
-    for (int item = tid; item < 16 * (DC / 8); item += 256) {
-      const int bi = item / (DC / 8), c0 = (item % (DC / 8)) * 8;
-      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      const int count = lds_count[bi], first = lds_first[bi];
-      const float L = lds_lse[bi];
-      for (int s = 0; s < count; ++s) {
-        const size_t slot = (size_t)(first + s);
-        const float w = __expf(part_lse[slot * H + h] - L);
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(part_o + (slot * H + h) * DC + c0);
+  int offv = total;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] += w * (float)v[e];
+  for (int l = 0; l <= SEQ; ++l) {  // lane SEQ: first tile after the group
+    const int b = b0 + l;
+    const int val = b < B ? ld_uniform(off + b) : total;
+    offv = lane == l ? val : offv;
+  }
+  const int offn = __shfl_down(offv, 1, 64);  // first tile of the next sequence
+  int firstv = 0, countv = 0;
+  if (lane < SEQ && b0 + lane < B) {
+    const int nt = offn - offv;
+    if (nt > 0) {
+      const int g0 = offv / per, g1 = (offv + nt - 1) / per;
+      firstv = g0 + b0 + lane;
+      countv = g1 - g0 + 1;
+    }
+  }
+  const int j = tid % J;
+  const size_t slot_stride = (size_t)H * DC;  // elements between consecutive slots of a head
+  int first[IPT], count[IPT];
+  bf16x8 v[IPT][CAP];
+  float ls[IPT][CAP];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int item = tid / J + it * (NT / J);
+    const int bi = item / NCH, ch = item % NCH;
+    first[it] = __shfl(firstv, bi, 64);
+    count[it] = __shfl(countv, bi, 64);
+    const uint16_t* src = part_o + ((size_t)first[it] * H + h) * DC + ch * 8;
+    const float* lsrc = part_lse + (size_t)first[it] * H + h;
+    // Unconditional loads (no branches between them, so none waits for another): a slot past
+    // the sequence's last one re-reads that last slot, and its lse is replaced by -inf, which
+    // gives it weight 0. With no slot at all (count 0) nothing loaded is used.
+    const int last = count[it] > 0 ? count[it] - 1 : 0;
+#pragma unroll
+    for (int u = 0; u < CAP; ++u) {
+      const int s = j + J * u;
+      const int sc = s < last ? s : last;
+      v[it][u] = *reinterpret_cast<const bf16x8*>(src + (size_t)sc * slot_stride);
+      const float l = lsrc[(size_t)sc * H];
+      ls[it][u] = s < count[it] ? l : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int item = tid / J + it * (NT / J);
+    const int bi = item / NCH, ch = item % NCH, b = b0 + bi;
+    const int cnt = count[it];
+    const float* lsrc = part_lse + (size_t)first[it] * H + h;
+    // merged lse: max, then sum of exponentials, over all slots of the sequence
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < CAP; ++u) m = fmaxf(m, ls[it][u]);
+    for (int s = j + J * CAP; s < cnt; s += J) m = fmaxf(m, lsrc[(size_t)s * H]);
+#pragma unroll
+    for (int d = 1; d < J; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = -INFINITY;
+    if (cnt > 0) {
+      float z = 0.f;
+#pragma unroll
+      for (int u = 0; u < CAP; ++u) z += __expf(ls[it][u] - m);  // exp(-inf) = 0 past count
+      for (int s = j + J * CAP; s < cnt; s += J) z += __expf(lsrc[(size_t)s * H] - m);
+#pragma unroll
+      for (int d = 1; d < J; d <<= 1) z += __shfl_xor(z, d, 64);
+      L = m + __logf(z);
+#pragma unroll
+      for (int u = 0; u < CAP; ++u) {
+        const float w = __expf(ls[it][u] - L);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += w * (float)v[it][u][e];
       }
+      const uint16_t* src = part_o + ((size_t)first[it] * H + h) * DC + ch * 8;
+      for (int s = j + J * CAP; s < cnt; s += J) {  // sequences with more than J*CAP slots
+        const float w = __expf(lsrc[(size_t)s * H] - L);
+        const bf16x8 r = *reinterpret_cast<const bf16x8*>(src + (size_t)s * slot_stride);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += w * (float)r[e];
+      }
+    }
+#pragma unroll
+    for (int d = 1; d < J; d <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] += __shfl_xor(a[e], d, 64);
+    if (j == 0) {
       bf16x8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (__bf16)a[e];
-      *reinterpret_cast<MLA_LDS bf16x8*>(ol + bi * OPITCH + c0 * 2) = o;
+      *reinterpret_cast<MLA_LDS bf16x8*>(ol + bi * OPITCH + ch * 16) = o;
+      if (ch == 0 && eblk == 0 && b < B && lse_out) lse_out[(size_t)b * H + h] = L;
     }
-    wait_vmcnt<0>();  // W block (first pass only; later passes have nothing outstanding)
-    __syncthreads();
-    // ---- out^T[e][b] for this wave's 16 columns e
-    {
-      const int mb = wave;  // EB / 16 == 4 blocks of e
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int ks = 0; ks < DC / 32; ++ks) {
-        const int row0 = ks * 32 + 8 * G16 + (q16 >> 2), row1 = row0 + 4;
-        const bf16x4 a0 = lds_read_tr16(
-            wl, row0 * ROWB + ((mb ^ (row0 % UNITS)) * 32) + 8 * (q16 & 3));
-        const bf16x4 a1 = lds_read_tr16(
-            wl, row1 * ROWB + ((mb ^ (row1 % UNITS)) * 32) + 8 * (q16 & 3));
-        const bf16x8 bo = lds_read_b128(ol, q16 * OPITCH + (ks * 32 + 8 * G16) * 2);
-        acc = mfma_16x16x32(cat4(a0, a1), bo, acc);
-      }
-      const int b = b0 + q16;
-      if (b < B) {
-        const int e0 = eblk * EB + mb * 16 + 4 * G16;
-        bf16x4 o = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
-        *reinterpret_cast<bf16x4*>(out + ((size_t)b * H + h) * DV + e0) = o;
-      }
-    }
-    __syncthreads();
   }
-  (void)max_pages;
-  (void)seq_lens;
+  wait_vmcnt<0>();  // W block
+  block_sync();
+
+  // ---- out^T[e][b]: waves 0..3 take 16 columns e each
+  if (wave < EB / 16) {
+    const int G16 = lane >> 4, q16 = lane & 15;
+    const int mb = wave;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int ks = 0; ks < DC / 32; ++ks) {
+      const int row0 = ks * 32 + 8 * G16 + (q16 >> 2), row1 = row0 + 4;
+      const bf16x4 a0 = lds_read_tr16(wl, row0 * ROWB + ((mb ^ (row0 % UNITS)) * 32) + 8 * (q16 & 3));
+      const bf16x4 a1 = lds_read_tr16(wl, row1 * ROWB + ((mb ^ (row1 % UNITS)) * 32) + 8 * (q16 & 3));
+      const bf16x8 bo = lds_read_b128(ol, q16 * OPITCH + (ks * 32 + 8 * G16) * 2);
+      acc = mfma_16x16x32(cat4(a0, a1), bo, acc);
+    }
+    const int b = b0 + q16;
+    if (b < B) {
+      const int e0 = eblk * EB + mb * 16 + 4 * G16;
+      bf16x4 o = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+      *reinterpret_cast<bf16x4*>(out + ((size_t)b * H + h) * DV + e0) = o;
+    }
+  }
 }
 
 hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, const void* plan,
                           const int32_t* seq_lens, const void* W_UV, void* out, float* lse_out,
                           int B, int H, int max_pages, hipStream_t stream) {
+  (void)seq_lens;
+  (void)max_pages;
+  const int groups = H * ((B + comb::SEQ - 1) / comb::SEQ);
+  const int blocks = 16 * ((groups + 7) / 8);  // pairs of column halves, 8 ids apart
   if (shape == kShapeDeepSeek) {
-    combine_kernel<128, 512, 128, 64><<<H * 2, 256, 0, stream>>>(
-        (const uint16_t*)part_o, part_lse, (const Plan*)plan, seq_lens, (const uint16_t*)W_UV,
-        (uint16_t*)out, lse_out, B, max_pages);
+    combine_kernel<128, 512, 128><<<blocks, comb::NT, 0, stream>>>(
+        (const uint16_t*)part_o, part_lse, (const Plan*)plan, (const uint16_t*)W_UV,
+        (uint16_t*)out, lse_out, B, groups);
   } else {
-    combine_kernel<32, 64, 128, 64><<<H * 2, 256, 0, stream>>>(
-        (const uint16_t*)part_o, part_lse, (const Plan*)plan, seq_lens, (const uint16_t*)W_UV,
-        (uint16_t*)out, lse_out, B, max_pages);
+    combine_kernel<32, 64, 128><<<blocks, comb::NT, 0, stream>>>(
+        (const uint16_t*)part_o, part_lse, (const Plan*)plan, (const uint16_t*)W_UV,
+        (uint16_t*)out, lse_out, B, groups);
   }
   return hipGetLastError();
 }

@@ -66,6 +66,14 @@ __device__ __forceinline__ void load_lds_16(const void* base, uint32_t off, MLA_
 __device__ __forceinline__ void block_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// The same barrier with a distinct text per call site family: code paths of different waves
+// that meet the barrier in different places (teams of a work group) keep their own copies, so
+// the optimiser cannot merge them into one block (which would make both paths' registers live
+// at once).
+template <int TAG>
+__device__ __forceinline__ void block_sync_tagged() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier ; team %0" ::"n"(TAG) : "memory");
+}
 
 // Read of a value that is the same for the whole wave from memory the kernel never writes:
 // through the constant address space it becomes a scalar load (lgkmcnt, not vmcnt).
@@ -104,12 +112,15 @@ struct Plan {
   int32_t per;    // tiles per plan unit
   int32_t groups; // G
   int32_t pad;
-  // followed by int32_t off[B]: first tile of sequence b
+  // followed by int32_t off[B]: first tile of sequence b,
+  // then int32_t first[G]: the sequence holding unit g's first tile (units with tiles only)
 };
 __device__ __forceinline__ const int32_t* plan_off(const Plan* p) {
   return reinterpret_cast<const int32_t*>(p + 1);
 }
 __device__ __forceinline__ int32_t* plan_off(Plan* p) { return reinterpret_cast<int32_t*>(p + 1); }
+__device__ __forceinline__ const int32_t* plan_first(const Plan* p, int B) { return plan_off(p) + B; }
+__device__ __forceinline__ int32_t* plan_first(Plan* p, int B) { return plan_off(p) + B; }
 
 // Effective S_b: clamped to what the page table row can address.
 __device__ __forceinline__ int clamp_len(int s, int max_pages) {

@@ -41,14 +41,23 @@ struct PagedTile {
     return (uint32_t)(r * ROWB + chunk_pos(r, ch) * 16);
   }
 
-  // Global address of the tile holding logical sub-tile j (ROWS tokens) of a sequence.
+  static constexpr int TPP = kPage / ROWS;  // tiles per page
+
+  // Page-table entry of logical sub-tile j (ROWS tokens) of a sequence (a scalar load; callers
+  // that read it ahead of use hide its latency).
+  __device__ static __forceinline__ int page_of(const int32_t* page_row, int j) {
+    return ld_uniform(page_row + j / TPP);
+  }
+  // Global address of sub-tile j given its page-table entry, clamped into the pool.
+  __device__ static __forceinline__ const char* base_of(const char* kv, int page, int j,
+                                                        int num_pages) {
+    page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+    return kv + (size_t)page * (kPage * ROWB) + (size_t)(j % TPP) * BYTES;
+  }
   __device__ static __forceinline__ const char* tile_base(const char* kv,
                                                           const int32_t* page_row, int j,
                                                           int num_pages) {
-    constexpr int TPP = kPage / ROWS;  // tiles per page
-    int page = ld_uniform(page_row + j / TPP);
-    page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
-    return kv + (size_t)page * (kPage * ROWB) + (size_t)(j % TPP) * BYTES;
+    return base_of(kv, page_of(page_row, j), j, num_pages);
   }
 
   // Byte offset inside the tile that lane `lane` of load instruction i fetches.
