@@ -159,12 +159,36 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         const bool seg_last = t == n - 1 || ca.j == ca.nj - 1;
         if (seg_first && t > 0) load_queries(ca.b);
         const MLA_LDS char* kb = tiles + (t % NBUF) * Tile::BYTES;
+        // operands in three batches of six steps, double buffered: the reads of one batch are
+        // in flight while the previous batch's MFMAs run (scheduling fences keep that order)
         f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        bf16x8 kop[2][12];
+        auto read_batch = [&](bf16x8* dst, int s0) {
 #pragma unroll
-        for (int s = 0; s < KST; ++s)
+          for (int i = 0; i < 6; ++i)
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            sc[tb] = mfma_16x16x32(lds_read_b128(kb, ko[tb][s & 1] + 128 * (s >> 1)), qf[s], sc[tb]);
+            for (int tb = 0; tb < 2; ++tb)
+              dst[2 * i + tb] = lds_read_b128(kb, ko[tb][(s0 + i) & 1] + 128 * ((s0 + i) >> 1));
+        };
+        auto mfma_batch = [&](const bf16x8* src, int s0) {
+#pragma unroll
+          for (int i = 0; i < 6; ++i)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+              sc[tb] = mfma_16x16x32(src[2 * i + tb], qf[s0 + i], sc[tb]);
+        };
+        read_batch(kop[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_batch(kop[1], 6);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_batch(kop[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_batch(kop[0], 12);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_batch(kop[1], 6);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_batch(kop[0], 12);
+        static_assert(KST == 18, "three batches of six steps");
         // lane: head hl, tokens 16tb + 4g4 + e
         const int valid = min(kSub, ca.S - ca.j * kSub);
         float v[2][4];

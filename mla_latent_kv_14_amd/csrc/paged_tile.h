@@ -6,12 +6,13 @@
 // one wave instruction moves 64 lanes x 16 bytes into one contiguous KiB of LDS, and each lane
 // picks its own global source, which is how the LDS copy gets its layout:
 //   LDS byte offset of 16-byte chunk ch of row r = r*ROWB + 16*s,
-//   s = (ch & ~7) | ((ch & 7) ^ swz(r)) inside the whole groups of 8 chunks, s = ch past them,
-//   swz(r): m = (r >> 1) & 7, swz = ((m & 3) << 1) | (m >> 2).
-// With 64 four-byte banks served 16 lanes per clock, the XOR makes two read patterns
-// conflict-free: 16 consecutive rows at the same chunk (16-byte reads of the score operand) and
-// 4 consecutive rows x 32 bytes (transposing 8-byte reads of the value operand). Rows of 1152
-// bytes start alternately at bank 0 and bank 32, which the pattern accounts for.
+//   s = (ch & ~7) | ((ch & 7) ^ swz(r)) inside the whole groups of 8 chunks, s = ch past them.
+// The row swizzle swz(r) is chosen per row width from measured LDS costs on gfx950:
+//   1152-byte rows (DeepSeek widths): swz(r) = (r >> 1) & 7. Both reads of the attention
+//     kernel run at the conflict-free rate with it: the score operand of 16x16x32 MFMA
+//     (rows 16t..16t+15 x 4 consecutive chunks, 16 bytes per lane) and the transposing 8-byte
+//     reads of the value operand.
+//   other widths: m = (r >> 1) & 7, swz = ((m & 3) << 1) | (m >> 2).
 // Rows at or past `valid` (cache slots past the end of the sequence) are loaded from row
 // valid-1 instead: they hold finite data and their softmax weight is forced to zero.
 #pragma once
@@ -30,7 +31,8 @@ struct PagedTile {
 
   __device__ static __forceinline__ int swz(int r) {
     const int m = (r >> 1) & 7;
-    return ((m & 3) << 1) | (m >> 2);
+    if constexpr (ROWB == 1152) return m;
+    else return ((m & 3) << 1) | (m >> 2);
   }
   // Position of logical chunk ch of row r (and, the XOR being an involution, the logical chunk
   // kept at position ch).
