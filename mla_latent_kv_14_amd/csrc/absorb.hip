@@ -9,7 +9,8 @@
 // straight from global memory (8 consecutive d per lane), fp32 accumulation, bf16 (RNE) out.
 // The kernel streams 2*H*d_n*d_c bytes of weight once; it is HBM-bound.
 //
-// Block 0 also writes the work plan for the attention kernel (see Plan in device.h).
+// One extra block (the last) writes the work plan for the attention kernel (see Plan in
+// device.h), in parallel with the others.
 #include "device.h"
 #include "kernels.h"
 
@@ -77,8 +78,11 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = DC / CB;
+  if (blockIdx.x == H * nblk) {  // the extra last block writes the work plan, nothing else
+    build_plan(seq_lens, B, max_pages, G, TT, plan);
+    return;
+  }
   const int h = blockIdx.x / nblk, cblk = blockIdx.x % nblk;
-  if (blockIdx.x == 0) build_plan(seq_lens, B, max_pages, G, TT, plan);
 
   // ---- stage W_UK[h][0:DN][cblk*CB : +CB] in LDS
   const char* Wg = reinterpret_cast<const char*>(W_UK + (size_t)h * DN * DC + (size_t)cblk * CB);
@@ -145,12 +149,12 @@ hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* 
                          hipStream_t stream) {
   if (shape == kShapeDeepSeek) {
     constexpr int DN = 128, DC = 512, CB = 128;
-    absorb_kernel<DN, DC, CB><<<H * (DC / CB), 256, 0, stream>>>(
+    absorb_kernel<DN, DC, CB><<<H * (DC / CB) + 1, 256, 0, stream>>>(
         (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H, seq_lens,
         max_pages, G, kSub, (Plan*)plan);
   } else {
     constexpr int DN = 120, DC = 64, CB = 64;
-    absorb_kernel<DN, DC, CB><<<H * (DC / CB), 256, 0, stream>>>(
+    absorb_kernel<DN, DC, CB><<<H * (DC / CB) + 1, 256, 0, stream>>>(
         (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H, seq_lens,
         max_pages, G, kPage, (Plan*)plan);
   }

@@ -200,8 +200,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
             v[tb][e] = 16 * tb + 4 * g4 + e < valid ? sc[tb][e] * scale_log2 : -INFINITY;
             mx = fmaxf(mx, v[tb][e]);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = rows4_max(mx);  // over the head's 32 tokens (lanes hl, hl+16, hl+32, hl+48)
         float alpha = 1.f;
         int need = 0;
         if (seg_first) {
@@ -231,8 +230,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         }
         l_lane += lsum;
         if (seg_last) {  // the head's row sum over the segment, its lse and 1/l
-          float lt = l_lane + __shfl_xor(l_lane, 16, 64);
-          lt += __shfl_xor(lt, 32, 64);
+          const float lt = rows4_sum(l_lane);
           if (g4 == 0) {
             lds_invl[pb][16 * a + hl] = 1.f / lt;
             part_lse[(size_t)(ca.b + g) * H + head] = (m_ref + log2f_fast(lt)) * kLn2;

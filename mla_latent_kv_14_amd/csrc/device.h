@@ -95,6 +95,37 @@ __device__ __forceinline__ void settle(const T& v) {
   asm volatile("" ::"v"(v));
 }
 
+// Reductions over the lanes l, l^16, l^32, l^48 (the four 16-lane rows) with the gfx950 row
+// swaps: v_permlane16_swap exchanges rows 1 and 3 of its first operand with rows 0 and 2 of its
+// second, v_permlane32_swap the upper half of the first with the lower half of the second
+// (checked on the device). Fed two copies of x, every lane ends with the pair {x[l], x[l^16]}
+// (resp. {x[l], x[l^32]}), lower lane first, so the four lanes of a column get bit-identical
+// results. VALU only, no LDS traffic. Written as inline assembly with both registers read and
+// written (the compiler builtin returns the pair, but its second element is lost in code
+// generation); the s_nop covers the wait after a VALU write of the operands.
+__device__ __forceinline__ void swap_rows16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_halves32(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float rows4_max(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap_rows16(a, b);
+  uint32_t c = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+  uint32_t d = c;
+  swap_halves32(c, d);
+  return fmaxf(__builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap_rows16(a, b);
+  uint32_t c = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+  uint32_t d = c;
+  swap_halves32(c, d);
+  return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
+}
+
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2f_fast(float x) { return __builtin_amdgcn_logf(x); }
 
