@@ -9,10 +9,10 @@ weights and cache) are rotated so that the working set of consecutive steps exce
 256 MiB Infinity Cache: the timed steps read from HBM ("cold"). A single-set run is reported
 as "warm" next to it.
 
-Prints one JSON line (the contract): metric/value (KV tokens per second), TFLOP/s, GB/s, the
-roofline object of the dominant kernel (paged attention; HIP events recorded on the library's
-stream around that kernel in every timed step) and the fp64 CPU oracle's throughput on the
-host cores (a reported baseline).
+Prints one JSON line (the contract): metric/value (KV tokens per second, from K plain calls),
+TFLOP/s, GB/s, the roofline object of the dominant kernel (paged attention; its duration comes
+from HIP events recorded on the library's stream around that kernel in a second pass of K calls)
+and the fp64 CPU oracle's throughput on the host cores (a reported baseline).
 
 Algorithmic work of one call (what the method must move or compute; partials and the
 decompression it avoids excluded):
@@ -149,14 +149,19 @@ def run(args):
             raise RuntimeError("mla_decode failed: %s" % lib.mla_status_str(rc).decode())
 
     def timed(rotate):
+        """Step time from K plain calls (no per-stage events in the timed loop), then the
+        per-kernel breakdown from K more calls that record HIP events between the kernels."""
         for i in range(Wu):
             step(i if rotate else 0)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            step(i if rotate else 0, ev_arr[i])
+            step(i if rotate else 0)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        for i in range(K):
+            step(i if rotate else 0, ev_arr[i])
+        torch.cuda.synchronize()
         stages = [[hip.ms(e[j], e[j + 1]) for e in ev] for j in range(3)]
         busy = [hip.ms(e[0], e[3]) for e in ev]
         return (t1 - t0) / K, [sum(s) / K for s in stages], sum(busy) / K

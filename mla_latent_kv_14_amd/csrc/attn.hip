@@ -159,66 +159,50 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         const bool seg_last = t == n - 1 || ca.j == ca.nj - 1;
         if (seg_first && t > 0) load_queries(ca.b);
         const MLA_LDS char* kb = tiles + (t % NBUF) * Tile::BYTES;
-        // operands in three batches of six steps, double buffered: the reads of one batch are
-        // in flight while the previous batch's MFMAs run (scheduling fences keep that order)
-        f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        bf16x8 kop[2][12];
-        auto read_batch = [&](bf16x8* dst, int s0) {
+        // Token block 0 first, then block 1; each block accumulates in two chains (even and odd
+        // steps). Operand reads run one half-block (9 steps) ahead of the MFMAs, and on tiles
+        // whose reference max is already set the weights of block 0 are formed while block 1's
+        // MFMAs run (scheduling fences and groups keep that order).
+        bf16x8 kop[2][9];
+        auto read_half = [&](bf16x8* dst, int tb, int s0) {
 #pragma unroll
-          for (int i = 0; i < 6; ++i)
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-              dst[2 * i + tb] = lds_read_b128(kb, ko[tb][(s0 + i) & 1] + 128 * ((s0 + i) >> 1));
+          for (int i = 0; i < 9; ++i)
+            dst[i] = lds_read_b128(kb, ko[tb][(s0 + i) & 1] + 128 * ((s0 + i) >> 1));
         };
-        auto mfma_batch = [&](const bf16x8* src, int s0) {
+        auto mfma_half = [&](f32x4* c, const bf16x8* src, int s0) {
 #pragma unroll
-          for (int i = 0; i < 6; ++i)
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-              sc[tb] = mfma_16x16x32(src[2 * i + tb], qf[s0 + i], sc[tb]);
+          for (int i = 0; i < 9; ++i)
+            c[(s0 + i) & 1] = mfma_16x16x32(src[i], qf[s0 + i], c[(s0 + i) & 1]);
         };
-        read_batch(kop[0], 0);
+        static_assert(KST == 18, "two half-blocks of nine steps");
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 c0[2] = {zero4, zero4}, c1[2] = {zero4, zero4};
+        read_half(kop[0], 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        read_batch(kop[1], 6);
+        read_half(kop[1], 0, 9);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_batch(kop[0], 0);
+        mfma_half(c0, kop[0], 0);
         __builtin_amdgcn_sched_barrier(0);
-        read_batch(kop[0], 12);
+        read_half(kop[0], 1, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_batch(kop[1], 6);
+        mfma_half(c0, kop[1], 9);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_batch(kop[0], 12);
-        static_assert(KST == 18, "three batches of six steps");
+        read_half(kop[1], 1, 9);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(c1, kop[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
         // lane: head hl, tokens 16tb + 4g4 + e
         const int valid = min(kSub, ca.S - ca.j * kSub);
-        float v[2][4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[tb][e] = 16 * tb + 4 * g4 + e < valid ? sc[tb][e] * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, v[tb][e]);
-          }
-        mx = rows4_max(mx);  // over the head's 32 tokens (lanes hl, hl+16, hl+32, hl+48)
-        float alpha = 1.f;
-        int need = 0;
-        if (seg_first) {
-          m_ref = mx;
-          l_lane = 0.f;
-        } else if (mx > m_ref + kRescale) {  // rare: the head's reference max moves
-          alpha = exp2f_fast(m_ref - mx);
-          m_ref = mx;
-          l_lane *= alpha;
-          need = 1;
-        }
         const int pb = t & 1;
-        if (lane == 0) lds_flag[pb][a] = __ballot(need) != 0;
-        if (g4 == 0) lds_alpha[pb][16 * a + hl] = alpha;
-        float lsum = 0.f;
         MLA_LDS char* prow = (MLA_LDS char*)lds_p[pb] + (16 * a + hl) * PPITCH + 8 * g4;
+        float v[2][4];
+        auto scale_block = [&](int tb, const f32x4* c) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
+          for (int e = 0; e < 4; ++e)
+            v[tb][e] = 16 * tb + 4 * g4 + e < valid ? (c[0][e] + c[1][e]) * scale_log2 : -INFINITY;
+        };
+        float lsum = 0.f;
+        auto weights_block = [&](int tb) {  // bf16 weights of block tb against m_ref, to P
           bf16x4 pv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -227,7 +211,48 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
             lsum += (float)pbf;
           }
           *reinterpret_cast<MLA_LDS bf16x4*>(prow + 32 * tb) = pv;
+        };
+        if (!seg_first) {
+          scale_block(0, c0);
+          weights_block(0);
+          mfma_half(c1, kop[1], 9);
+#pragma unroll
+          for (int i = 0; i < 9; ++i) {  // one MFMA, then a few VALU instructions of block 0
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          scale_block(1, c1);
+          weights_block(1);
+        } else {
+          mfma_half(c1, kop[1], 9);
+          scale_block(0, c0);
+          scale_block(1, c1);
         }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, v[tb][e]);
+        mx = rows4_max(mx);  // over the head's 32 tokens (lanes hl, hl+16, hl+32, hl+48)
+        float alpha = 1.f;
+        int need = 0;
+        if (seg_first) {
+          m_ref = mx;
+          l_lane = 0.f;
+          weights_block(0);
+          weights_block(1);
+        } else if (mx > m_ref + kRescale) {  // rare: the head's reference max moves
+          alpha = exp2f_fast(m_ref - mx);
+          m_ref = mx;
+          l_lane *= alpha;
+          need = 1;
+          lsum = 0.f;  // this tile's weights again, against the new reference
+          weights_block(0);
+          weights_block(1);
+        }
+        if (lane == 0) lds_flag[pb][a] = __ballot(need) != 0;
+        if (g4 == 0) lds_alpha[pb][16 * a + hl] = alpha;
         l_lane += lsum;
         if (seg_last) {  // the head's row sum over the segment, its lse and 1/l
           const float lt = rows4_sum(l_lane);
@@ -267,7 +292,12 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
     Cursor lc = c0;
     int issued = 0;
     int pw_v = 0, pw_b = -1, pw_base = 0;
-    auto issue_next = [&]() {
+    // The next tile to load: its global base, valid rows and LDS buffer (lookup), then its 9
+    // instructions per wave, possibly in parts, then the cursor moves on (advance).
+    const char* nbase = kv;
+    int nvalid = 0;
+    MLA_LDS char* ndst = tiles;
+    auto lookup = [&]() {
       const int p = lc.j / Tile::TPP;
       if (lc.b != pw_b || p < pw_base || p >= pw_base + 64) {  // refill (waits for earlier loads)
         pw_b = lc.b;
@@ -275,12 +305,18 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         const int idx = p + lane;
         pw_v = idx < max_pages ? page_table[(size_t)lc.b * max_pages + idx] : 0;
       }
-      const char* base =
-          Tile::base_of(kv, __builtin_amdgcn_readlane(pw_v, p - pw_base), lc.j, num_pages);
-      Tile::issue<4>(base, min(kSub, lc.S - lc.j * kSub), dmo,
-                     tiles + (issued % NBUF) * Tile::BYTES, vw, lane);
+      nbase = Tile::base_of(kv, __builtin_amdgcn_readlane(pw_v, p - pw_base), lc.j, num_pages);
+      nvalid = min(kSub, lc.S - lc.j * kSub);
+      ndst = tiles + (issued % NBUF) * Tile::BYTES;
+    };
+    auto advance = [&]() {
       ++issued;
       cursor_next(lc, off, seq_lens, B, total, max_pages);
+    };
+    auto issue_next = [&]() {
+      lookup();
+      Tile::issue<4>(nbase, nvalid, dmo, ndst, vw, lane);
+      advance();
     };
     while (issued < 3 && issued < n) issue_next();
     wait_tiles_after<IPW>(issued - 1);  // tile 0 landed
@@ -301,8 +337,10 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
       for (int k = 0; k < seg; ++k, ++r) {
-        // tile r+3 goes into the buffer tile r-1 left (read before the last barrier)
-        if (issued < n) issue_next();
+        // tile r+3 goes into the buffer tile r-1 left (read before the last barrier); its
+        // loads are issued in three parts between the value MFMAs
+        const bool load = issued < n;
+        if (load) lookup();
         const int pb = r & 1;
         const MLA_LDS char* kb = tiles + (r % NBUF) * Tile::BYTES;
         const MLA_LDS char* pbuf = (const MLA_LDS char*)lds_p[pb];
@@ -334,11 +372,19 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
           for (int nb = 0; nb < 4; ++nb)
             vb[nb] = cat4(lds_read_tr16(kb, ov[0][nb & 1] + 128 * (nb >> 1) + ks * 16 * ROWB),
                           lds_read_tr16(kb, ov[1][nb & 1] + 128 * (nb >> 1) + ks * 16 * ROWB));
+          if (load) {
+            if (ks == 0) Tile::issue_part<4, 0, 3>(nbase, nvalid, dmo, ndst, vw, lane);
+            else Tile::issue_part<4, 3, 6>(nbase, nvalid, dmo, ndst, vw, lane);
+          }
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
               acc[mb][nb] = mfma_32x32x16(pa[mb], vb[nb], acc[mb][nb]);
+        }
+        if (load) {
+          Tile::issue_part<4, 6, 9>(nbase, nvalid, dmo, ndst, vw, lane);
+          advance();
         }
         if (k == seg - 1) {
           // Normalise and write this wave's block of the segment's partial. It is staged, 32

@@ -70,21 +70,28 @@ struct PagedTile {
     return (uint32_t)(rr * ROWB + chunk_pos(r, s) * 16);
   }
 
-  // Issue this wave's share of the tile: instructions i0 + k*STEP for k < INSTR/STEP. Full tiles
-  // use the precomputed lane offsets `offs`; a tile with fewer valid rows computes them.
+  // Issue part of this wave's share of the tile: instructions i0 + k*STEP for KB <= k < KE.
+  // Full tiles use the precomputed lane offsets `offs`; a tile with fewer valid rows computes
+  // them.
+  template <int STEP, int KB, int KE>
+  __device__ static __forceinline__ void issue_part(const char* base, int valid,
+                                                    const uint32_t* offs, MLA_LDS char* lds,
+                                                    int i0, int lane) {
+    static_assert(INSTR % STEP == 0 && 0 <= KB && KB <= KE && KE <= INSTR / STEP, "range");
+    if (valid >= ROWS) {
+#pragma unroll
+      for (int k = KB; k < KE; ++k) load_lds_16(base, offs[k], lds + (i0 + k * STEP) * 1024);
+    } else {
+#pragma unroll
+      for (int k = KB; k < KE; ++k)
+        load_lds_16(base, src_off(i0 + k * STEP, lane, valid), lds + (i0 + k * STEP) * 1024);
+    }
+  }
+  // Issue this wave's whole share of the tile: instructions i0 + k*STEP for k < INSTR/STEP.
   template <int STEP>
   __device__ static __forceinline__ void issue(const char* base, int valid, const uint32_t* offs,
                                                MLA_LDS char* lds, int i0, int lane) {
-    static_assert(INSTR % STEP == 0, "instructions must split evenly");
-    if (valid >= ROWS) {
-#pragma unroll
-      for (int k = 0; k < INSTR / STEP; ++k)
-        load_lds_16(base, offs[k], lds + (i0 + k * STEP) * 1024);
-    } else {
-#pragma unroll
-      for (int k = 0; k < INSTR / STEP; ++k)
-        load_lds_16(base, src_off(i0 + k * STEP, lane, valid), lds + (i0 + k * STEP) * 1024);
-    }
+    issue_part<STEP, 0, INSTR / STEP>(base, valid, offs, lds, i0, lane);
   }
 };
 
