@@ -16,19 +16,26 @@
 
 namespace mla {
 
-// off[b] = sum_{b' < b} ceil(S_b' / TT) with S clamped; header {total, per, groups}.
-__device__ void build_plan(const int32_t* __restrict__ seq_lens, int B, int max_pages, int G,
+// off[b] = sum_{b' < b} ceil(S_b' / TT) with S clamped; header {total, per, groups}; and the
+// start record of every unit that owns tiles (see UnitStart).
+__device__ void build_plan(const int32_t* __restrict__ seq_lens,
+                           const int32_t* __restrict__ page_table, int B, int max_pages, int G,
                            int TT, Plan* __restrict__ plan) {
+  constexpr int kSeqInLds = 4096;  // batches up to this size keep offsets and lengths in LDS
   __shared__ int32_t wave_tot[4];
   __shared__ int32_t carry;
+  __shared__ int32_t seq_off[kSeqInLds], seq_len[kSeqInLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) carry = 0;
   __syncthreads();
   int32_t* off = plan_off(plan);
   for (int base = 0; base < B; base += 256) {
     const int b = base + tid;
-    int n = 0;
-    if (b < B) n = (clamp_len(seq_lens[b], max_pages) + TT - 1) / TT;
+    int n = 0, S = 0;
+    if (b < B) {
+      S = clamp_len(seq_lens[b], max_pages);
+      n = (S + TT - 1) / TT;
+    }
     int x = n;  // inclusive wave scan
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -39,7 +46,13 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens, int B, int max_
     __syncthreads();
     int before = carry;
     for (int w = 0; w < wave; ++w) before += wave_tot[w];
-    if (b < B) off[b] = before + x - n;
+    if (b < B) {
+      off[b] = before + x - n;
+      if (b < kSeqInLds) {
+        seq_off[b] = before + x - n;
+        seq_len[b] = S;
+      }
+    }
     __syncthreads();
     if (tid == 0) carry += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
     __syncthreads();
@@ -53,12 +66,56 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens, int B, int max_
     plan->groups = g;
     plan->pad = 0;
   }
-  // first[u] = b for every unit u whose first tile u*per falls in sequence b's tiles
-  int32_t* first = plan_first(plan, B);
-  for (int b = tid; b < B; b += 256) {
-    const int n = (clamp_len(seq_lens[b], max_pages) + TT - 1) / TT;
-    const int o = off[b];
-    for (int u = (o + per - 1) / per; u < g && (long long)u * per < o + n; ++u) first[u] = b;
+  UnitStart* start = plan_units(plan, B);
+  auto write_unit = [&](int u, int b, int j, int S, int page) {
+    UnitStart rec;
+    rec.b = b;
+    rec.j = j;
+    rec.nj = (S + TT - 1) / TT;
+    rec.S = S;
+    rec.page = page;
+    rec.pad[0] = rec.pad[1] = rec.pad[2] = 0;
+    start[u] = rec;
+  };
+  if (B <= kSeqInLds) {
+    // every unit on its own: its sequence by binary search over the offsets in LDS (the last
+    // b with off[b] <= u*per; sequences with no tiles share their successor's offset and are
+    // skipped by taking the last), then the page of its first tile
+    for (int u0 = tid; u0 < g; u0 += 4 * 256) {
+      int ub[4], uj[4], page[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int u = u0 + k * 256;
+        ub[k] = -1;
+        uj[k] = 0;
+        page[k] = 0;
+        if (u < g && (long long)u * per < total) {
+          const int t = u * per;
+          int lo = 0, hi = B - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seq_off[mid] <= t) lo = mid; else hi = mid - 1;
+          }
+          ub[k] = lo;
+          uj[k] = t - seq_off[lo];
+          page[k] = page_table[(size_t)lo * max_pages + (uj[k] * TT) / kPage];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (ub[k] >= 0) write_unit(u0 + k * 256, ub[k], uj[k], seq_len[ub[k]], page[k]);
+    }
+  } else {
+    // large batches: each thread walks the units that start in its sequences
+    for (int b = tid; b < B; b += 256) {
+      const int S = clamp_len(seq_lens[b], max_pages);
+      const int n = (S + TT - 1) / TT;
+      const int o = off[b];
+      for (int u = (o + per - 1) / per; u < g && (long long)u * per < o + n; ++u) {
+        const int j = u * per - o;
+        write_unit(u, b, j, S, page_table[(size_t)b * max_pages + (j * TT) / kPage]);
+      }
+    }
   }
 }
 
@@ -67,6 +124,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ W_UK,
                                                      uint16_t* __restrict__ q_abs, int B, int H,
                                                      const int32_t* __restrict__ seq_lens,
+                                                     const int32_t* __restrict__ page_table,
                                                      int max_pages, int G, int TT, Plan* plan) {
   constexpr int DNP = (DN + 31) / 32 * 32;  // contraction padded to the MFMA K of 32
   constexpr int ROWB = CB * 2;              // LDS bytes per W row
@@ -79,7 +137,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = DC / CB;
   if (blockIdx.x == H * nblk) {  // the extra last block writes the work plan, nothing else
-    build_plan(seq_lens, B, max_pages, G, TT, plan);
+    build_plan(seq_lens, page_table, B, max_pages, G, TT, plan);
     return;
   }
   const int h = blockIdx.x / nblk, cblk = blockIdx.x % nblk;
@@ -145,18 +203,18 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 }
 
 hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* q_abs, int B,
-                         int H, const int32_t* seq_lens, int max_pages, int G, void* plan,
-                         hipStream_t stream) {
+                         int H, const int32_t* seq_lens, const int32_t* page_table, int max_pages,
+                         int G, void* plan, hipStream_t stream) {
   if (shape == kShapeDeepSeek) {
     constexpr int DN = 128, DC = 512, CB = 128;
     absorb_kernel<DN, DC, CB><<<H * (DC / CB) + 1, 256, 0, stream>>>(
         (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H, seq_lens,
-        max_pages, G, kSub, (Plan*)plan);
+        page_table, max_pages, G, kSub, (Plan*)plan);
   } else {
     constexpr int DN = 120, DC = 64, CB = 64;
     absorb_kernel<DN, DC, CB><<<H * (DC / CB) + 1, 256, 0, stream>>>(
         (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H, seq_lens,
-        max_pages, G, kPage, (Plan*)plan);
+        page_table, max_pages, G, kPage, (Plan*)plan);
   }
   return hipGetLastError();
 }

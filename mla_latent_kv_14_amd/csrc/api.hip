@@ -70,7 +70,7 @@ Layout layout(const mla_dims_t* d, const ShapeInfo& s) {
   const size_t B = (size_t)d->batch, slots = (size_t)plan_units(d, s) + B;
   Layout L;
   L.plan = 0;
-  L.q_abs = align256(sizeof(mla::Plan) + 4 * B + 4 * (size_t)plan_units(d, s));
+  L.q_abs = align256(mla::plan_bytes((int)B, plan_units(d, s)));
   L.part_lse = L.q_abs + align256(B * s.H * s.DC * 2);
   L.part_o = L.part_lse + align256(slots * s.H * 4);
   L.total = L.part_o + align256(slots * s.H * s.DC * 2);
@@ -126,8 +126,8 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
   };
 
   if ((st = mark(0)) != MLA_OK) return st;
-  st = hip_status(mla::launch_absorb(s.shape, q_nope, W_UK, ws + L.q_abs, B, s.H, seq_lens, mp,
-                                     G, ws + L.plan, hs));
+  st = hip_status(mla::launch_absorb(s.shape, q_nope, W_UK, ws + L.q_abs, B, s.H, seq_lens,
+                                     page_table, mp, G, ws + L.plan, hs));
   if (st != MLA_OK || (st = mark(1)) != MLA_OK) return st;
   st = hip_status(mla::launch_attention(s.shape, ws + L.q_abs, q_rope, kv_pages, page_table,
                                         seq_lens, B, mp, dims->num_pages, ws + L.plan, G,

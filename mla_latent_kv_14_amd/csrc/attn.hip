@@ -116,11 +116,8 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
   const int n = u1 - u0;
   MLA_LDS char* tiles = (MLA_LDS char*)lds_tiles;
 
-  Cursor c0;  // the unit's first tile
-  {
-    const int b0 = ld_uniform(plan_first(plan, B) + g);
-    cursor_at(c0, b0, u0 - ld_uniform(off + b0), off, seq_lens, B, total, max_pages);
-  }
+  const UnitStart us = load_unit(plan, B, g);
+  const Cursor c0 = {us.b, us.j, us.nj, us.S};  // the unit's first tile
 
   if (wave < 4) {
     // ================= score team: wave a owns local heads 16a .. 16a+15
@@ -318,6 +315,22 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
       Tile::issue<4>(nbase, nvalid, dmo, ndst, vw, lane);
       advance();
     };
+    {
+      // Tile 0 goes out at once with the page from the unit record. Beside it, the page window
+      // of the sequence is loaded for the next tiles; that load is not tracked by the compiler
+      // and is waited for explicitly (loads complete in order: it is older than tile 0's).
+      pw_b = lc.b;
+      pw_base = lc.j / Tile::TPP;
+      const int idx = pw_base + lane < max_pages ? pw_base + lane : max_pages - 1;
+      const int32_t* src = page_table + (size_t)lc.b * max_pages + idx;
+      asm volatile("global_load_dword %0, %1, off" : "=v"(pw_v) : "v"(src) : "memory");
+      nbase = Tile::base_of(kv, us.page, lc.j, num_pages);
+      nvalid = min(kSub, lc.S - lc.j * kSub);
+      ndst = tiles;
+      Tile::issue<4>(nbase, nvalid, dmo, ndst, vw, lane);
+      advance();
+      asm volatile("s_waitcnt vmcnt(%1)" : "+v"(pw_v) : "n"(IPW) : "memory");
+    }
     while (issued < 3 && issued < n) issue_next();
     wait_tiles_after<IPW>(issued - 1);  // tile 0 landed
     block_sync_tagged<1>();
@@ -462,11 +475,8 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   const int n = u1 - u0;
   MLA_LDS char* tiles = (MLA_LDS char*)lds_tiles[wave];
 
-  Cursor lc;
-  {
-    const int b0 = ld_uniform(plan_first(plan, B) + g);
-    cursor_at(lc, b0, u0 - ld_uniform(off + b0), off, seq_lens, B, total, max_pages);
-  }
+  const UnitStart us = load_unit(plan, B, g);
+  Cursor lc = {us.b, us.j, us.nj, us.S};
   Cursor cc = lc;
   uint32_t dmo[IPW];  // lane offsets of a full-tile load
 #pragma unroll

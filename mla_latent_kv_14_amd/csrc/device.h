@@ -144,14 +144,45 @@ struct Plan {
   int32_t groups; // G
   int32_t pad;
   // followed by int32_t off[B]: first tile of sequence b,
-  // then int32_t first[G]: the sequence holding unit g's first tile (units with tiles only)
+  // then (at a 32-byte boundary) UnitStart start[G]
+};
+// Where plan unit g starts (written for units that own tiles), so that a work group finds its
+// first tile, its sequence and the page of that tile with one scalar load.
+struct UnitStart {
+  int32_t b;     // sequence holding the unit's first tile
+  int32_t j;     // that tile's index inside the sequence
+  int32_t nj;    // tiles of sequence b
+  int32_t S;     // clamped length of sequence b
+  int32_t page;  // page-table entry of the page holding tile j (as stored; clamped at use)
+  int32_t pad[3];
 };
 __device__ __forceinline__ const int32_t* plan_off(const Plan* p) {
   return reinterpret_cast<const int32_t*>(p + 1);
 }
 __device__ __forceinline__ int32_t* plan_off(Plan* p) { return reinterpret_cast<int32_t*>(p + 1); }
-__device__ __forceinline__ const int32_t* plan_first(const Plan* p, int B) { return plan_off(p) + B; }
-__device__ __forceinline__ int32_t* plan_first(Plan* p, int B) { return plan_off(p) + B; }
+__host__ __device__ constexpr size_t plan_units_offset(int B) {
+  return (sizeof(Plan) + 4 * (size_t)B + 31) & ~(size_t)31;
+}
+__host__ __device__ constexpr size_t plan_bytes(int B, int G) {
+  return plan_units_offset(B) + sizeof(UnitStart) * (size_t)G;
+}
+__device__ __forceinline__ const UnitStart* plan_units(const Plan* p, int B) {
+  return reinterpret_cast<const UnitStart*>(reinterpret_cast<const char*>(p) + plan_units_offset(B));
+}
+__device__ __forceinline__ UnitStart* plan_units(Plan* p, int B) {
+  return reinterpret_cast<UnitStart*>(reinterpret_cast<char*>(p) + plan_units_offset(B));
+}
+// The unit record through the scalar path (written by an earlier kernel, read-only here).
+__device__ __forceinline__ UnitStart load_unit(const Plan* p, int B, int g) {
+  const int32_t* w = reinterpret_cast<const int32_t*>(plan_units(p, B) + g);
+  UnitStart u;
+  u.b = ld_uniform(w + 0);
+  u.j = ld_uniform(w + 1);
+  u.nj = ld_uniform(w + 2);
+  u.S = ld_uniform(w + 3);
+  u.page = ld_uniform(w + 4);
+  return u;
+}
 
 // Effective S_b: clamped to what the page table row can address.
 __device__ __forceinline__ int clamp_len(int s, int max_pages) {

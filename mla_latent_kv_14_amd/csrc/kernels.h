@@ -16,8 +16,8 @@ enum Shape : int {
 constexpr int kAttnWavesMha2Mla = 4;
 
 hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* q_abs, int B,
-                         int H, const int32_t* seq_lens, int max_pages, int G, void* plan,
-                         hipStream_t stream);
+                         int H, const int32_t* seq_lens, const int32_t* page_table, int max_pages,
+                         int G, void* plan, hipStream_t stream);
 
 hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, const void* kv,
                             const int32_t* page_table, const int32_t* seq_lens, int B,

@@ -51,21 +51,23 @@ def call(d, ptrs=None, ws=None, ws_bytes=None, lse=None):
 
 
 def test_workspace_bytes_closed_form():
-    # plan header + offsets + unit starts, q_abs, per-slot lse, per-slot bf16 partials
-    # (slots = units + B)
+    # plan (header + offsets, then one 32-byte start record per unit at a 32-byte boundary),
+    # q_abs, per-slot lse, per-slot bf16 partials (slots = units + B)
+    def plan(B, G):
+        return (16 + 4 * B + 31) // 32 * 32 + 32 * G
     def al(x):
         return (x + 255) // 256 * 256
     d = ds_dims()
     slots = 128 + 16
-    assert M.workspace_bytes(d) == (al(16 + 4 * 16 + 4 * 128) + al(16 * 128 * 512 * 2) + al(slots * 128 * 4)
+    assert M.workspace_bytes(d) == (al(plan(16, 128)) + al(16 * 128 * 512 * 2) + al(slots * 128 * 4)
                                     + al(slots * 128 * 512 * 2))
     d = m2_dims()
     slots = 1024 + 32
-    assert M.workspace_bytes(d) == (al(16 + 4 * 32 + 4 * 1024) + al(32 * 32 * 64 * 2) + al(slots * 32 * 4)
+    assert M.workspace_bytes(d) == (al(plan(32, 1024)) + al(32 * 32 * 64 * 2) + al(slots * 32 * 4)
                                     + al(slots * 32 * 64 * 2))
     # units are capped by the tiles that can exist: B=1, S=512 -> 16 tiles of 32 tokens
     d = ds_dims(B=1, max_pages=8, num_pages=8, max_seq_len=512)
-    assert M.workspace_bytes(d) == al(16 + 4 + 4 * 16) + al(128 * 512 * 2) + al(17 * 128 * 4) + \
+    assert M.workspace_bytes(d) == al(plan(1, 16)) + al(128 * 512 * 2) + al(17 * 128 * 4) + \
         al(17 * 128 * 512 * 2)
 
 
