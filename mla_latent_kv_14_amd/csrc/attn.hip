@@ -296,11 +296,17 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
     MLA_LDS char* ndst = tiles;
     auto lookup = [&]() {
       const int p = lc.j / Tile::TPP;
-      if (lc.b != pw_b || p < pw_base || p >= pw_base + 64) {  // refill (waits for earlier loads)
+      if (lc.b != pw_b || p < pw_base || p >= pw_base + 64) {
+        // refill: the load and its wait are one asm statement, so the compiler sees pw_v as
+        // ready and puts no wait of its own before the readlane below (such a wait would drain
+        // the tile loads in flight on every tile). Loads complete in order, so this wait also
+        // lets the earlier tile loads land; it happens once per 64 pages or sequence.
         pw_b = lc.b;
         pw_base = p;
-        const int idx = p + lane;
-        pw_v = idx < max_pages ? page_table[(size_t)lc.b * max_pages + idx] : 0;
+        const int idx = min(p + lane, max_pages - 1);
+        const int32_t* src = page_table + (size_t)lc.b * max_pages + idx;
+        asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)"
+                     : "=v"(pw_v) : "v"(src) : "memory");
       }
       nbase = Tile::base_of(kv, __builtin_amdgcn_readlane(pw_v, p - pw_base), lc.j, num_pages);
       nvalid = min(kSub, lc.S - lc.j * kSub);
@@ -405,7 +411,11 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
           // of every row: 256 bytes at 256vw of each 1152-byte row), then written as whole
           // 256-byte rows.
           MLA_LDS char* stg = tiles + (r % NBUF) * Tile::BYTES + 256 * vw;
-          uint16_t* po = part_o + ((size_t)slot * H + HG * hh) * DC + 128 * vw;
+          // (the slot and lane pass through empty asm so that the store addresses are formed
+          // here, not kept in registers through the whole segment)
+          int slot_e = slot, lane_e = lane;
+          asm volatile("" : "+s"(slot_e), "+v"(lane_e));
+          uint16_t* po = part_o + ((size_t)slot_e * H + HG * hh) * DC + 128 * vw;
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -422,7 +432,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
             }
 #pragma unroll
             for (int q8 = 0; q8 < 8; ++q8) {  // 32 rows x 16 pieces of 16 bytes
-              const int q = q8 * 64 + lane, row = q >> 4, piece = q & 15;
+              const int q = q8 * 64 + lane_e, row = q >> 4, piece = q & 15;
               *reinterpret_cast<u32x4*>(po + (size_t)(32 * mb + row) * DC + piece * 8) =
                   *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * ROWB + piece * 16);
             }
