@@ -17,7 +17,7 @@
 namespace mla {
 
 // off[b] = sum_{b' < b} ceil(S_b' / TT) with S clamped; header {total, per, groups}; and the
-// start record of every unit that owns tiles (see UnitStart).
+// start record of every unit (see UnitStart).
 __device__ void build_plan(const int32_t* __restrict__ seq_lens,
                            const int32_t* __restrict__ page_table, int B, int max_pages, int G,
                            int TT, Plan* __restrict__ plan) {
@@ -74,9 +74,13 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens,
     rec.nj = (S + TT - 1) / TT;
     rec.S = S;
     rec.page = page;
-    rec.pad[0] = rec.pad[1] = rec.pad[2] = 0;
+    rec.n = min(per, total - u * per);
+    rec.pad[0] = rec.pad[1] = 0;
     start[u] = rec;
   };
+  // idle units (no tiles: u * per >= total) get an all-zero record
+  for (int u = tid; u < g; u += 256)
+    if ((long long)u * per >= total) start[u] = UnitStart{0, 0, 0, 0, 0, 0, {0, 0}};
   if (B <= kSeqInLds) {
     // every unit on its own: its sequence by binary search over the offsets in LDS (the last
     // b with off[b] <= u*per; sequences with no tiles share their successor's offset and are

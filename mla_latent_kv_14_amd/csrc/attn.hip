@@ -10,8 +10,9 @@
 // The combine kernel merges the segments of a sequence and applies W_UV.
 //
 // Softmax runs in the log2 domain (scale folded with log2 e). The running max is updated
-// lazily: a head's reference max only moves when a tile beats it by more than 2^8, so most
-// tiles need no rescale of the accumulator; weights stay <= 256, exact in the final ratio.
+// lazily: a head's reference max only moves when a tile beats it by more than 64 (log2 units),
+// so most tiles need no rescale of the accumulator; weights stay below 2^64, far inside the
+// fp32 and bf16 range, and the final ratio does not depend on the reference.
 // p is rounded to bf16 for the value MFMA and l sums the rounded weights, so the weights that
 // multiply the values are exactly normalised.
 #include "device.h"
@@ -28,26 +29,26 @@ struct Cursor {
   int S;   // clamped sequence length
 };
 
-__device__ __forceinline__ int seq_tiles(const int32_t* off, int B, int total, int b) {
-  return (b + 1 < B ? ld_uniform(off + b + 1) : total) - ld_uniform(off + b);
+__device__ __forceinline__ int seq_tiles(const Plan* plan, int B, int b) {
+  const int32_t* off = plan_off(plan);
+  return (b + 1 < B ? ld_uniform(off + b + 1) : ld_uniform(&plan->total)) - ld_uniform(off + b);
 }
 
-__device__ __forceinline__ void cursor_at(Cursor& c, int b, int j, const int32_t* off,
-                                          const int32_t* seq_lens, int B, int total,
-                                          int max_pages) {
+__device__ __forceinline__ void cursor_at(Cursor& c, int b, int j, const Plan* plan,
+                                          const int32_t* seq_lens, int B, int max_pages) {
   c.b = b;
   c.j = j;
-  c.nj = seq_tiles(off, B, total, b);
+  c.nj = seq_tiles(plan, B, b);
   c.S = clamp_len(ld_uniform(seq_lens + b), max_pages);
 }
 
-__device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* off,
-                                            const int32_t* seq_lens, int B, int total,
-                                            int max_pages) {
+// The next tile of the stream; the plan is read only when a sequence ends.
+__device__ __forceinline__ void cursor_next(Cursor& c, const Plan* plan, const int32_t* seq_lens,
+                                            int B, int max_pages) {
   if (++c.j < c.nj) return;
   int b = c.b + 1;
-  while (b < B && seq_tiles(off, B, total, b) == 0) ++b;
-  if (b < B) cursor_at(c, b, 0, off, seq_lens, B, total, max_pages);
+  while (b < B && seq_tiles(plan, B, b) == 0) ++b;
+  if (b < B) cursor_at(c, b, 0, plan, seq_lens, B, max_pages);
 }
 
 // ================================================================ DeepSeek widths
@@ -94,7 +95,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
                      const char* __restrict__ kv, const int32_t* __restrict__ page_table,
                      const int32_t* __restrict__ seq_lens, int B, int max_pages, int num_pages,
-                     const Plan* __restrict__ plan, float scale_log2,
+                     const Plan* __restrict__ plan, int G, float scale_log2,
                      uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   using namespace ds;
   __shared__ __attribute__((aligned(1024))) char lds_tiles[NBUF * Tile::BYTES];
@@ -108,15 +109,12 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
   // work group -> (tile stream g, head half hh); both halves of g share an XCD
   const int x = blockIdx.x;
   const int g = 8 * (x >> 4) + (x & 7), hh = (x >> 3) & 1;
-  const int total = ld_uniform(&plan->total), per = ld_uniform(&plan->per);
-  const int u0 = g * per;
-  const int u1 = min(u0 + per, total);
-  if (u0 >= u1) return;
-  const int32_t* off = plan_off(plan);
-  const int n = u1 - u0;
+  // the unit record is the only load before the queries and the first tile (ids past G, from
+  // padding the grid to whole groups of 16, read the last record and leave)
+  const UnitStart us = load_unit(plan, B, g < G ? g : G - 1);
+  const int n = g < G ? us.n : 0;  // tiles of this unit
+  if (n <= 0) return;
   MLA_LDS char* tiles = (MLA_LDS char*)lds_tiles;
-
-  const UnitStart us = load_unit(plan, B, g);
   const Cursor c0 = {us.b, us.j, us.nj, us.S};  // the unit's first tile
 
   if (wave < 4) {
@@ -258,7 +256,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
             part_lse[(size_t)(ca.b + g) * H + head] = (m_ref + log2f_fast(lt)) * kLn2;
           }
         }
-        cursor_next(ca, off, seq_lens, B, total, max_pages);
+        cursor_next(ca, plan, seq_lens, B, max_pages);
       }
       block_sync_tagged<0>();
     }
@@ -314,7 +312,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
     };
     auto advance = [&]() {
       ++issued;
-      cursor_next(lc, off, seq_lens, B, total, max_pages);
+      cursor_next(lc, plan, seq_lens, B, max_pages);
     };
     auto issue_next = [&]() {
       lookup();
@@ -442,7 +440,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         block_sync_tagged<1>();  // P of tile r+1 visible; tile r free
       }
       cb.j += seg - 1;
-      cursor_next(cb, off, seq_lens, B, total, max_pages);
+      cursor_next(cb, plan, seq_lens, B, max_pages);
     }
     wait_vmcnt<0>();
   }
@@ -469,7 +467,7 @@ __global__ void __launch_bounds__(256)
 attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
                     const char* __restrict__ kv, const int32_t* __restrict__ page_table,
                     const int32_t* __restrict__ seq_lens, int B, int max_pages, int num_pages,
-                    const Plan* __restrict__ plan, float scale_log2,
+                    const Plan* __restrict__ plan, int G, float scale_log2,
                     uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   using namespace m2;
   __shared__ __attribute__((aligned(1024))) char lds_tiles[kAttnWavesMha2Mla][NBUF * Tile::BYTES];
@@ -477,15 +475,11 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int g = blockIdx.x * kAttnWavesMha2Mla + wave;  // plan unit = wave
-  const int total = ld_uniform(&plan->total), per = ld_uniform(&plan->per);
-  const int u0 = g * per;
-  const int u1 = min(u0 + per, total);
-  if (u0 >= u1) return;
-  const int32_t* off = plan_off(plan);
-  const int n = u1 - u0;
+  const UnitStart us = load_unit(plan, B, g < G ? g : G - 1);
+  const int n = g < G ? us.n : 0;  // tiles of this unit
+  if (n <= 0) return;
   MLA_LDS char* tiles = (MLA_LDS char*)lds_tiles[wave];
 
-  const UnitStart us = load_unit(plan, B, g);
   Cursor lc = {us.b, us.j, us.nj, us.S};
   Cursor cc = lc;
   uint32_t dmo[IPW];  // lane offsets of a full-tile load
@@ -522,7 +516,7 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   int issued = 0;
   for (; issued < NBUF - 1 && issued < n; ++issued) {
     issue(lc, issued % NBUF);
-    cursor_next(lc, off, seq_lens, B, total, max_pages);
+    cursor_next(lc, plan, seq_lens, B, max_pages);
   }
   for (int it = 0; it < n; ++it) {
     if (seg_start) {
@@ -535,7 +529,7 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
     else wait_vmcnt<0>();
     if (issued < n) {
       issue(lc, issued % NBUF);
-      cursor_next(lc, off, seq_lens, B, total, max_pages);
+      cursor_next(lc, plan, seq_lens, B, max_pages);
       ++issued;
     }
     const MLA_LDS char* kb = tiles + (it % NBUF) * Tile::BYTES;
@@ -631,7 +625,7 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       }
       seg_start = true;
     }
-    cursor_next(cc, off, seq_lens, B, total, max_pages);
+    cursor_next(cc, plan, seq_lens, B, max_pages);
   }
 }
 
@@ -645,12 +639,12 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
     const int blocks = 16 * ((G + 7) / 8);
     attn_deepseek_kernel<<<blocks, 64 * ds::NW, 0, stream>>>(
         (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv, page_table, seq_lens,
-        B, max_pages, num_pages, (const Plan*)plan, scale_log2, (uint16_t*)part_o, part_lse);
+        B, max_pages, num_pages, (const Plan*)plan, G, scale_log2, (uint16_t*)part_o, part_lse);
   } else {
     const int blocks = (G + kAttnWavesMha2Mla - 1) / kAttnWavesMha2Mla;
     attn_mha2mla_kernel<<<blocks, 64 * kAttnWavesMha2Mla, 0, stream>>>(
         (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv, page_table, seq_lens,
-        B, max_pages, num_pages, (const Plan*)plan, scale_log2, (uint16_t*)part_o, part_lse);
+        B, max_pages, num_pages, (const Plan*)plan, G, scale_log2, (uint16_t*)part_o, part_lse);
   }
   return hipGetLastError();
 }

@@ -146,15 +146,16 @@ struct Plan {
   // followed by int32_t off[B]: first tile of sequence b,
   // then (at a 32-byte boundary) UnitStart start[G]
 };
-// Where plan unit g starts (written for units that own tiles), so that a work group finds its
-// first tile, its sequence and the page of that tile with one scalar load.
+// Where plan unit g starts, written for every unit, so that a work group finds its tile count,
+// its first tile, that tile's sequence and page with one scalar load and no other dependency.
 struct UnitStart {
   int32_t b;     // sequence holding the unit's first tile
   int32_t j;     // that tile's index inside the sequence
   int32_t nj;    // tiles of sequence b
   int32_t S;     // clamped length of sequence b
   int32_t page;  // page-table entry of the page holding tile j (as stored; clamped at use)
-  int32_t pad[3];
+  int32_t n;     // tiles the unit owns; 0 for an idle unit (whose other fields are 0)
+  int32_t pad[2];
 };
 __device__ __forceinline__ const int32_t* plan_off(const Plan* p) {
   return reinterpret_cast<const int32_t*>(p + 1);
@@ -181,6 +182,7 @@ __device__ __forceinline__ UnitStart load_unit(const Plan* p, int B, int g) {
   u.nj = ld_uniform(w + 2);
   u.S = ld_uniform(w + 3);
   u.page = ld_uniform(w + 4);
+  u.n = ld_uniform(w + 5);
   return u;
 }
 
