@@ -63,10 +63,10 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const Plan* plan, const i
 //           those heads is then entirely its own (row maxima by two lane exchanges), and it
 //           writes the bf16 weights P, the per-head rescale factors and, at the end of a
 //           segment, 1/l and the lse.
-//   values  (waves 4..7) wave v accumulates O[64 heads x 128 latent columns] += P * V with
-//           16 MFMA 32x32x16 per tile (value operand by transposing LDS reads), and issues the
-//           tile loads; at the end of a segment it normalises, stages its block in the part of
-//           the finished tile that only it read, and writes whole rows.
+//   values  (waves 4..7) wave v accumulates O^T[128 latent columns x 64 heads] += V^T * P^T
+//           with 16 MFMA 32x32x16 per tile (value operand by transposing LDS reads), and issues
+//           the tile loads; at the end of a segment it normalises, stages its block in the part
+//           of the finished tile that only it read, and writes whole rows.
 // In round r the score team works on tile r+1 while the value team works on tile r. The ring
 // has four 36 KiB buffers: tiles r and r+1 in use, r+2 and r+3 in flight, so a load has two
 // rounds to land. P, the rescale factors and 1/l are double buffered by tile parity.
@@ -366,19 +366,18 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
               *reinterpret_cast<const MLA_LDS u32x4*>((const MLA_LDS char*)lds_flag[pb]);
           if (fl[0] | fl[1] | fl[2] | fl[3]) {  // rare: some reference maxima moved
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb) {
+              const float a = lds_alpha[pb][32 * mb + t32];  // this lane's head
 #pragma unroll
-              for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x4 a4 = *reinterpret_cast<const MLA_LDS f32x4*>(
-                    (const MLA_LDS char*)lds_alpha[pb] + (32 * mb + 8 * r4 + 4 * hi) * 4);
+              for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) acc[mb][nb][4 * r4 + e] *= a4[e];
-              }
+                for (int i = 0; i < 16; ++i) acc[mb][nb][i] *= a;
+            }
           }
         }
-        // O[64 heads][128 columns] += P * V
+        // O^T[128 columns][64 heads] += V^T * P^T: the operand registers of P * V serve
+        // unchanged with the roles swapped, and each lane then holds one head and four
+        // consecutive columns (32nb + 8r4 + 4hi + e) per block
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           bf16x8 pa[2], vb[4];
@@ -397,7 +396,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
           for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
-              acc[mb][nb] = mfma_32x32x16(pa[mb], vb[nb], acc[mb][nb]);
+              acc[mb][nb] = mfma_32x32x16(vb[nb], pa[mb], acc[mb][nb]);
         }
         if (load) {
           Tile::issue_part<4, 6, 9>(nbase, nvalid, dmo, ndst, vw, lane);
@@ -405,34 +404,40 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         }
         if (k == seg - 1) {
           // Normalise and write this wave's block of the segment's partial. It is staged, 32
-          // heads at a time, in the bytes of tile r that only this wave read (its own columns
-          // of every row: 256 bytes at 256vw of each 1152-byte row), then written as whole
-          // 256-byte rows.
+          // heads at a time, in the bytes of tile r that only this wave read (256 bytes at
+          // 256vw of each 1152-byte row), then written as whole 256-byte rows.
           MLA_LDS char* stg = tiles + (r % NBUF) * Tile::BYTES + 256 * vw;
           // (the slot and lane pass through empty asm so that the store addresses are formed
           // here, not kept in registers through the whole segment)
           int slot_e = slot, lane_e = lane;
           asm volatile("" : "+s"(slot_e), "+v"(lane_e));
           uint16_t* po = part_o + ((size_t)slot_e * H + HG * hh) * DC + 128 * vw;
+          // Staging row t32 is head 32mb + t32; its 8-byte chunk c (four columns) sits at chunk
+          // c ^ sw(row), sw(row) = 2((row >> 1) & 7), which spreads the 64 lanes of a write
+          // over all banks (two per bank) and keeps 16-byte pieces whole for the read-back.
+          const int t32e = lane_e & 31;
+          const uint32_t wrow = t32e * ROWB + 8 * (lane_e >> 5);
+          const int wsw = 2 * ((t32e >> 1) & 7);
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) {
+            const float il = lds_invl[pb][32 * mb + t32e];
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const f32x4 il = *reinterpret_cast<const MLA_LDS f32x4*>(
-                  (const MLA_LDS char*)lds_invl[pb] + (32 * mb + 8 * r4 + 4 * hi) * 4);
+            for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-              for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  *reinterpret_cast<MLA_LDS __bf16*>(
-                      stg + (8 * r4 + 4 * hi + e) * ROWB + (32 * nb + t32) * 2) =
-                      (__bf16)(acc[mb][nb][4 * r4 + e] * il[e]);
-            }
+              for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x16& o = acc[mb][nb];
+                const uint32_t lo = pack_bf16x2(o[4 * r4] * il, o[4 * r4 + 1] * il);
+                const uint32_t hi2 = pack_bf16x2(o[4 * r4 + 2] * il, o[4 * r4 + 3] * il);
+                *reinterpret_cast<MLA_LDS uint64_t*>(stg + wrow + 8 * ((8 * nb + 2 * r4) ^ wsw)) =
+                    (uint64_t)lo | ((uint64_t)hi2 << 32);
+              }
 #pragma unroll
             for (int q8 = 0; q8 < 8; ++q8) {  // 32 rows x 16 pieces of 16 bytes
               const int q = q8 * 64 + lane_e, row = q >> 4, piece = q & 15;
+              const int rsw = 2 * ((row >> 1) & 7);
               *reinterpret_cast<u32x4*>(po + (size_t)(32 * mb + row) * DC + piece * 8) =
-                  *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * ROWB + piece * 16);
+                  *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * ROWB +
+                                                          8 * ((2 * piece) ^ rsw));
             }
           }
         }

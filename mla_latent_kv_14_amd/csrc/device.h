@@ -8,6 +8,7 @@ namespace mla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -130,6 +131,12 @@ __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_e
 __device__ __forceinline__ float log2f_fast(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ uint16_t bf16_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+// Two floats rounded (RNE) to bf16 and packed, lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
 
 // ---------------------------------------------------------------- work plan
 // The cache of all sequences is viewed as one stream of tiles of TT tokens (32 for the DeepSeek
