@@ -9,7 +9,8 @@
 // straight from global memory (8 consecutive d per lane), fp32 accumulation, bf16 (RNE) out.
 // The kernel streams 2*H*d_n*d_c bytes of weight once; it is HBM-bound.
 //
-// One extra block (the last) writes the work plan for the attention kernel (see Plan in
+// One extra block (the first, so that it is dispatched at once: its chain of dependent loads is
+// the longest in the kernel) writes the work plan for the attention kernel (see Plan in
 // device.h), in parallel with the others.
 #include "device.h"
 #include "kernels.h"
@@ -18,13 +19,17 @@ namespace mla {
 
 // off[b] = sum_{b' < b} ceil(S_b' / TT) with S clamped; header {total, per, groups}; and the
 // start record of every unit (see UnitStart).
+// Batches up to this size keep offsets and lengths in LDS (the scratch passed in).
+constexpr int kSeqInLds = 4096;
+constexpr int kPlanLdsBytes = (2 * kSeqInLds + 8) * 4;
+
 __device__ void build_plan(const int32_t* __restrict__ seq_lens,
                            const int32_t* __restrict__ page_table, int B, int max_pages, int G,
-                           int TT, Plan* __restrict__ plan) {
-  constexpr int kSeqInLds = 4096;  // batches up to this size keep offsets and lengths in LDS
-  __shared__ int32_t wave_tot[4];
-  __shared__ int32_t carry;
-  __shared__ int32_t seq_off[kSeqInLds], seq_len[kSeqInLds];
+                           int TT, Plan* __restrict__ plan, MLA_LDS char* scratch) {
+  MLA_LDS int32_t* seq_off = (MLA_LDS int32_t*)scratch;
+  MLA_LDS int32_t* seq_len = seq_off + kSeqInLds;
+  MLA_LDS int32_t* wave_tot = seq_len + kSeqInLds;
+  MLA_LDS int32_t& carry = wave_tot[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) carry = 0;
   __syncthreads();
@@ -136,15 +141,17 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
   constexpr int NCHUNK = DN * ROWB / 16;    // 16-byte pieces of the W block
   static_assert(NCHUNK % 64 == 0, "W block must be whole KiB");
   static_assert(DN % 8 == 0 && CB % 16 == 0 && DC % CB == 0, "shape");
-  __shared__ __attribute__((aligned(16))) char wt[DNP * ROWB];
+  // the W block, or in the plan block the plan builder's scratch
+  constexpr int LDS_BYTES = DNP * ROWB > kPlanLdsBytes ? DNP * ROWB : kPlanLdsBytes;
+  __shared__ __attribute__((aligned(16))) char wt[LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = DC / CB;
-  if (blockIdx.x == H * nblk) {  // the extra last block writes the work plan, nothing else
-    build_plan(seq_lens, page_table, B, max_pages, G, TT, plan);
+  if (blockIdx.x == 0) {  // the extra first block writes the work plan, nothing else
+    build_plan(seq_lens, page_table, B, max_pages, G, TT, plan, (MLA_LDS char*)wt);
     return;
   }
-  const int h = blockIdx.x / nblk, cblk = blockIdx.x % nblk;
+  const int h = (blockIdx.x - 1) / nblk, cblk = (blockIdx.x - 1) % nblk;
 
   // ---- stage W_UK[h][0:DN][cblk*CB : +CB] in LDS
   const char* Wg = reinterpret_cast<const char*>(W_UK + (size_t)h * DN * DC + (size_t)cblk * CB);
@@ -177,15 +184,30 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
       bq[ks] = __builtin_bit_cast(bf16x8, raw & keep);
     }
   };
-  bf16x8 bq[KS];
-  load_q(0, bq);
+  // up to QB sequence blocks of q_nope are loaded at a time, all in flight together (the first
+  // ones while W is in flight)
+  constexpr int QB = 4;
+  bf16x8 bq[QB][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) settle(bq[ks]);  // issued here, with W still in flight
+  for (int i = 0; i < QB; ++i)
+    if (i < nblocks) {
+      load_q(i, bq[i]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) settle(bq[i][ks]);
+    }
   wait_vmcnt<0>();
   __syncthreads();
 
-  for (int nb = 0; nb < nblocks; ++nb) {
-    if (nb > 0) load_q(nb, bq);
+  for (int nb0 = 0; nb0 < nblocks; nb0 += QB) {
+    if (nb0 > 0) {
+#pragma unroll
+      for (int i = 0; i < QB; ++i)
+        if (nb0 + i < nblocks) load_q(nb0 + i, bq[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+    const int nb = nb0 + i;
+    if (nb >= nblocks) break;
     const int b = nb * 16 + q16;
     for (int mb = wave; mb < MBLK; mb += 4) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -195,13 +217,14 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
         const int row1 = row0 + 4;
         const uint32_t o0 = row0 * ROWB + ((mb ^ (row0 % UNITS)) * 32) + 8 * (q16 & 3);
         const uint32_t o1 = row1 * ROWB + ((mb ^ (row1 % UNITS)) * 32) + 8 * (q16 & 3);
-        acc = mfma_16x16x32(cat4(lds_read_tr16(wl, o0), lds_read_tr16(wl, o1)), bq[ks], acc);
+        acc = mfma_16x16x32(cat4(lds_read_tr16(wl, o0), lds_read_tr16(wl, o1)), bq[i][ks], acc);
       }
       if (b < B) {
         const int c0 = cblk * CB + mb * 16 + 4 * G16;
         bf16x4 o = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
         *reinterpret_cast<bf16x4*>(q_abs + ((size_t)b * H + h) * DC + c0) = o;
       }
+    }
     }
   }
 }
