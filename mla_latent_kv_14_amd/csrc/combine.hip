@@ -22,7 +22,7 @@
 namespace mla {
 
 namespace comb {
-constexpr int NT = 512;   // threads per work group
+constexpr int NT = 1024;  // threads per work group
 constexpr int SEQ = 16;   // sequences per work group (the MFMA N)
 constexpr int EB = 64;    // output columns per work group
 constexpr int CAP = 8;    // slots per thread whose loads are issued together

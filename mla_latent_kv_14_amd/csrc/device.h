@@ -180,16 +180,18 @@ __device__ __forceinline__ const UnitStart* plan_units(const Plan* p, int B) {
 __device__ __forceinline__ UnitStart* plan_units(Plan* p, int B) {
   return reinterpret_cast<UnitStart*>(reinterpret_cast<char*>(p) + plan_units_offset(B));
 }
-// The unit record through the scalar path (written by an earlier kernel, read-only here).
+// The unit record through the scalar path (written by an earlier kernel, read-only here), as
+// one 32-byte load: no field waits for a second round trip, whatever branches on which field.
 __device__ __forceinline__ UnitStart load_unit(const Plan* p, int B, int g) {
-  const int32_t* w = reinterpret_cast<const int32_t*>(plan_units(p, B) + g);
+  typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 w = ld_uniform(reinterpret_cast<const i32x8*>(plan_units(p, B) + g));
   UnitStart u;
-  u.b = ld_uniform(w + 0);
-  u.j = ld_uniform(w + 1);
-  u.nj = ld_uniform(w + 2);
-  u.S = ld_uniform(w + 3);
-  u.page = ld_uniform(w + 4);
-  u.n = ld_uniform(w + 5);
+  u.b = w[0];
+  u.j = w[1];
+  u.nj = w[2];
+  u.S = w[3];
+  u.page = w[4];
+  u.n = w[5];
   return u;
 }
 
