@@ -4,13 +4,14 @@
 //   o_lat[c]   = sum_s exp(lse_s - lse_b) * o_s[c]         (fp32; o_s are normalised partials)
 //   out[b,h,e] = sum_c o_lat[c] * W_UV[h,c,e]              (lpnh.cn/news/2494972 S2.1, v = c_kv W_uv)
 //
-// One work group per (head h, group of 16 sequences, half of the d_v output columns). The two
-// halves of a (head, group) get block ids 8 apart, which places them on the same XCD: the
-// second read of the head's partials is served by that XCD's L2.
+// One work group per (head h, group of 16 sequences, block of EB output columns). At the
+// DeepSeek widths EB = d_v = 128, so a head's partials are read by one work group; at the
+// MHA2MLA widths (small W_UV) EB = 64 and the two halves of a (head, group) get block ids 8
+// apart, which places them on the same XCD: the second read of the partials hits its L2.
 //
-// The W_UV block [d_latent x 64] goes to LDS by direct loads (32-byte units XOR-swizzled by
+// The W_UV block [d_latent x EB] goes to LDS by direct loads (32-byte units XOR-swizzled by
 // row) and stays in flight while the partials are merged. For the merge every thread owns one
-// 16-byte column chunk of a sequence's latent row (or a quarter of its slots, when the rows are
+// 16-byte column chunk of a sequence's latent row (or 1/J of its slots, when the rows are
 // short); it issues the loads of all its slots (rows and their lse values) at once, forms the
 // merged lse from the values it holds, and sums the weighted rows in fp32. The merged rows are
 // rounded once to bf16 in LDS, then out^T[e, b] = W^T[e, c] * o_lat^T[c, b] runs on 16x16x32
@@ -24,11 +25,13 @@ namespace mla {
 namespace comb {
 constexpr int NT = 1024;  // threads per work group
 constexpr int SEQ = 16;   // sequences per work group (the MFMA N)
-constexpr int EB = 64;    // output columns per work group
 constexpr int CAP = 8;    // slots per thread whose loads are issued together
+// Output columns per work group at the DeepSeek widths: all 128 of a head, so the head's
+// partials cross the memory system once (two column halves would read them twice).
+constexpr int EB_DS = 128;
 }  // namespace comb
 
-template <int H, int DC, int DV>
+template <int H, int DC, int DV, int EB>
 __global__ void __launch_bounds__(comb::NT)
 combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
                const Plan* __restrict__ plan, const uint16_t* __restrict__ W_UV,
@@ -42,7 +45,8 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
   constexpr int ITEMS = SEQ * NCH;    // (sequence, chunk) items of a work group
   constexpr int J = ITEMS >= NT ? 1 : NT / ITEMS;  // threads sharing one item (split by slot)
   constexpr int IPT = ITEMS >= NT ? ITEMS / NT : 1; // items per thread
-  static_assert(DV == 2 * EB, "two column halves per head");
+  constexpr int NEB = DV / EB;  // column blocks per head: 1, or 2 (paired 8 ids apart)
+  static_assert(NEB * EB == DV && (NEB == 1 || NEB == 2), "column blocks");
   static_assert(NCHUNK % 64 == 0 && DC % 32 == 0, "shape");
   static_assert(ITEMS * J == NT * IPT && (J & (J - 1)) == 0 && J <= 64, "item split");
   __shared__ __attribute__((aligned(16))) char lds_w[DC * ROWB];
@@ -51,8 +55,8 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int x = blockIdx.x;
-  const int eblk = (x >> 3) & 1;
-  const int grp = ((x >> 4) << 3) | (x & 7);  // (sequence group, head)
+  const int eblk = NEB == 2 ? (x >> 3) & 1 : 0;
+  const int grp = NEB == 2 ? ((x >> 4) << 3) | (x & 7) : x;  // (sequence group, head)
   if (grp >= groups) return;                  // padding block: leaves before any barrier
   const int h = grp % H, b0 = (grp / H) * SEQ;
   MLA_LDS char* wl = (MLA_LDS char*)lds_w;
@@ -194,13 +198,15 @@ hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, 
   (void)seq_lens;
   (void)max_pages;
   const int groups = H * ((B + comb::SEQ - 1) / comb::SEQ);
-  const int blocks = 16 * ((groups + 7) / 8);  // pairs of column halves, 8 ids apart
   if (shape == kShapeDeepSeek) {
-    combine_kernel<128, 512, 128><<<blocks, comb::NT, 0, stream>>>(
+    constexpr int EB = comb::EB_DS;
+    const int blocks = EB == 128 ? groups : 16 * ((groups + 7) / 8);
+    combine_kernel<128, 512, 128, EB><<<blocks, comb::NT, 0, stream>>>(
         (const uint16_t*)part_o, part_lse, (const Plan*)plan, (const uint16_t*)W_UV,
         (uint16_t*)out, lse_out, B, groups);
   } else {
-    combine_kernel<32, 64, 128><<<blocks, comb::NT, 0, stream>>>(
+    const int blocks = 16 * ((groups + 7) / 8);  // pairs of column halves, 8 ids apart
+    combine_kernel<32, 64, 128, 64><<<blocks, comb::NT, 0, stream>>>(
         (const uint16_t*)part_o, part_lse, (const Plan*)plan, (const uint16_t*)W_UV,
         (uint16_t*)out, lse_out, B, groups);
   }
