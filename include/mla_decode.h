@@ -23,7 +23,8 @@
  *   - tensors are dense row-major, in device memory, 16-byte aligned; bf16 is stored as its
  *     16-bit pattern; int32 is native.
  *   - the caller allocates and owns every buffer, including the workspace. The library
- *     allocates no device memory, keeps no per-call state, and never synchronises the stream.
+ *     allocates no device memory, keeps no per-call state, and does not synchronise the
+ *     stream (except in the MLA_CHECK mode below).
  *     Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  *     returns; results are valid once the stream reaches that point.
  *   - argument errors are reported by the return value before anything is enqueued; a HIP
@@ -31,6 +32,10 @@
  *   - device-resident values are clamped, never trusted: seq_lens[b] is clamped to
  *     [0, max_pages_per_seq * 64] and page ids to [0, num_pages - 1], so a bad table gives
  *     wrong numbers, not a memory fault. A sequence with S_b <= 0 gets out = 0, lse = -inf.
+ *   - with MLA_CHECK=1 in the environment, mla_decode and mla_decode_timed first validate
+ *     seq_lens and the page-table entries the sequences use on the device, synchronise the
+ *     stream, and return MLA_ERR_DEVICE_CHECK (with nothing else enqueued) when one is out of
+ *     range. This debugging mode is the only case in which the library synchronises.
  *   - page-table entries at or past ceil(S_b / 64) and cache slots at or past S_b are never
  *     read into the result (they may hold anything, including NaN).
  */
@@ -51,7 +56,10 @@ typedef enum {
     MLA_ERR_MISALIGNED = 3,  /* a tensor pointer is not 16-byte aligned                   */
     MLA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than mla_decode_workspace_bytes */
     MLA_ERR_UNSUPPORTED = 5, /* head/width combination or page size not built             */
-    MLA_ERR_HIP = 6          /* the HIP runtime reported an error while enqueueing        */
+    MLA_ERR_HIP = 6,         /* the HIP runtime reported an error while enqueueing        */
+    MLA_ERR_DEVICE_CHECK = 7 /* MLA_CHECK=1 only: a seq_lens value is outside
+                                [0, max_seq_len], or a page-table entry that its sequence uses
+                                is outside [0, num_pages); nothing else was enqueued         */
 } mla_status_t;
 
 typedef struct {

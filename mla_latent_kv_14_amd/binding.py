@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(HERE, "libmla_decode.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "mla_decode.h")
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL_ARG", 2: "MLA_ERR_BAD_DIMS", 3: "MLA_ERR_MISALIGNED",
-          4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_UNSUPPORTED", 6: "MLA_ERR_HIP"}
+          4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_UNSUPPORTED", 6: "MLA_ERR_HIP",
+          7: "MLA_ERR_DEVICE_CHECK"}
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 

@@ -2,6 +2,7 @@
 // launches (absorb -> attention -> combine) on the caller's stream. No allocation, no sync.
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "mla_decode.h"
@@ -62,6 +63,12 @@ int plan_units(const mla_dims_t* d, const ShapeInfo& s) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// MLA_CHECK=1 in the environment: validate device-resident inputs before each decode.
+bool check_mode() {
+  const char* e = getenv("MLA_CHECK");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
 struct Layout {
   size_t plan, q_abs, part_lse, part_o, total;
 };
@@ -116,6 +123,19 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
   const hipStream_t hs = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const int B = dims->batch, mp = dims->max_pages_per_seq;
+  if (check_mode()) {
+    // validate the device-resident inputs first; the flag lives in the query region, which
+    // the decode overwrites afterwards
+    int* flag = (int*)(ws + L.q_abs);
+    int host_flag = 0;
+    st = hip_status(mla::launch_check(seq_lens, page_table, B, mp, dims->num_pages,
+                                      max_len(dims), flag, hs));
+    if (st != MLA_OK) return st;
+    st = hip_status(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, hs));
+    if (st != MLA_OK) return st;
+    if ((st = hip_status(hipStreamSynchronize(hs))) != MLA_OK) return st;
+    if (host_flag != 0) return MLA_ERR_DEVICE_CHECK;
+  }
   const int G = plan_units(dims, s);
   const float scale = dims->softmax_scale > 0.f ? dims->softmax_scale
                                                 : 1.0f / sqrtf((float)(s.DN + s.DR));
@@ -177,6 +197,8 @@ const char* mla_status_str(mla_status_t s) {
     case MLA_ERR_WORKSPACE: return "workspace missing or smaller than mla_decode_workspace_bytes";
     case MLA_ERR_UNSUPPORTED: return "head/width combination or page size not supported";
     case MLA_ERR_HIP: return "HIP runtime error while enqueueing";
+    case MLA_ERR_DEVICE_CHECK:
+      return "MLA_CHECK: a sequence length or a used page-table entry is out of range";
   }
   return "unknown status";
 }

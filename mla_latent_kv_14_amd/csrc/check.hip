@@ -1,0 +1,38 @@
+// Validation of the device-resident inputs, run before the decode when MLA_CHECK=1 is set:
+// every S_b must lie in [0, max_len] and every page-table entry that the sequence uses
+// (logical pages j < ceil(S_b / 64)) must name a pool page in [0, num_pages). Violations set
+// bits of *flag (1: a length, 2: a page id); the fast path itself only clamps them.
+#include "device.h"
+#include "kernels.h"
+
+namespace mla {
+
+__global__ void check_clear_kernel(int* flag) { *flag = 0; }
+
+__global__ void __launch_bounds__(256)
+check_inputs_kernel(const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table,
+                    int B, int max_pages, int num_pages, int max_len, int* flag) {
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    const int S = seq_lens[b];
+    if (S < 0 || S > max_len) {
+      if (threadIdx.x == 0) atomicOr(flag, 1);
+      continue;
+    }
+    const int np = (S + kPage - 1) / kPage;  // <= max_pages, as max_len <= max_pages * 64
+    for (int j = threadIdx.x; j < np; j += blockDim.x) {
+      const int p = page_table[(size_t)b * max_pages + j];
+      if (p < 0 || p >= num_pages) atomicOr(flag, 2);
+    }
+  }
+}
+
+hipError_t launch_check(const int32_t* seq_lens, const int32_t* page_table, int B, int max_pages,
+                        int num_pages, int max_len, int* flag, hipStream_t stream) {
+  check_clear_kernel<<<1, 1, 0, stream>>>(flag);
+  const int blocks = B < 1024 ? B : 1024;
+  check_inputs_kernel<<<blocks, 256, 0, stream>>>(seq_lens, page_table, B, max_pages, num_pages,
+                                                   max_len, flag);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -28,6 +28,10 @@ hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, 
                           const int32_t* seq_lens, const void* W_UV, void* out, float* lse_out,
                           int B, int H, int max_pages, hipStream_t stream);
 
+// Sets bits of *flag (cleared first) for out-of-range lengths (1) or used page ids (2).
+hipError_t launch_check(const int32_t* seq_lens, const int32_t* page_table, int B, int max_pages,
+                        int num_pages, int max_len, int* flag, hipStream_t stream);
+
 hipError_t launch_gather(int d_latent, int d_rope, const void* kv, const int32_t* page_table,
                          const int32_t* seq_lens, int B, int max_pages, int num_pages, int S_max,
                          void* dst, hipStream_t stream);

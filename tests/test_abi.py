@@ -125,7 +125,7 @@ def test_gather_rejects_bad_args():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         assert M.lib().mla_status_str(code)
     assert M.lib().mla_last_hip_error() is not None
 
