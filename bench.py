@@ -211,20 +211,24 @@ def run(args):
     return res
 
 
-def cpu_baseline(inp, alg):
-    """The fp64 oracle, as it stands, on the host cores: every (b, h) of one input set."""
+def cpu_baseline(inp, alg, runs=3):
+    """The fp64 oracle, as it stands, on the host cores: every (b, h) of one input set, the
+    median of `runs` runs (each run well under a minute at every workload but the longest)."""
     import oracle
     import workloads as W
     cores = len(os.sched_getaffinity(0))
     args = W.oracle_args(inp)
-    t0 = time.perf_counter()
-    oracle.decode(*args, threads=cores)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.decode(*args, threads=cores)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     return {"value": round(alg["sumS"] / dt, 1), "unit": "KV-tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": "all %d (b,h) pairs of one input set of this workload (%d KV tokens), "
-                      "fp64, OpenMP over (b,h); %.2f s wall" % (inp["B"] * inp["H"],
-                                                              alg["sumS"], dt)}
+                      "fp64, OpenMP over (b,h); median of %d runs, %.2f s wall each"
+                      % (inp["B"] * inp["H"], alg["sumS"], runs, dt)}
 
 
 def main():
