@@ -125,10 +125,19 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
     const int cnt = count[it];
     const float* lsrc = part_lse + (size_t)first[it] * H + h;
     // merged lse: max, then sum of exponentials, over all slots of the sequence
+    // Slots past the first J*CAP (a sequence spread over many units) are taken TB at a time,
+    // each batch's loads issued together (clamped to the last slot, masked by the count).
+    constexpr int TB = 8;
     float m = -INFINITY;
 #pragma unroll
     for (int u = 0; u < CAP; ++u) m = fmaxf(m, ls[it][u]);
-    for (int s = j + J * CAP; s < cnt; s += J) m = fmaxf(m, lsrc[(size_t)s * H]);
+    for (int s0 = j + J * CAP; s0 < cnt; s0 += J * TB) {
+      float l[TB];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) l[u] = lsrc[(size_t)min(s0 + J * u, cnt - 1) * H];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) m = fmaxf(m, l[u]);  // clamped copies repeat a real value
+    }
 #pragma unroll
     for (int d = 1; d < J; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -137,7 +146,13 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
       float z = 0.f;
 #pragma unroll
       for (int u = 0; u < CAP; ++u) z += __expf(ls[it][u] - m);  // exp(-inf) = 0 past count
-      for (int s = j + J * CAP; s < cnt; s += J) z += __expf(lsrc[(size_t)s * H] - m);
+      for (int s0 = j + J * CAP; s0 < cnt; s0 += J * TB) {
+        float l[TB];
+#pragma unroll
+        for (int u = 0; u < TB; ++u) l[u] = lsrc[(size_t)min(s0 + J * u, cnt - 1) * H];
+#pragma unroll
+        for (int u = 0; u < TB; ++u) z += s0 + J * u < cnt ? __expf(l[u] - m) : 0.f;
+      }
 #pragma unroll
       for (int d = 1; d < J; d <<= 1) z += __shfl_xor(z, d, 64);
       L = m + __logf(z);
@@ -148,11 +163,21 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
         for (int e = 0; e < 8; ++e) a[e] += w * (float)v[it][u][e];
       }
       const uint16_t* src = part_o + ((size_t)first[it] * H + h) * DC + ch * 8;
-      for (int s = j + J * CAP; s < cnt; s += J) {  // sequences with more than J*CAP slots
-        const float w = __expf(lsrc[(size_t)s * H] - L);
-        const bf16x8 r = *reinterpret_cast<const bf16x8*>(src + (size_t)s * slot_stride);
+      for (int s0 = j + J * CAP; s0 < cnt; s0 += J * TB) {
+        float l[TB];
+        bf16x8 r[TB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] += w * (float)r[e];
+        for (int u = 0; u < TB; ++u) {
+          const int sc = min(s0 + J * u, cnt - 1);
+          l[u] = lsrc[(size_t)sc * H];
+          r[u] = *reinterpret_cast<const bf16x8*>(src + (size_t)sc * slot_stride);
+        }
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          const float w = s0 + J * u < cnt ? __expf(l[u] - L) : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] += w * (float)r[u][e];
+        }
       }
     }
 #pragma unroll
