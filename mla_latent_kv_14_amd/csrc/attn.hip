@@ -490,9 +490,23 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   uint32_t dmo[IPW];  // lane offsets of a full-tile load
 #pragma unroll
   for (int k = 0; k < IPW; ++k) dmo[k] = Tile::src_off(k, lane, TT);
+  // The wave keeps 64 page-table entries of the current sequence in one VGPR (lane l: entry
+  // pw_base + l) and picks them with readlane, so issuing a tile needs no scalar load (whose
+  // wait would stall the wave before every tile). A refill is one asm statement, load and wait,
+  // so the compiler adds no wait of its own before the readlane.
+  int pw_v = 0, pw_b = -1, pw_base = 0;
   auto issue = [&](const Cursor& c, int buf) {
+    const int p = c.j / Tile::TPP;
+    if (c.b != pw_b || p < pw_base || p >= pw_base + 64) {
+      pw_b = c.b;
+      pw_base = p;
+      const int idx = min(p + lane, max_pages - 1);
+      const int32_t* src = page_table + (size_t)c.b * max_pages + idx;
+      asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)"
+                   : "=v"(pw_v) : "v"(src) : "memory");
+    }
     const char* base =
-        Tile::tile_base(kv, page_table + (size_t)c.b * max_pages, c.j, num_pages);
+        Tile::base_of(kv, __builtin_amdgcn_readlane(pw_v, p - pw_base), c.j, num_pages);
     Tile::issue<1>(base, min(TT, c.S - c.j * TT), dmo, tiles + buf * Tile::BYTES, 0, lane);
   };
 
@@ -555,15 +569,26 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
     // ---- online softmax, lane = head t32 x 32 tokens
     const int valid = min(TT, cc.S - cc.j * TT);
     float mt = -INFINITY;
+    if (valid == TT) {  // a full tile (all but a sequence's last): no tail mask
 #pragma unroll
-    for (int mb2 = 0; mb2 < 2; ++mb2)
+      for (int mb2 = 0; mb2 < 2; ++mb2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * mb2 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const float v = t < valid ? s[mb2][r] * scale_log2 : -INFINITY;
-        s[mb2][r] = v;
-        mt = fmaxf(mt, v);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const float v = s[mb2][r] * scale_log2;
+          s[mb2][r] = v;
+          mt = fmaxf(mt, v);
+        }
+    } else {
+#pragma unroll
+      for (int mb2 = 0; mb2 < 2; ++mb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * mb2 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const float v = t < valid ? s[mb2][r] * scale_log2 : -INFINITY;
+          s[mb2][r] = v;
+          mt = fmaxf(mt, v);
+        }
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     float alpha = 1.f;
     int need = 0;
