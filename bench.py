@@ -257,7 +257,7 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs the decode on a single MI355X and has "
+        print("bench.py measures one GPU: the decode runs on a single MI355X and has "
               "no multi-GPU path (got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     print(json.dumps(run(args)), flush=True)
