@@ -40,6 +40,15 @@ def test_mha2mla_ragged(M, units):
     check_against_oracle(M, inp, units=units, label="mha2mla ragged")
 
 
+@pytest.mark.parametrize("dims", [DS, M2], ids=["deepseek", "mha2mla"])
+@pytest.mark.parametrize("units", [1, 2])
+def test_long_sequences_few_units(M, dims, units):
+    # a unit walks more than 64 pages of one sequence (its page-table window refills inside
+    # the unit) and then crosses into the next sequence
+    inp = _inp(dims, [64 * 150 + 7, 64 * 70], 17)
+    check_against_oracle(M, inp, units=units, label="long sequences, %d units" % units)
+
+
 def test_deepseek_many_short_sequences(M):
     lens = [1 + (7 * i) % 90 for i in range(300)]  # more sequences than units
     check_against_oracle(M, _inp(DS, lens, 13), label="deepseek 300 short")
