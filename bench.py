@@ -25,6 +25,7 @@ Attention kernel alone: sumS (d_c + d_R) 2 bytes of cache (1152 B per token) plu
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import math
 import os
@@ -82,10 +83,15 @@ class Hip:
 
 
 def source_digest():
+    """Digest of the attention kernel's sources with comments and blank space removed, so that
+    only a change to the code itself retires a stored traffic measurement."""
     h = hashlib.sha256()
     for f in ATTN_SOURCES:
-        with open(os.path.join(ROOT, "mla_latent_kv_14_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mla_latent_kv_14_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

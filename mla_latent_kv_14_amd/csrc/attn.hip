@@ -71,7 +71,7 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const Plan* plan, const i
 // has four 36 KiB buffers: tiles r and r+1 in use, r+2 and r+3 in flight, so a load has two
 // rounds to land. P, the rescale factors and 1/l are double buffered by tile parity.
 // The reference max of a head is fixed on the segment's first tile and only moves when a tile
-// beats it by more than 2^64 (log2 units); the value team then rescales its rows.
+// beats it by more than 64 in log2 units (a factor 2^64); the value team then rescales.
 namespace ds {
 constexpr int H = 128, HG = 64, DC = 512, DR = 64, DK = DC + DR, ROWB = DK * 2;
 constexpr int NBUF = 4;
