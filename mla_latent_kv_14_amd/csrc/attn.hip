@@ -108,7 +108,10 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   // work group -> (tile stream g, head half hh); both halves of g share an XCD
   const int x = blockIdx.x;
-  const int g = 8 * (x >> 4) + (x & 7), hh = (x >> 3) & 1;
+  // consecutive units (usually the parts of one sequence, which read the same queries) go to
+  // the same XCD: ids x with x % 8 == k serve units k*ceil(G/8) ..
+  const int per_xcd = (G + 7) >> 3;
+  const int g = (x & 7) * per_xcd + (x >> 4), hh = (x >> 3) & 1;
   // the unit record is the only load before the queries and the first tile (ids past G, from
   // padding the grid to whole groups of 16, read the last record and leave)
   const UnitStart us = load_unit(plan, B, g < G ? g : G - 1);
