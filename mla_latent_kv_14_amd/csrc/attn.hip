@@ -13,8 +13,10 @@
 // lazily: a head's reference max only moves when a tile beats it by more than 64 (log2 units),
 // so most tiles need no rescale of the accumulator; weights stay below 2^64, far inside the
 // fp32 and bf16 range, and the final ratio does not depend on the reference.
-// p is rounded to bf16 for the value MFMA and l sums the rounded weights, so the weights that
-// multiply the values are exactly normalised.
+// p is rounded to bf16 for the value MFMA. At the DeepSeek widths l sums the rounded weights,
+// so the weights that multiply the values are exactly normalised; at the MHA2MLA widths l sums
+// the fp32 weights (one instruction less per weight; the two sums differ by bf16 rounding noise
+// that averages out over the tokens).
 #include "device.h"
 #include "kernels.h"
 #include "paged_tile.h"
@@ -570,29 +572,27 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       s[mb2] = mfma_32x32x8(kr, qr4, a);
     }
     // ---- online softmax, lane = head t32 x 32 tokens
+    // raw logits stay unscaled: the scale enters once in the tile maximum and as one FMA in
+    // each exponent
     const int valid = min(TT, cc.S - cc.j * TT);
     float mt = -INFINITY;
     if (valid == TT) {  // a full tile (all but a sequence's last): no tail mask
 #pragma unroll
       for (int mb2 = 0; mb2 < 2; ++mb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float v = s[mb2][r] * scale_log2;
-          s[mb2][r] = v;
-          mt = fmaxf(mt, v);
-        }
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[mb2][r]);
     } else {
 #pragma unroll
       for (int mb2 = 0; mb2 < 2; ++mb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = 32 * mb2 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const float v = t < valid ? s[mb2][r] * scale_log2 : -INFINITY;
+          const float v = t < valid ? s[mb2][r] : -INFINITY;
           s[mb2][r] = v;
           mt = fmaxf(mt, v);
         }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
     float alpha = 1.f;
     int need = 0;
     if (m_used == -INFINITY) {
@@ -619,9 +619,10 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const __bf16 pb = (__bf16)exp2f_fast(s[mb2][8 * half + j] - m_used);
-          pa[2 * mb2 + half][j] = pb;
-          lsum += (float)pb;
+          const float p = exp2f_fast(__builtin_fmaf(s[mb2][8 * half + j], scale_log2, -m_used));
+          pa[2 * mb2 + half][j] = (__bf16)p;
+          lsum += p;  // the unrounded weight: l differs from the sum of the bf16 weights by
+                      // rounding noise of relative size 2^-9 / sqrt(tokens)
         }
     l_lane = l_lane * alpha + lsum;
     // ---- values: block kk holds, for lane half hi, the tokens
