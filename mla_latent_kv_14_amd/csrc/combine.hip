@@ -4,10 +4,12 @@
 //   o_lat[c]   = sum_s exp(lse_s - lse_b) * o_s[c]         (fp32; o_s are normalised partials)
 //   out[b,h,e] = sum_c o_lat[c] * W_UV[h,c,e]              (lpnh.cn/news/2494972 S2.1, v = c_kv W_uv)
 //
-// One work group per (head h, group of 16 sequences, block of EB output columns). At the
-// DeepSeek widths EB = d_v = 128, so a head's partials are read by one work group; at the
-// MHA2MLA widths (small W_UV) EB = 64 and the two halves of a (head, group) get block ids 8
-// apart, which places them on the same XCD: the second read of the partials hits its L2.
+// One work group per (head h, group of 16 sequences, block of EB output columns). With EB = 64
+// the two halves of a (head, group) get block ids 8 apart, which places them on the same XCD:
+// the second read of the partials hits its L2. At the DeepSeek widths EB = d_v = 128 (a head's
+// partials are read by one work group) when there are enough (head, group) pairs to fill the
+// chip, else EB = 64 (twice the work groups, half of W_UV each); at the MHA2MLA widths (small
+// W_UV) EB = 64.
 //
 // The W_UV block [d_latent x EB] goes to LDS by direct loads (32-byte units XOR-swizzled by
 // row) and stays in flight while the partials are merged. For the merge every thread owns one
@@ -26,9 +28,9 @@ namespace comb {
 constexpr int NT = 1024;  // threads per work group
 constexpr int SEQ = 16;   // sequences per work group (the MFMA N)
 constexpr int CAP = 8;    // slots per thread whose loads are issued together
-// Output columns per work group at the DeepSeek widths: all 128 of a head, so the head's
-// partials cross the memory system once (two column halves would read them twice).
-constexpr int EB_DS = 128;
+// At the DeepSeek widths, from this many (head, group) pairs on, a work group takes all 128
+// output columns of its head (below it, two work groups of 64 columns fill more of the chip).
+constexpr int kWholeHeadGroups = 256;
 }  // namespace comb
 
 template <int H, int DC, int DV, int EB>
@@ -223,10 +225,13 @@ hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, 
   (void)seq_lens;
   (void)max_pages;
   const int groups = H * ((B + comb::SEQ - 1) / comb::SEQ);
-  if (shape == kShapeDeepSeek) {
-    constexpr int EB = comb::EB_DS;
-    const int blocks = EB == 128 ? groups : 16 * ((groups + 7) / 8);
-    combine_kernel<128, 512, 128, EB><<<blocks, comb::NT, 0, stream>>>(
+  if (shape == kShapeDeepSeek && groups >= comb::kWholeHeadGroups) {
+    combine_kernel<128, 512, 128, 128><<<groups, comb::NT, 0, stream>>>(
+        (const uint16_t*)part_o, part_lse, (const Plan*)plan, (const uint16_t*)W_UV,
+        (uint16_t*)out, lse_out, B, groups);
+  } else if (shape == kShapeDeepSeek) {
+    const int blocks = 16 * ((groups + 7) / 8);  // pairs of column halves, 8 ids apart
+    combine_kernel<128, 512, 128, 64><<<blocks, comb::NT, 0, stream>>>(
         (const uint16_t*)part_o, part_lse, (const Plan*)plan, (const uint16_t*)W_UV,
         (uint16_t*)out, lse_out, B, groups);
   } else {
