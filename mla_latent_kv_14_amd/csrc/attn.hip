@@ -251,7 +251,9 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
           weights_block(0);
           weights_block(1);
         }
-        if (lane == 0) lds_flag[pb][a] = __ballot(need) != 0;
+        // the ballot is taken by the whole wave (inside a lane-0 branch it would see lane 0 only)
+        const bool any_need = __ballot(need) != 0;
+        if (lane == 0) lds_flag[pb][a] = any_need;
         if (g4 == 0) lds_alpha[pb][16 * a + hl] = alpha;
         l_lane += lsum;
         if (seg_last) {  // the head's row sum over the segment, its lse and 1/l

@@ -65,6 +65,28 @@ def test_explicit_scale_and_wide_logits(M):
     check_against_oracle(M, inp, label="deepseek wide logits")
 
 
+@pytest.mark.parametrize("dims,heads", [(DS, [5, 37, 77, 126]), (M2, [5, 13, 30])],
+                         ids=["deepseek", "mha2mla"])
+@pytest.mark.parametrize("units", [1, 3])
+def test_rescale_on_some_heads(M, dims, heads, units):
+    # One late token per sequence whose RoPE logit is several hundred (log2 units) above every
+    # other logit, for a few heads only, none of them the first of a block of 16: mid-segment
+    # the running reference max of those heads moves far past the rescale threshold while that
+    # of the other heads stays, so the rescale must reach exactly those heads' accumulators.
+    # (The tokens sit in neither the first tile of a segment nor the first of a sequence.)
+    inp = _inp(dims, [700, 1500], 18)
+    qr = inp["q_rope"].float()
+    for b in range(2):
+        for h in heads:
+            qr[b, h, :] = 0.0
+            qr[b, h, 0] = 64.0
+    inp["q_rope"] = qr.to(torch.bfloat16)
+    for b, t in ((0, 650), (1, 1400)):
+        page = int(inp["page_table"][b, t // 64])
+        inp["kv_pages"][page, t % 64, dims["d_c"]] = 64.0
+    check_against_oracle(M, inp, units=units, label="rescale on heads %s" % heads)
+
+
 def test_empty_sequence_gives_zero_and_neg_inf(M):
     inp = _inp(DS, [100, 5, 64], 16)
     d = to_dev(inp)
