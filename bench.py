@@ -15,7 +15,7 @@ about 13 % slower.
 
 Prints one JSON line (the contract): metric/value (KV tokens per second, from K plain calls),
 TFLOP/s, GB/s, the roofline object of the dominant kernel (paged attention; its duration comes
-from HIP events recorded on the library's stream around that kernel in a second pass of K calls)
+from HIP events bound to that kernel's own start and end in a second pass of K calls)
 and the fp64 CPU oracle's throughput on the host cores (a reported baseline).
 
 Algorithmic work of one call (what the method must move or compute; partials and the
@@ -149,8 +149,8 @@ def run(args):
     dref = ctypes.byref(dims)
     hip = Hip()
     K, Wu = args.steps, args.warmup
-    ev = [[hip.event() for _ in range(4)] for _ in range(K)]
-    ev_arr = [(vp * 4)(*e) for e in ev]
+    ev = [[hip.event() for _ in range(6)] for _ in range(K)]  # start, end of each kernel
+    ev_arr = [(vp * 6)(*e) for e in ev]
     nullev = ctypes.POINTER(vp)()
 
     def step(i, events=nullev):
@@ -159,8 +159,9 @@ def run(args):
             raise RuntimeError("mla_decode failed: %s" % lib.mla_status_str(rc).decode())
 
     def timed(rotate):
-        """Step time from K plain calls (no per-stage events in the timed loop), then the
-        per-kernel breakdown from K more calls that record HIP events between the kernels."""
+        """Step time from K plain calls (no events in the timed loop), then the per-kernel
+        durations from K more calls whose kernels carry HIP events bound to their own start
+        and end (the launch gap before a kernel is not counted)."""
         for i in range(Wu):
             step(i if rotate else 0)
         torch.cuda.synchronize()
@@ -172,12 +173,11 @@ def run(args):
         for i in range(K):
             step(i if rotate else 0, ev_arr[i])
         torch.cuda.synchronize()
-        stages = [[hip.ms(e[j], e[j + 1]) for e in ev] for j in range(3)]
-        busy = [hip.ms(e[0], e[3]) for e in ev]
-        return (t1 - t0) / K, [sum(s) / K for s in stages], sum(busy) / K
+        stages = [[hip.ms(e[2 * k], e[2 * k + 1]) for e in ev] for k in range(3)]
+        return (t1 - t0) / K, [sum(s) / K for s in stages]
 
-    sec, stage_ms, busy_ms = timed(rotate=True)
-    warm_sec, warm_stage_ms, warm_busy = timed(rotate=False) if not args.cold_only else (None, None, None)
+    sec, stage_ms = timed(rotate=True)
+    warm_sec, warm_stage_ms = timed(rotate=False) if not args.cold_only else (None, None)
 
     attn_s = stage_ms[1] * 1e-3
     achieved = alg["attn_bytes"] / attn_s / 1e9
@@ -200,7 +200,6 @@ def run(args):
         "tflops": round(alg["flops"] / sec / 1e12, 2),
         "gbps": round(alg["bytes"] / sec / 1e9, 1),
         "roofline_frac_call": round(call_frac, 4),
-        "gpu_busy_us": round(busy_ms * 1e3, 2),
         "kernels_us": {"absorb": round(stage_ms[0] * 1e3, 2), "attention": round(stage_ms[1] * 1e3, 2),
                        "combine": round(stage_ms[2] * 1e3, 2)},
         "roofline": roofline,

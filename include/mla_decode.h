@@ -108,11 +108,13 @@ mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* 
                         float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * mla_decode with stage timing: identical work and results, and, when stage_events is not NULL,
- * records stage_events[i] (hipEvent_t, each may be NULL) on `stream` before the absorb kernel
- * (i = 0), after it (1), after the attention kernel (2) and after the combine kernel (3), so
- * the caller can time each kernel with hipEventElapsedTime on the stream the kernels run on.
- * The events are owned by the caller. Used by the benchmark's roofline measurement.
+ * mla_decode with kernel timing: identical work and results, and, when stage_events is not
+ * NULL, binds six caller-owned events (hipEvent_t, each may be NULL) to the kernels it enqueues
+ * on `stream`: stage_events[2k] to the start and stage_events[2k+1] to the end of kernel k's
+ * execution, k = 0 absorb, 1 attention, 2 combine (hipExtLaunchKernel semantics). The elapsed
+ * time of a pair is that kernel's execution alone, without the launch gap before it, which is
+ * what the benchmark's roofline measurement divides by. The events must have been created
+ * with timing enabled.
  */
 mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
                               const void* W_UK, const void* W_UV, const void* kv_pages,

@@ -231,19 +231,17 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 
 hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* q_abs, int B,
                          int H, const int32_t* seq_lens, const int32_t* page_table, int max_pages,
-                         int G, void* plan, hipStream_t stream) {
+                         int G, void* plan, const Launch& L) {
   if (shape == kShapeDeepSeek) {
     constexpr int DN = 128, DC = 512, CB = 128;
-    absorb_kernel<DN, DC, CB><<<H * (DC / CB) + 1, 256, 0, stream>>>(
-        (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H, seq_lens,
-        page_table, max_pages, G, kSub, (Plan*)plan);
-  } else {
-    constexpr int DN = 120, DC = 64, CB = 64;
-    absorb_kernel<DN, DC, CB><<<H * (DC / CB) + 1, 256, 0, stream>>>(
-        (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H, seq_lens,
-        page_table, max_pages, G, kPage, (Plan*)plan);
+    return launch_kernel(absorb_kernel<DN, DC, CB>, dim3(H * (DC / CB) + 1), dim3(256), L,
+                         (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H,
+                         seq_lens, page_table, max_pages, G, (int)kSub, (Plan*)plan);
   }
-  return hipGetLastError();
+  constexpr int DN = 120, DC = 64, CB = 64;
+  return launch_kernel(absorb_kernel<DN, DC, CB>, dim3(H * (DC / CB) + 1), dim3(256), L,
+                       (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H,
+                       seq_lens, page_table, max_pages, G, (int)kPage, (Plan*)plan);
 }
 
 }  // namespace mla

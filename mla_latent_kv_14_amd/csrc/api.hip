@@ -140,23 +140,26 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
   const float scale = dims->softmax_scale > 0.f ? dims->softmax_scale
                                                 : 1.0f / sqrtf((float)(s.DN + s.DR));
   const float scale_log2 = scale * mla::kLog2e;
-  auto mark = [&](int i) -> mla_status_t {
-    if (!stage_events || !stage_events[i]) return MLA_OK;
-    return hip_status(hipEventRecord((hipEvent_t)stage_events[i], hs));
+  // stage_events: start and end of each kernel's own execution (bound to the kernels)
+  auto ctx = [&](int k) {
+    mla::Launch L{hs};
+    if (stage_events) {
+      L.start = (hipEvent_t)stage_events[2 * k];
+      L.stop = (hipEvent_t)stage_events[2 * k + 1];
+    }
+    return L;
   };
-
-  if ((st = mark(0)) != MLA_OK) return st;
   st = hip_status(mla::launch_absorb(s.shape, q_nope, W_UK, ws + L.q_abs, B, s.H, seq_lens,
-                                     page_table, mp, G, ws + L.plan, hs));
-  if (st != MLA_OK || (st = mark(1)) != MLA_OK) return st;
+                                     page_table, mp, G, ws + L.plan, ctx(0)));
+  if (st != MLA_OK) return st;
   st = hip_status(mla::launch_attention(s.shape, ws + L.q_abs, q_rope, kv_pages, page_table,
                                         seq_lens, B, mp, dims->num_pages, ws + L.plan, G,
-                                        scale_log2, ws + L.part_o, (float*)(ws + L.part_lse), hs));
-  if (st != MLA_OK || (st = mark(2)) != MLA_OK) return st;
-  st = hip_status(mla::launch_combine(s.shape, ws + L.part_o, (const float*)(ws + L.part_lse),
-                                      ws + L.plan, seq_lens, W_UV, out, lse_out, B, s.H, mp, hs));
+                                        scale_log2, ws + L.part_o, (float*)(ws + L.part_lse),
+                                        ctx(1)));
   if (st != MLA_OK) return st;
-  return mark(3);
+  return hip_status(mla::launch_combine(s.shape, ws + L.part_o, (const float*)(ws + L.part_lse),
+                                        ws + L.plan, seq_lens, W_UV, out, lse_out, B, s.H, mp,
+                                        ctx(2)));
 }
 
 mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* q_rope,

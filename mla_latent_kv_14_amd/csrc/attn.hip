@@ -668,21 +668,20 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
 hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, const void* kv,
                             const int32_t* page_table, const int32_t* seq_lens, int B,
                             int max_pages, int num_pages, const void* plan, int G,
-                            float scale_log2, void* part_o, float* part_lse,
-                            hipStream_t stream) {
+                            float scale_log2, void* part_o, float* part_lse, const Launch& L) {
   if (shape == kShapeDeepSeek) {
     // two head halves per tile stream, paired 8 ids apart; ids padded to whole groups of 16
     const int blocks = 16 * ((G + 7) / 8);
-    attn_deepseek_kernel<<<blocks, 64 * ds::NW, 0, stream>>>(
-        (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv, page_table, seq_lens,
-        B, max_pages, num_pages, (const Plan*)plan, G, scale_log2, (uint16_t*)part_o, part_lse);
-  } else {
-    const int blocks = (G + kAttnWavesMha2Mla - 1) / kAttnWavesMha2Mla;
-    attn_mha2mla_kernel<<<blocks, 64 * kAttnWavesMha2Mla, 0, stream>>>(
-        (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv, page_table, seq_lens,
-        B, max_pages, num_pages, (const Plan*)plan, G, scale_log2, (uint16_t*)part_o, part_lse);
+    return launch_kernel(attn_deepseek_kernel, dim3(blocks), dim3(64 * ds::NW), L,
+                         (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv,
+                         page_table, seq_lens, B, max_pages, num_pages, (const Plan*)plan, G,
+                         scale_log2, (uint16_t*)part_o, part_lse);
   }
-  return hipGetLastError();
+  const int blocks = (G + kAttnWavesMha2Mla - 1) / kAttnWavesMha2Mla;
+  return launch_kernel(attn_mha2mla_kernel, dim3(blocks), dim3(64 * kAttnWavesMha2Mla), L,
+                       (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv,
+                       page_table, seq_lens, B, max_pages, num_pages, (const Plan*)plan, G,
+                       scale_log2, (uint16_t*)part_o, part_lse);
 }
 
 }  // namespace mla

@@ -221,26 +221,23 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
 
 hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, const void* plan,
                           const int32_t* seq_lens, const void* W_UV, void* out, float* lse_out,
-                          int B, int H, int max_pages, hipStream_t stream) {
+                          int B, int H, int max_pages, const Launch& L) {
   (void)seq_lens;
   (void)max_pages;
   const int groups = H * ((B + comb::SEQ - 1) / comb::SEQ);
-  if (shape == kShapeDeepSeek && groups >= comb::kWholeHeadGroups) {
-    combine_kernel<128, 512, 128, 128><<<groups, comb::NT, 0, stream>>>(
-        (const uint16_t*)part_o, part_lse, (const Plan*)plan, (const uint16_t*)W_UV,
-        (uint16_t*)out, lse_out, B, groups);
-  } else if (shape == kShapeDeepSeek) {
-    const int blocks = 16 * ((groups + 7) / 8);  // pairs of column halves, 8 ids apart
-    combine_kernel<128, 512, 128, 64><<<blocks, comb::NT, 0, stream>>>(
-        (const uint16_t*)part_o, part_lse, (const Plan*)plan, (const uint16_t*)W_UV,
-        (uint16_t*)out, lse_out, B, groups);
-  } else {
-    const int blocks = 16 * ((groups + 7) / 8);  // pairs of column halves, 8 ids apart
-    combine_kernel<32, 64, 128, 64><<<blocks, comb::NT, 0, stream>>>(
-        (const uint16_t*)part_o, part_lse, (const Plan*)plan, (const uint16_t*)W_UV,
-        (uint16_t*)out, lse_out, B, groups);
-  }
-  return hipGetLastError();
+  const uint16_t* po = (const uint16_t*)part_o;
+  const Plan* pl = (const Plan*)plan;
+  const uint16_t* w = (const uint16_t*)W_UV;
+  uint16_t* o = (uint16_t*)out;
+  if (shape == kShapeDeepSeek && groups >= comb::kWholeHeadGroups)
+    return launch_kernel(combine_kernel<128, 512, 128, 128>, dim3(groups), dim3(comb::NT), L, po,
+                         part_lse, pl, w, o, lse_out, B, groups);
+  const int blocks = 16 * ((groups + 7) / 8);  // pairs of column halves, 8 ids apart
+  if (shape == kShapeDeepSeek)
+    return launch_kernel(combine_kernel<128, 512, 128, 64>, dim3(blocks), dim3(comb::NT), L, po,
+                         part_lse, pl, w, o, lse_out, B, groups);
+  return launch_kernel(combine_kernel<32, 64, 128, 64>, dim3(blocks), dim3(comb::NT), L, po,
+                       part_lse, pl, w, o, lse_out, B, groups);
 }
 
 }  // namespace mla

@@ -1,9 +1,28 @@
 // Host-side launch entry points of the gfx950 kernels (implemented in the .hip files).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace mla {
+
+// Where a kernel goes: the stream, and optionally two events that the runtime binds to the
+// kernel's own start and end (hipExtLaunchKernel), so that their elapsed time is the kernel's
+// execution alone, without the launch gap before it.
+struct Launch {
+  hipStream_t stream;
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename F, typename... Args>
+hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, const Launch& L, Args... args) {
+  if (L.start || L.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, L.stream, L.start, L.stop, 0, args...);
+  else
+    kernel<<<grid, block, 0, L.stream>>>(args...);
+  return hipGetLastError();
+}
 
 // The two head/width families the kernels are built for.
 enum Shape : int {
@@ -17,16 +36,16 @@ constexpr int kAttnWavesMha2Mla = 4;
 
 hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* q_abs, int B,
                          int H, const int32_t* seq_lens, const int32_t* page_table, int max_pages,
-                         int G, void* plan, hipStream_t stream);
+                         int G, void* plan, const Launch& L);
 
 hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, const void* kv,
                             const int32_t* page_table, const int32_t* seq_lens, int B,
                             int max_pages, int num_pages, const void* plan, int G,
-                            float scale_log2, void* part_o, float* part_lse, hipStream_t stream);
+                            float scale_log2, void* part_o, float* part_lse, const Launch& L);
 
 hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, const void* plan,
                           const int32_t* seq_lens, const void* W_UV, void* out, float* lse_out,
-                          int B, int H, int max_pages, hipStream_t stream);
+                          int B, int H, int max_pages, const Launch& L);
 
 // Sets bits of *flag (cleared first) for out-of-range lengths (1) or used page ids (2).
 hipError_t launch_check(const int32_t* seq_lens, const int32_t* page_table, int B, int max_pages,
