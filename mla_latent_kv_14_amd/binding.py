@@ -128,12 +128,15 @@ def _want(t, name, dtype, ndim, device):
 
 def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None, lse=None,
            max_seq_len=None, softmax_scale=None, num_units=0, workspace=None, stream=None,
-           return_lse=False):
+           return_lse=False, kernel_events=None):
     """Absorbed MLA decode through mla_decode(). Tensors live on one HIP device.
 
     q_nope bf16 [B,H,d_n], q_rope bf16 [B,H,d_R], W_UK bf16 [H,d_n,d_c], W_UV bf16 [H,d_c,d_v],
     kv_pages bf16 [P,64,d_c+d_R], page_table int32 [B,max_pages], seq_lens int32 [B].
     Returns out bf16 [B,H,d_v] (and lse fp32 [B,H] when return_lse).
+    kernel_events: optional six raw hipEvent_t handles (int or None), passed to
+    mla_decode_timed, which binds them to the start and end of the absorb, attention and
+    combine kernels.
     """
     dev = q_nope.device
     if dev.type != "cuda":
@@ -161,10 +164,16 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
                                 ctypes.c_void_p(0)))
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    code = lib().mla_decode(ctypes.byref(dims), _ptr(q_nope), _ptr(q_rope), _ptr(W_UK),
-                            _ptr(W_UV), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
-                            _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
-                            _stream(stream, dev))
+    args = (ctypes.byref(dims), _ptr(q_nope), _ptr(q_rope), _ptr(W_UK), _ptr(W_UV),
+            _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
+            _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    if kernel_events is None:
+        code = lib().mla_decode(*args)
+    else:
+        if len(kernel_events) != 6:
+            raise ValueError("kernel_events needs six entries (start, end of three kernels)")
+        ev = (ctypes.c_void_p * 6)(*[e or None for e in kernel_events])
+        code = lib().mla_decode_timed(*args, ev)
     _check(code)
     return (out, lse) if return_lse else out
 

@@ -118,3 +118,55 @@ def test_sequence_longer_than_table_is_clamped(M):
     b = gpu_decode(M, over)
     torch.cuda.synchronize()
     assert torch.equal(_bits(a), _bits(b))
+
+
+class _HipEvents:
+    """hipEvent_t handles through ctypes (the library takes raw events)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = self.ct.c_void_p()
+        assert self.L.hipEventCreate(self.ct.byref(e)) == 0
+        return e.value
+
+    def ms(self, a, b):
+        t = self.ct.c_float()
+        assert self.L.hipEventElapsedTime(self.ct.byref(t), self.ct.c_void_p(a),
+                                          self.ct.c_void_p(b)) == 0
+        return t.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(self.ct.c_void_p(e))
+
+
+@pytest.mark.parametrize("dims", [DS, M2], ids=["deepseek", "mha2mla"])
+def test_timed_entry_point(M, dims):
+    # mla_decode_timed gives the same bits as mla_decode, and its six events bracket the three
+    # kernels in stream order: every kernel takes time, none starts before the previous ends
+    inp = _inp(dims, [300, 1000, 64], 24)
+    d = to_dev(inp)
+    say("timed entry point", dims["d_c"])
+    ref = gpu_decode(M, d)
+    hip = _HipEvents()
+    ev = [hip.create() for _ in range(6)]
+    out = gpu_decode(M, d, kernel_events=ev)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out), _bits(ref))
+    for k in range(3):
+        assert hip.ms(ev[2 * k], ev[2 * k + 1]) > 0
+    assert hip.ms(ev[1], ev[2]) >= 0 and hip.ms(ev[3], ev[4]) >= 0
+    # events may be left out (NULL): only the attention kernel timed
+    out2 = gpu_decode(M, d, kernel_events=[None, None, ev[2], ev[3], None, None])
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out2), _bits(ref))
+    assert hip.ms(ev[2], ev[3]) > 0
+    for e in ev:
+        hip.destroy(e)
