@@ -47,17 +47,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 ATTN_SOURCES = ["attn.hip", "paged_tile.h", "device.h"]
 
 
-def algorithmic(inp):
+def algorithmic(inp, T=1):
+    """Algorithmic work of one call with T query tokens per sequence (query token i of
+    sequence b attends to S_b - T + 1 + i tokens; the cache is read once)."""
     B, H = inp["B"], inp["H"]
     d_n, d_c, d_R, d_v = inp["d_n"], inp["d_c"], inp["d_R"], inp["d_v"]
-    S = int(inp["seq_lens"].sum())
+    lens = [int(x) for x in inp["seq_lens"]]
+    S = sum(lens)                                                    # cached tokens
+    A = sum(max(0, s - T + 1 + i) for s in lens for i in range(T))  # (query, token) pairs
+    Q = B * T                                                        # query tokens
     mp = inp["max_pages"]
-    flops = 2 * B * H * d_n * d_c + 2 * H * (d_c + d_R) * S + 2 * H * d_c * S + 2 * B * H * d_c * d_v
-    nbytes = (S * (d_c + d_R) * 2 + 2 * H * d_c * (d_n + d_v) + 2 * B * H * (d_n + d_R)
-              + 2 * B * H * d_v + 4 * (B * mp + B))
-    attn_bytes = S * (d_c + d_R) * 2 + 2 * B * H * (d_c + d_R) + 4 * (B * mp + B)
-    attn_flops = 2 * H * (d_c + d_R) * S + 2 * H * d_c * S
-    return dict(sumS=S, flops=flops, bytes=nbytes, attn_bytes=attn_bytes, attn_flops=attn_flops)
+    flops = 2 * Q * H * d_n * d_c + 2 * H * (d_c + d_R) * A + 2 * H * d_c * A + 2 * Q * H * d_c * d_v
+    nbytes = (S * (d_c + d_R) * 2 + 2 * H * d_c * (d_n + d_v) + 2 * Q * H * (d_n + d_R)
+              + 2 * Q * H * d_v + 4 * (B * mp + B))
+    attn_bytes = S * (d_c + d_R) * 2 + 2 * Q * H * (d_c + d_R) + 4 * (B * mp + B)
+    attn_flops = 2 * H * (d_c + d_R) * A + 2 * H * d_c * A
+    return dict(sumS=A, flops=flops, bytes=nbytes, attn_bytes=attn_bytes, attn_flops=attn_flops)
 
 
 class Hip:
@@ -122,20 +127,31 @@ def run(args):
     cfg = W.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    base = W.config_inputs(args.workload)
-    alg = algorithmic(base)
+    T = args.q_len
+
+    def with_tokens(inp, seed):  # T query tokens per sequence, seeded like the rest
+        if T > 1:
+            g = torch.Generator().manual_seed(seed)
+            B, H = inp["B"], inp["H"]
+            inp["q_nope"] = torch.randn(B, T, H, inp["d_n"], generator=g).to(torch.bfloat16)
+            inp["q_rope"] = torch.randn(B, T, H, inp["d_R"], generator=g).to(torch.bfloat16)
+        return inp
+
+    base = with_tokens(W.config_inputs(args.workload), cfg["seed"] + 500)
+    alg = algorithmic(base, T)
     n_sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / alg["bytes"]))
     sets = []
     for i in range(n_sets):
-        inp = base if i == 0 else W.config_inputs(args.workload, seed=cfg["seed"] + 1000 * i)
+        inp = base if i == 0 else with_tokens(
+            W.config_inputs(args.workload, seed=cfg["seed"] + 1000 * i), cfg["seed"] + 1000 * i + 500)
         sets.append({k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()})
     d0 = sets[0]
     dims = M.make_dims(d0["q_nope"], d0["q_rope"], d0["W_UK"], d0["W_UV"], d0["kv_pages"],
                        d0["page_table"])
     ws_bytes = M.workspace_bytes(dims)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    outs = [torch.empty((d["B"], d["H"], d["d_v"]), dtype=torch.bfloat16, device=dev)
-            for d in sets]
+    outs = [torch.empty(((d["B"],) if T == 1 else (d["B"], T)) + (d["H"], d["d_v"]),
+                        dtype=torch.bfloat16, device=dev) for d in sets]
     stream = torch.cuda.current_stream(dev)
     vp = ctypes.c_void_p
 
@@ -196,7 +212,8 @@ def run(args):
                    if cfg["seq"][0] == "fixed" else "ragged", "kv_tokens": alg["sumS"],
                    "heads": cfg["H"], "d_nope": cfg["d_n"], "d_latent": cfg["d_c"],
                    "d_rope": cfg["d_R"], "d_v": cfg["d_v"], "page_size": 64,
-                   "page_table": cfg["layout"], "input_sets_rotated": n_sets},
+                   "page_table": cfg["layout"], "input_sets_rotated": n_sets,
+                   "query_tokens_per_seq": T},
         "tflops": round(alg["flops"] / sec / 1e12, 2),
         "gbps": round(alg["bytes"] / sec / 1e9, 1),
         "roofline_frac_call": round(call_frac, 4),
@@ -213,7 +230,7 @@ def run(args):
     for e in ev:
         for x in e:
             hip.destroy(x)
-    if not args.no_cpu:
+    if not args.no_cpu and T == 1:
         res["cpu_baseline"] = cpu_baseline(base, alg)
     else:
         res["cpu_baseline"] = None
@@ -252,6 +269,9 @@ def main():
                     help="which workload (2 = B=16, S=4096, the headline)")
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = enough to "
                     "exceed twice the Infinity Cache)")
+    ap.add_argument("--q-len", type=int, default=1, help="query tokens per sequence (the "
+                    "sequence's newest tokens, causal among themselves); with more than one, "
+                    "value counts (query token, cached token) pairs per second")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-only", action="store_true", help="skip the single-set warm run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

@@ -80,6 +80,15 @@ typedef struct {
                                   order. 0 = automatic (fills the 256 compute units: 128 for
                                   the DeepSeek widths, one unit = two work groups; 1024 for
                                   MHA2MLA, one unit = one wave). At most 65536.            */
+    int32_t q_len;             /* T: query tokens per sequence, 0 or 1 = one (plain decode),
+                                  at most 256, B*T at most 2^20. With T > 1 the T query
+                                  tokens of sequence b are its T newest tokens, whose
+                                  [c_KV | k_R] are already in the cache (multi-token decode:
+                                  verification of drafted tokens): query token i sits at
+                                  position S_b - T + i and attends to tokens
+                                  0 .. S_b - T + i, itself included. A query token with no
+                                  token to attend to (S_b - T + i < 0) gets out = 0,
+                                  lse = -inf.                                              */
 } mla_dims_t;
 
 /* Bytes of scratch a call with these dims needs (pure function of the dims, host only).
@@ -87,16 +96,16 @@ typedef struct {
 size_t mla_decode_workspace_bytes(const mla_dims_t* dims);
 
 /*
- * Absorbed MLA decode (the operation above).
- *   q_nope     bf16 [B, H, d_nope]
- *   q_rope     bf16 [B, H, d_rope]                       already rotated
+ * Absorbed MLA decode (the operation above). T = q_len (1 when dims->q_len is 0 or 1).
+ *   q_nope     bf16 [B, T, H, d_nope]                    ([B, H, d_nope] when T = 1)
+ *   q_rope     bf16 [B, T, H, d_rope]                    already rotated
  *   W_UK       bf16 [H, d_nope, d_latent]
  *   W_UV       bf16 [H, d_latent, d_v]
  *   kv_pages   bf16 [num_pages, 64, d_latent + d_rope]   token = [c_KV | k_R]
  *   page_table int32 [B, max_pages_per_seq]              logical page j of b -> pool page
  *   seq_lens   int32 [B]                                 S_b, 1 <= S_b <= max_seq_len
- *   out        bf16 [B, H, d_v]                          written
- *   lse_out    fp32 [B, H] natural-log LSE of the logits, or NULL
+ *   out        bf16 [B, T, H, d_v]                       written
+ *   lse_out    fp32 [B, T, H] natural-log LSE of the logits, or NULL
  *   workspace  device scratch, 256-byte aligned, of at least mla_decode_workspace_bytes(dims)
  *              bytes; its contents need no initialisation and are garbage afterwards
  * Inputs are read only; out, lse_out and workspace are the only memory written. Calls that

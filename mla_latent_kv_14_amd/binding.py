@@ -28,7 +28,8 @@ class Dims(ctypes.Structure):
                 ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("num_units", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("num_units", ctypes.c_int32),
+                ("q_len", ctypes.c_int32)]
 
 
 class MlaError(RuntimeError):
@@ -84,11 +85,17 @@ def _check(code):
 
 def make_dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, max_seq_len=None,
               softmax_scale=None, num_units=0):
-    B, H, d_n = q_nope.shape
+    """Dims of a call; q_nope [B, H, d_n] (one query token per sequence) or [B, T, H, d_n]
+    (T query tokens per sequence)."""
+    if q_nope.dim() == 4:
+        B, T, H, d_n = q_nope.shape
+    else:
+        (B, H, d_n), T = q_nope.shape, 1
     d = Dims()
     d.batch, d.num_heads, d.d_nope = B, H, d_n
+    d.q_len = T
     d.d_latent = W_UK.shape[2]
-    d.d_rope = q_rope.shape[2]
+    d.d_rope = q_rope.shape[-1]
     d.d_v = W_UV.shape[2]
     d.page_size = kv_pages.shape[1]
     d.max_pages_per_seq = page_table.shape[1]
@@ -134,6 +141,9 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
     q_nope bf16 [B,H,d_n], q_rope bf16 [B,H,d_R], W_UK bf16 [H,d_n,d_c], W_UV bf16 [H,d_c,d_v],
     kv_pages bf16 [P,64,d_c+d_R], page_table int32 [B,max_pages], seq_lens int32 [B].
     Returns out bf16 [B,H,d_v] (and lse fp32 [B,H] when return_lse).
+    Several query tokens per sequence: q_nope [B,T,H,d_n] and q_rope [B,T,H,d_R] give out
+    [B,T,H,d_v] and lse [B,T,H]; query token i of sequence b attends to its first
+    seq_lens[b] - T + 1 + i cached tokens.
     kernel_events: optional six raw hipEvent_t handles (int or None), passed to
     mla_decode_timed, which binds them to the start and end of the absorb, attention and
     combine kernels.
@@ -142,7 +152,10 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
     if dev.type != "cuda":
         raise ValueError("mla decode runs on a HIP device; got %s" % dev)
     bf, i32 = torch.bfloat16, torch.int32
-    for t, n, dt, nd in ((q_nope, "q_nope", bf, 3), (q_rope, "q_rope", bf, 3),
+    nq = q_nope.dim() if isinstance(q_nope, torch.Tensor) else 3
+    if nq not in (3, 4):
+        raise ValueError("q_nope must be [B,H,d_n] or [B,T,H,d_n]")
+    for t, n, dt, nd in ((q_nope, "q_nope", bf, nq), (q_rope, "q_rope", bf, nq),
                          (W_UK, "W_UK", bf, 3), (W_UV, "W_UV", bf, 3),
                          (kv_pages, "kv_pages", bf, 3), (page_table, "page_table", i32, 2),
                          (seq_lens, "seq_lens", i32, 1)):
@@ -150,14 +163,18 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
     dims = make_dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, max_seq_len,
                      softmax_scale, num_units)
     B, H, d_v = dims.batch, dims.num_heads, dims.d_v
+    lead = (B,) if nq == 3 else (B, dims.q_len)
+    if q_rope.shape[:-1] != q_nope.shape[:-1]:
+        raise ValueError("q_rope %s does not match q_nope %s" % (tuple(q_rope.shape),
+                                                                 tuple(q_nope.shape)))
     if out is None:
-        out = torch.empty((B, H, d_v), dtype=bf, device=dev)
+        out = torch.empty(lead + (H, d_v), dtype=bf, device=dev)
     else:
-        _want(out, "out", bf, 3, dev)
+        _want(out, "out", bf, nq, dev)
     if return_lse and lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        lse = torch.empty(lead + (H,), dtype=torch.float32, device=dev)
     if lse is not None:
-        _want(lse, "lse", torch.float32, 2, dev)
+        _want(lse, "lse", torch.float32, nq - 1, dev)
     nbytes = workspace_bytes(dims)
     if nbytes == 0:
         _check(lib().mla_decode(ctypes.byref(dims), *([ctypes.c_void_p(0)] * 10), 0,

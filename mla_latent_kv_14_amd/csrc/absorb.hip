@@ -24,8 +24,9 @@ constexpr int kSeqInLds = 4096;
 constexpr int kPlanLdsBytes = (2 * kSeqInLds + 8) * 4;
 
 __device__ void build_plan(const int32_t* __restrict__ seq_lens,
-                           const int32_t* __restrict__ page_table, int B, int max_pages, int G,
-                           int TT, Plan* __restrict__ plan, MLA_LDS char* scratch) {
+                           const int32_t* __restrict__ page_table, int B, int max_pages,
+                           int q_len, int G, int TT, Plan* __restrict__ plan,
+                           MLA_LDS char* scratch) {
   MLA_LDS int32_t* seq_off = (MLA_LDS int32_t*)scratch;
   MLA_LDS int32_t* seq_len = seq_off + kSeqInLds;
   MLA_LDS int32_t* wave_tot = seq_len + kSeqInLds;
@@ -38,7 +39,7 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens,
     const int b = base + tid;
     int n = 0, S = 0;
     if (b < B) {
-      S = clamp_len(seq_lens[b], max_pages);
+      S = virt_len(clamp_len(seq_lens[virt_row(b, q_len)], max_pages), b, q_len);
       n = (S + TT - 1) / TT;
     }
     int x = n;  // inclusive wave scan
@@ -107,7 +108,7 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens,
           }
           ub[k] = lo;
           uj[k] = t - seq_off[lo];
-          page[k] = page_table[(size_t)lo * max_pages + (uj[k] * TT) / kPage];
+          page[k] = page_table[(size_t)virt_row(lo, q_len) * max_pages + (uj[k] * TT) / kPage];
         }
       }
 #pragma unroll
@@ -117,12 +118,13 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens,
   } else {
     // large batches: each thread walks the units that start in its sequences
     for (int b = tid; b < B; b += 256) {
-      const int S = clamp_len(seq_lens[b], max_pages);
+      const int S = virt_len(clamp_len(seq_lens[virt_row(b, q_len)], max_pages), b, q_len);
       const int n = (S + TT - 1) / TT;
       const int o = off[b];
       for (int u = (o + per - 1) / per; u < g && (long long)u * per < o + n; ++u) {
         const int j = u * per - o;
-        write_unit(u, b, j, S, page_table[(size_t)b * max_pages + (j * TT) / kPage]);
+        write_unit(u, b, j, S,
+                   page_table[(size_t)virt_row(b, q_len) * max_pages + (j * TT) / kPage]);
       }
     }
   }
@@ -134,7 +136,8 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
                                                      uint16_t* __restrict__ q_abs, int B, int H,
                                                      const int32_t* __restrict__ seq_lens,
                                                      const int32_t* __restrict__ page_table,
-                                                     int max_pages, int G, int TT, Plan* plan) {
+                                                     int max_pages, int q_len, int G, int TT,
+                                                     Plan* plan) {
   constexpr int DNP = (DN + 31) / 32 * 32;  // contraction padded to the MFMA K of 32
   constexpr int ROWB = CB * 2;              // LDS bytes per W row
   constexpr int UNITS = ROWB / 32;          // 32-byte units per row (swizzle period)
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = DC / CB;
   if (blockIdx.x == 0) {  // the extra first block writes the work plan, nothing else
-    build_plan(seq_lens, page_table, B, max_pages, G, TT, plan, (MLA_LDS char*)wt);
+    build_plan(seq_lens, page_table, B, max_pages, q_len, G, TT, plan, (MLA_LDS char*)wt);
     return;
   }
   const int h = (blockIdx.x - 1) / nblk, cblk = (blockIdx.x - 1) % nblk;
@@ -231,17 +234,17 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 
 hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* q_abs, int B,
                          int H, const int32_t* seq_lens, const int32_t* page_table, int max_pages,
-                         int G, void* plan, const Launch& L) {
+                         int q_len, int G, void* plan, const Launch& L) {
   if (shape == kShapeDeepSeek) {
     constexpr int DN = 128, DC = 512, CB = 128;
     return launch_kernel(absorb_kernel<DN, DC, CB>, dim3(H * (DC / CB) + 1), dim3(256), L,
                          (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H,
-                         seq_lens, page_table, max_pages, G, (int)kSub, (Plan*)plan);
+                         seq_lens, page_table, max_pages, q_len, G, (int)kSub, (Plan*)plan);
   }
   constexpr int DN = 120, DC = 64, CB = 64;
   return launch_kernel(absorb_kernel<DN, DC, CB>, dim3(H * (DC / CB) + 1), dim3(256), L,
                        (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H,
-                       seq_lens, page_table, max_pages, G, (int)kPage, (Plan*)plan);
+                       seq_lens, page_table, max_pages, q_len, G, (int)kPage, (Plan*)plan);
 }
 
 }  // namespace mla

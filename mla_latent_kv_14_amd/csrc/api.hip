@@ -11,6 +11,8 @@
 
 namespace {
 
+constexpr int kMaxQLen = 256;  // query tokens per sequence
+
 thread_local char g_hip_err[256] = "";
 
 struct ShapeInfo {
@@ -36,7 +38,8 @@ mla_status_t check_dims(const mla_dims_t* d, ShapeInfo* s) {
   if (!d) return MLA_ERR_NULL_ARG;
   if (d->batch < 1 || d->batch > (1 << 20) || d->max_pages_per_seq < 1 || d->num_pages < 1 ||
       d->num_units < 0 || d->num_units > 65536 || d->num_heads < 1 || d->d_nope < 1 ||
-      d->d_latent < 1 || d->d_rope < 1 || d->d_v < 1 || d->page_size < 1)
+      d->d_latent < 1 || d->d_rope < 1 || d->d_v < 1 || d->page_size < 1 || d->q_len < 0 ||
+      d->q_len > kMaxQLen || (int64_t)d->batch * (d->q_len > 1 ? d->q_len : 1) > (1 << 20))
     return MLA_ERR_BAD_DIMS;
   if ((int64_t)d->batch * d->max_pages_per_seq > (int64_t)1 << 29) return MLA_ERR_BAD_DIMS;
   if ((int64_t)d->max_seq_len > (int64_t)d->max_pages_per_seq * d->page_size)
@@ -46,6 +49,12 @@ mla_status_t check_dims(const mla_dims_t* d, ShapeInfo* s) {
   return MLA_OK;
 }
 
+// Query tokens per sequence (0 in the dims means 1).
+int q_len(const mla_dims_t* d) { return d->q_len > 1 ? d->q_len : 1; }
+
+// Decoded rows: one per (sequence, query token), the kernels' virtual sequences.
+int rows(const mla_dims_t* d) { return d->batch * q_len(d); }
+
 int max_len(const mla_dims_t* d) {
   return d->max_seq_len > 0 ? d->max_seq_len : d->max_pages_per_seq * d->page_size;
 }
@@ -54,7 +63,7 @@ int max_len(const mla_dims_t* d) {
 // widths) or single waves (MHA2MLA). The automatic count fills 256 compute units; it is capped
 // by the tiles that can exist so that no unit is sure to be idle.
 int plan_units(const mla_dims_t* d, const ShapeInfo& s) {
-  const int64_t upper = (int64_t)d->batch * ((max_len(d) + s.TT - 1) / s.TT);
+  const int64_t upper = (int64_t)rows(d) * ((max_len(d) + s.TT - 1) / s.TT);
   int64_t g = d->num_units;
   if (g == 0) g = s.shape == mla::kShapeDeepSeek ? 128 : 256 * mla::kAttnWavesMha2Mla;
   if (g > upper) g = upper;
@@ -74,7 +83,7 @@ struct Layout {
 };
 
 Layout layout(const mla_dims_t* d, const ShapeInfo& s) {
-  const size_t B = (size_t)d->batch, slots = (size_t)plan_units(d, s) + B;
+  const size_t B = (size_t)rows(d), slots = (size_t)plan_units(d, s) + B;
   Layout L;
   L.plan = 0;
   L.q_abs = align256(mla::plan_bytes((int)B, plan_units(d, s)));
@@ -122,7 +131,7 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
 
   const hipStream_t hs = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  const int B = dims->batch, mp = dims->max_pages_per_seq;
+  const int B = dims->batch, mp = dims->max_pages_per_seq, T = q_len(dims), R = B * T;
   if (check_mode()) {
     // validate the device-resident inputs first; the flag lives in the query region, which
     // the decode overwrites afterwards
@@ -149,16 +158,16 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
     }
     return L;
   };
-  st = hip_status(mla::launch_absorb(s.shape, q_nope, W_UK, ws + L.q_abs, B, s.H, seq_lens,
-                                     page_table, mp, G, ws + L.plan, ctx(0)));
+  st = hip_status(mla::launch_absorb(s.shape, q_nope, W_UK, ws + L.q_abs, R, s.H, seq_lens,
+                                     page_table, mp, T, G, ws + L.plan, ctx(0)));
   if (st != MLA_OK) return st;
   st = hip_status(mla::launch_attention(s.shape, ws + L.q_abs, q_rope, kv_pages, page_table,
-                                        seq_lens, B, mp, dims->num_pages, ws + L.plan, G,
+                                        seq_lens, R, mp, T, dims->num_pages, ws + L.plan, G,
                                         scale_log2, ws + L.part_o, (float*)(ws + L.part_lse),
                                         ctx(1)));
   if (st != MLA_OK) return st;
   return hip_status(mla::launch_combine(s.shape, ws + L.part_o, (const float*)(ws + L.part_lse),
-                                        ws + L.plan, seq_lens, W_UV, out, lse_out, B, s.H, mp,
+                                        ws + L.plan, seq_lens, W_UV, out, lse_out, R, s.H, mp,
                                         ctx(2)));
 }
 

@@ -37,20 +37,22 @@ __device__ __forceinline__ int seq_tiles(const Plan* plan, int B, int b) {
 }
 
 __device__ __forceinline__ void cursor_at(Cursor& c, int b, int j, const Plan* plan,
-                                          const int32_t* seq_lens, int B, int max_pages) {
+                                          const int32_t* seq_lens, int B, int max_pages,
+                                          int q_len) {
   c.b = b;
   c.j = j;
   c.nj = seq_tiles(plan, B, b);
-  c.S = clamp_len(ld_uniform(seq_lens + b), max_pages);
+  c.S = virt_len(clamp_len(ld_uniform(seq_lens + virt_row(b, q_len)), max_pages), b, q_len);
 }
 
-// The next tile of the stream; the plan is read only when a sequence ends.
+// The next tile of the stream (sequences are virtual ones when q_len > 1); the plan is read
+// only when a sequence ends.
 __device__ __forceinline__ void cursor_next(Cursor& c, const Plan* plan, const int32_t* seq_lens,
-                                            int B, int max_pages) {
+                                            int B, int max_pages, int q_len) {
   if (++c.j < c.nj) return;
   int b = c.b + 1;
   while (b < B && seq_tiles(plan, B, b) == 0) ++b;
-  if (b < B) cursor_at(c, b, 0, plan, seq_lens, B, max_pages);
+  if (b < B) cursor_at(c, b, 0, plan, seq_lens, B, max_pages, q_len);
 }
 
 // ================================================================ DeepSeek widths
@@ -96,7 +98,8 @@ __device__ __forceinline__ void wait_tiles_after(int after) {
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
                      const char* __restrict__ kv, const int32_t* __restrict__ page_table,
-                     const int32_t* __restrict__ seq_lens, int B, int max_pages, int num_pages,
+                     const int32_t* __restrict__ seq_lens, int B, int max_pages, int q_len,
+                     int num_pages,
                      const Plan* __restrict__ plan, int G, float scale_log2,
                      uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   using namespace ds;
@@ -263,7 +266,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
             part_lse[(size_t)(ca.b + g) * H + head] = (m_ref + log2f_fast(lt)) * kLn2;
           }
         }
-        cursor_next(ca, plan, seq_lens, B, max_pages);
+        cursor_next(ca, plan, seq_lens, B, max_pages, q_len);
       }
       block_sync_tagged<0>();
     }
@@ -309,7 +312,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         pw_b = lc.b;
         pw_base = p;
         const int idx = min(p + lane, max_pages - 1);
-        const int32_t* src = page_table + (size_t)lc.b * max_pages + idx;
+        const int32_t* src = page_table + (size_t)virt_row(lc.b, q_len) * max_pages + idx;
         asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)"
                      : "=v"(pw_v) : "v"(src) : "memory");
       }
@@ -319,7 +322,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
     };
     auto advance = [&]() {
       ++issued;
-      cursor_next(lc, plan, seq_lens, B, max_pages);
+      cursor_next(lc, plan, seq_lens, B, max_pages, q_len);
     };
     auto issue_next = [&]() {
       lookup();
@@ -333,7 +336,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
       pw_b = lc.b;
       pw_base = lc.j / Tile::TPP;
       const int idx = pw_base + lane < max_pages ? pw_base + lane : max_pages - 1;
-      const int32_t* src = page_table + (size_t)lc.b * max_pages + idx;
+      const int32_t* src = page_table + (size_t)virt_row(lc.b, q_len) * max_pages + idx;
       asm volatile("global_load_dword %0, %1, off" : "=v"(pw_v) : "v"(src) : "memory");
       nbase = Tile::base_of(kv, us.page, lc.j, num_pages);
       nvalid = min(kSub, lc.S - lc.j * kSub);
@@ -452,7 +455,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         block_sync_tagged<1>();  // P of tile r+1 visible; tile r free
       }
       cb.j += seg - 1;
-      cursor_next(cb, plan, seq_lens, B, max_pages);
+      cursor_next(cb, plan, seq_lens, B, max_pages, q_len);
     }
     wait_vmcnt<0>();
   }
@@ -478,7 +481,8 @@ constexpr float kRescale = 64.f;  // log2 headroom before the running max must m
 __global__ void __launch_bounds__(256)
 attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
                     const char* __restrict__ kv, const int32_t* __restrict__ page_table,
-                    const int32_t* __restrict__ seq_lens, int B, int max_pages, int num_pages,
+                    const int32_t* __restrict__ seq_lens, int B, int max_pages, int q_len,
+                    int num_pages,
                     const Plan* __restrict__ plan, int G, float scale_log2,
                     uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   using namespace m2;
@@ -508,7 +512,7 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       pw_b = c.b;
       pw_base = p;
       const int idx = min(p + lane, max_pages - 1);
-      const int32_t* src = page_table + (size_t)c.b * max_pages + idx;
+      const int32_t* src = page_table + (size_t)virt_row(c.b, q_len) * max_pages + idx;
       asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)"
                    : "=v"(pw_v) : "v"(src) : "memory");
     }
@@ -542,7 +546,7 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   int issued = 0;
   for (; issued < NBUF - 1 && issued < n; ++issued) {
     issue(lc, issued % NBUF);
-    cursor_next(lc, plan, seq_lens, B, max_pages);
+    cursor_next(lc, plan, seq_lens, B, max_pages, q_len);
   }
   for (int it = 0; it < n; ++it) {
     if (seg_start) {
@@ -555,7 +559,7 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
     else wait_vmcnt<0>();
     if (issued < n) {
       issue(lc, issued % NBUF);
-      cursor_next(lc, plan, seq_lens, B, max_pages);
+      cursor_next(lc, plan, seq_lens, B, max_pages, q_len);
       ++issued;
     }
     const MLA_LDS char* kb = tiles + (it % NBUF) * Tile::BYTES;
@@ -661,26 +665,26 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       }
       seg_start = true;
     }
-    cursor_next(cc, plan, seq_lens, B, max_pages);
+    cursor_next(cc, plan, seq_lens, B, max_pages, q_len);
   }
 }
 
 hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, const void* kv,
                             const int32_t* page_table, const int32_t* seq_lens, int B,
-                            int max_pages, int num_pages, const void* plan, int G,
+                            int max_pages, int q_len, int num_pages, const void* plan, int G,
                             float scale_log2, void* part_o, float* part_lse, const Launch& L) {
   if (shape == kShapeDeepSeek) {
     // two head halves per tile stream, paired 8 ids apart; ids padded to whole groups of 16
     const int blocks = 16 * ((G + 7) / 8);
     return launch_kernel(attn_deepseek_kernel, dim3(blocks), dim3(64 * ds::NW), L,
                          (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv,
-                         page_table, seq_lens, B, max_pages, num_pages, (const Plan*)plan, G,
+                         page_table, seq_lens, B, max_pages, q_len, num_pages, (const Plan*)plan, G,
                          scale_log2, (uint16_t*)part_o, part_lse);
   }
   const int blocks = (G + kAttnWavesMha2Mla - 1) / kAttnWavesMha2Mla;
   return launch_kernel(attn_mha2mla_kernel, dim3(blocks), dim3(64 * kAttnWavesMha2Mla), L,
                        (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv,
-                       page_table, seq_lens, B, max_pages, num_pages, (const Plan*)plan, G,
+                       page_table, seq_lens, B, max_pages, q_len, num_pages, (const Plan*)plan, G,
                        scale_log2, (uint16_t*)part_o, part_lse);
 }
 

@@ -202,4 +202,16 @@ __device__ __forceinline__ int clamp_len(int s, int max_pages) {
   return s > cap ? cap : s;
 }
 
+// Several query tokens per sequence (q_len of them: the sequence's newest tokens, already in
+// the cache) are decoded as virtual sequences v = b * q_len + i, i < q_len. Virtual sequence v
+// reads row b of the page table and sees the first S_b - (q_len - 1 - i) tokens: each query
+// token attends to itself and to every earlier token. With q_len = 1, v = b.
+__device__ __forceinline__ int virt_row(int v, int q_len) { return q_len == 1 ? v : v / q_len; }
+// Length of virtual sequence v, given the clamped length of its page-table row.
+__device__ __forceinline__ int virt_len(int row_len, int v, int q_len) {
+  if (q_len == 1) return row_len;
+  const int s = row_len - (q_len - 1 - (v - (v / q_len) * q_len));
+  return s > 0 ? s : 0;
+}
+
 }  // namespace mla

@@ -34,13 +34,15 @@ enum Shape : int {
 // plan unit is served by two work groups, one per half of the heads.)
 constexpr int kAttnWavesMha2Mla = 4;
 
+// B counts virtual sequences (sequences x query tokens, q_len per sequence) in the three
+// decode launches; seq_lens and page_table stay per sequence.
 hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* q_abs, int B,
                          int H, const int32_t* seq_lens, const int32_t* page_table, int max_pages,
-                         int G, void* plan, const Launch& L);
+                         int q_len, int G, void* plan, const Launch& L);
 
 hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, const void* kv,
                             const int32_t* page_table, const int32_t* seq_lens, int B,
-                            int max_pages, int num_pages, const void* plan, int G,
+                            int max_pages, int q_len, int num_pages, const void* plan, int G,
                             float scale_log2, void* part_o, float* part_lse, const Launch& L);
 
 hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, const void* plan,

@@ -104,6 +104,25 @@ class Oracle:
             raise ValueError("oracle_decode_absorbed failed (%d)" % rc)
         return out, lse
 
+    def decode_tokens(self, q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens,
+                      scale=0.0, threads=0):
+        """Several query tokens per sequence: q_nope [B,T,H,d_n], q_rope [B,T,H,d_R]. Query
+        token i of sequence b is the token at position S_b - T + i (the T newest tokens are in
+        the cache); it attends to the cached tokens 0 .. S_b - T + i, itself included, i.e.
+        the decode above over the first S_b - T + 1 + i tokens of sequence b. Returns
+        out [B,T,H,d_v] and lse [B,T,H]."""
+        q_nope, q_rope = _u16(q_nope), _u16(q_rope)
+        B, T, H = q_nope.shape[:3]
+        sl = _i32(seq_lens)
+        lens = np.repeat(sl, T) - (T - 1 - np.tile(np.arange(T, dtype=np.int32), B))
+        if np.any(lens <= 0):
+            raise ValueError("every query token needs at least one token to attend to")
+        rows = np.repeat(np.arange(B), T)
+        out, lse = self.decode(q_nope.reshape(B * T, H, -1), q_rope.reshape(B * T, H, -1),
+                               W_UK, W_UV, kv_pages, _i32(page_table)[rows], lens, scale=scale,
+                               threads=threads)
+        return out.reshape(B, T, H, -1), lse.reshape(B, T, H)
+
     def decode_naive(self, q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens,
                      scale=0.0, threads=0):
         """Naive decompressed decode (K and V materialised per head). Returns (out, lse)."""
@@ -161,6 +180,10 @@ def decode(*a, **k):
 
 def decode_naive(*a, **k):
     return default().decode_naive(*a, **k)
+
+
+def decode_tokens(*a, **k):
+    return default().decode_tokens(*a, **k)
 
 
 def probs(*a, **k):

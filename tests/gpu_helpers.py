@@ -53,7 +53,11 @@ def check_against_oracle(M, inp, pairs=None, units=0, label=""):
     torch.cuda.synchronize()
     out = out.float().cpu().numpy()
     lse = lse.cpu().numpy()
-    ref, ref_lse = oracle.decode(*W.oracle_args(inp), pairs=pairs)
+    if inp["q_nope"].dim() == 4:  # several query tokens per sequence
+        assert pairs is None
+        ref, ref_lse = oracle.decode_tokens(*W.oracle_args(inp))
+    else:
+        ref, ref_lse = oracle.decode(*W.oracle_args(inp), pairs=pairs)
     if pairs is not None:
         idx = np.asarray(pairs)
         out = out[idx[:, 0], idx[:, 1]]

@@ -20,6 +20,11 @@ Pins, and the passage or fact each one rests on:
                          sit in the pool (bhfrc.com/news/60867 S3 paged layout).
   split_combine          cutting the tokens into ranges and merging by log-sum-exp gives the
                          single-pass result.
+  tokens_causal_sdpa     several query tokens per sequence (the sequence's newest tokens):
+                         torch's scaled_dot_product_attention in float64 with an explicit
+                         causal mask (query token i of T sees tokens 0 .. S - T + i) on the
+                         same decompressed K and V; one query token gives exactly the plain
+                         decode.
 """
 import math
 
@@ -195,5 +200,50 @@ def split_combine(O):
         assert np.max(np.abs(l - l1)) <= 1e-13
 
 
+def _queries(B, T, H, d_n, d_R, seed):
+    g = torch.Generator().manual_seed(seed)
+    qn = torch.randn(B, T, H, d_n, generator=g).to(torch.bfloat16)
+    qr = torch.randn(B, T, H, d_R, generator=g).to(torch.bfloat16)
+    return qn, qr
+
+
+def tokens_causal_sdpa(O):
+    for seed, (seq, T, kw) in enumerate([([5, 64, 77], 3, {}),
+                                         ([33, 4, 100], 4, dict(H=3, d_n=5, d_c=16, d_R=3)),
+                                         ([130, 2, 65], 2, dict(d_n=8, d_c=12, d_R=4))]):
+        inp = _tiny(seq, 1000 + seed, **kw)
+        B, H, d_c = inp["B"], inp["H"], inp["d_c"]
+        qn_t, qr_t = _queries(B, T, H, inp["d_n"], inp["d_R"], 1100 + seed)
+        args = list(W.oracle_args(inp))
+        args[0], args[1] = W.u16(qn_t), W.u16(qr_t)
+        out, lse = O.decode_tokens(*args)
+        assert out.shape == (B, T, H, inp["d_v"]) and lse.shape == (B, T, H)
+        qn, qr = torch.from_numpy(_f64(W.u16(qn_t))), torch.from_numpy(_f64(W.u16(qr_t)))
+        Wk = torch.from_numpy(_f64(W.u16(inp["W_UK"])))
+        Wv = torch.from_numpy(_f64(W.u16(inp["W_UV"])))
+        for b, tok in enumerate(_logical(inp)):
+            tok = torch.from_numpy(tok)
+            S = tok.shape[0]
+            c, r = tok[:, :d_c], tok[:, d_c:]
+            K = torch.cat([torch.matmul(Wk, c.T).transpose(1, 2),
+                           r.unsqueeze(0).expand(H, -1, -1)], dim=2)           # [H, S, d_n+d_R]
+            V = torch.matmul(c.unsqueeze(0), Wv)                               # [H, S, d_v]
+            Q = torch.cat([qn[b], qr[b]], dim=2).transpose(0, 1)               # [H, T, d_n+d_R]
+            mask = torch.arange(S)[None, :] <= (S - T + torch.arange(T))[:, None]  # [T, S]
+            ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask)
+            got = torch.from_numpy(out[b]).transpose(0, 1)                     # [H, T, d_v]
+            assert _rel(got.numpy(), ref.numpy()) <= 1e-12, ("tokens", b)
+            logits = torch.matmul(Q, K.transpose(1, 2)) / math.sqrt(K.shape[2])
+            ref_lse = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=2)  # [H, T]
+            assert np.max(np.abs(lse[b].T - ref_lse.numpy())) <= 1e-12, ("tokens lse", b)
+    # one query token: exactly the plain decode
+    inp = _tiny([9, 70, 3], 1200)
+    args = list(W.oracle_args(inp))
+    o1, l1 = O.decode(*args)
+    args[0], args[1] = args[0][:, None], args[1][:, None]
+    o2, l2 = O.decode_tokens(*args)
+    assert np.array_equal(o1, o2[:, 0]) and np.array_equal(l1, l2[:, 0])
+
+
 ALL = [naive_equals_absorbed, sdpa_library, rows_sum_to_one, single_token, zero_query,
-       identical_tokens, dominant_rope, permutation, split_combine]
+       identical_tokens, dominant_rope, permutation, split_combine, tokens_causal_sdpa]

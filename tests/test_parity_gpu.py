@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import workloads as W
-from tests.gpu_helpers import check_against_oracle, need_gpu, say, to_dev, gpu_decode
+import oracle
+from tests.gpu_helpers import check_against_oracle, errors, need_gpu, say, to_dev, gpu_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -107,3 +108,65 @@ def test_workload_full_size(M, cfg):
         rng = np.random.default_rng(4)
         pairs = [(b, int(h)) for b in range(inp["B"]) for h in rng.choice(inp["H"], 8, False)]
     check_against_oracle(M, inp, pairs=pairs, label="workload %d %s" % (cfg, W.CONFIGS[cfg]["name"]))
+
+
+# ---- several query tokens per sequence (the T newest tokens, causal among themselves)
+
+def _with_tokens(inp, T, seed):
+    g = torch.Generator().manual_seed(seed)
+    B, H, d_n, d_R = inp["B"], inp["H"], inp["d_n"], inp["d_R"]
+    inp["q_nope"] = torch.randn(B, T, H, d_n, generator=g).to(torch.bfloat16)
+    inp["q_rope"] = torch.randn(B, T, H, d_R, generator=g).to(torch.bfloat16)
+    return inp
+
+
+@pytest.mark.parametrize("T", [2, 4])
+@pytest.mark.parametrize("units", [0, 1, 5])
+def test_deepseek_query_tokens(M, T, units):
+    inp = _with_tokens(_inp(DS, [4, 31, 33, 300, 64 * 9 + 5], 31), T, 32)
+    check_against_oracle(M, inp, units=units, label="deepseek %d query tokens" % T)
+
+
+@pytest.mark.parametrize("T", [2, 3])
+@pytest.mark.parametrize("units", [0, 3])
+def test_mha2mla_query_tokens(M, T, units):
+    inp = _with_tokens(_inp(M2, [4, 63, 65, 1000], 33), T, 34)
+    check_against_oracle(M, inp, units=units, label="mha2mla %d query tokens" % T)
+
+
+def test_query_tokens_full_size(M):
+    # B = 16 sequences of 4096 tokens with two query tokens each (shuffled pages)
+    inp = _with_tokens(W.config_inputs(2), 2, 35)
+    check_against_oracle(M, inp, label="deepseek B=16 S=4096, 2 query tokens")
+
+
+@pytest.mark.parametrize("dims", [DS, M2], ids=["deepseek", "mha2mla"])
+def test_one_query_token_as_4d_is_plain_decode(M, dims):
+    inp = _inp(dims, [70, 300, 129], 36)
+    d = to_dev(inp)
+    say("4-d query, one token", dims["d_c"])
+    o3 = gpu_decode(M, d)
+    d4 = dict(d)
+    d4["q_nope"] = d["q_nope"][:, None].contiguous()
+    d4["q_rope"] = d["q_rope"][:, None].contiguous()
+    o4 = gpu_decode(M, d4)
+    torch.cuda.synchronize()
+    assert o4.shape == (3, 1, dims["H"], dims["d_v"])
+    assert torch.equal(o3.view(torch.int16), o4[:, 0].view(torch.int16))
+
+
+def test_query_tokens_without_context(M):
+    # S_b = 1 with 3 query tokens: tokens 0 and 1 of that sequence have nothing to attend to
+    # (out = 0, lse = -inf); token 2 is the sequence's only cached token and sees it alone
+    inp = _with_tokens(_inp(DS, [1, 200], 37), 3, 38)
+    d = to_dev(inp)
+    say("query tokens without context")
+    out, lse = gpu_decode(M, d, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(out[0, :2].float() == 0) and torch.all(torch.isneginf(lse[0, :2]))
+    one = dict(inp)
+    one["q_nope"], one["q_rope"] = inp["q_nope"][:, 2], inp["q_rope"][:, 2]
+    ref, ref_lse = oracle.decode(*W.oracle_args(one))
+    rel, mx = errors(out[:, 2].float().cpu().numpy()[:1], ref[:1])
+    assert rel <= 5e-3 and mx <= 2e-2, (rel, mx)
+    assert np.max(np.abs(lse[0, 2].cpu().numpy() - ref_lse[0])) <= 1e-2
