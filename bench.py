@@ -237,6 +237,53 @@ def run(args):
     return res
 
 
+def run_append(args):
+    """Times mla_cache_append (one new token per sequence of the workload, T = --q-len) with
+    HIP events on the library's stream; algorithmic bytes = both weights + x + the written
+    rows (it is bound by streaming the weights)."""
+    import torch
+    import mla_latent_kv_14_amd as M
+    import workloads as W
+
+    cfg = W.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hidden = 7168 if cfg["H"] == 128 else 4096  # DeepSeek-V3 and Llama-2-7B model widths
+    inp = W.config_inputs(args.workload)
+    B, T, d_c, d_R = inp["B"], args.q_len, inp["d_c"], inp["d_R"]
+    g = torch.Generator().manual_seed(cfg["seed"] + 7)
+    x = torch.randn(B, T, hidden, generator=g).to(torch.bfloat16).to(dev)
+    Wd = (torch.randn(d_c, hidden, generator=g) / hidden ** 0.5).to(torch.bfloat16).to(dev)
+    Wr = (torch.randn(d_R, hidden, generator=g) / hidden ** 0.5).to(torch.bfloat16).to(dev)
+    kv = inp["kv_pages"].to(dev)
+    pt = inp["page_table"].to(dev)
+    # room for the new tokens: append before each sequence's last T tokens
+    before = (inp["seq_lens"] - T).clamp(min=0).to(torch.int32).to(dev)
+    for _ in range(args.warmup):
+        M.cache_append(x, Wd, Wr, kv, pt, before)
+    hip = Hip()
+    e0, e1 = hip.event(), hip.event()
+    stream = torch.cuda.current_stream(dev)
+    hip.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    hip.L.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(args.steps):
+        M.cache_append(x, Wd, Wr, kv, pt, before)
+    hip.L.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    us = hip.ms(e0, e1) * 1e3 / args.steps
+    nbytes = 2 * (d_c + d_R) * hidden + 2 * B * T * hidden + 2 * B * T * (d_c + d_R)
+    return {"metric": "MLA cache append (c_KV = x W_DKV, RoPE(x W_KR)) per call",
+            "value": round(us, 3), "unit": "us", "higher_is_better": False,
+            "steps": args.steps, "warmup": args.warmup,
+            "config": {"workload": cfg["name"], "batch": B, "new_tokens_per_seq": T,
+                       "hidden": hidden, "d_latent": d_c, "d_rope": d_R},
+            "gbps": round(nbytes / us / 1e3, 1),
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_baseline(inp, alg, runs=3):
     """The fp64 oracle, as it stands, on the host cores: every (b, h) of one input set, the
     median of `runs` runs (each run well under a minute at every workload but the longest)."""
@@ -272,6 +319,9 @@ def main():
     ap.add_argument("--q-len", type=int, default=1, help="query tokens per sequence (the "
                     "sequence's newest tokens, causal among themselves); with more than one, "
                     "value counts (query token, cached token) pairs per second")
+    ap.add_argument("--append", action="store_true", help="time the cache append "
+                    "(mla_cache_append) of --q-len new tokens per sequence of the workload "
+                    "instead of the decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-only", action="store_true", help="skip the single-set warm run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -292,7 +342,7 @@ def main():
         print("bench.py measures one GPU: the decode runs on a single MI355X and has "
               "no multi-GPU path (got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
-    print(json.dumps(run(args)), flush=True)
+    print(json.dumps(run_append(args) if args.append else run(args)), flush=True)
 
 
 if __name__ == "__main__":

@@ -132,6 +132,46 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
                               void* stream, void* const* stage_events);
 
 /*
+ * Cache append (the step before the decode): the latent and the decoupled RoPE key of new
+ * tokens, written into their page slots (lpnh.cn/news/2494972 S2.1: c_kv = x W_dkv and a
+ * RoPE key taken from the hidden state; bhfrc.com/news/60867 S1 [c_KV | k_R] format, S3
+ * RoPE computed in fp32 and 64-token pages).
+ * For token i of sequence b (i < T), at position p = seq_lens[b] + i:
+ *   c_KV[c] = sum_k x[b,i,k] W_DKV[c,k]
+ *   k[j]    = sum_k x[b,i,k] W_KR[j,k]
+ *   (k[j], k[j + d_rope/2]) <- (k[j] cos a - k[j + d_rope/2] sin a,
+ *                               k[j] sin a + k[j + d_rope/2] cos a),  a = p * base^(-2j/d_rope)
+ * (fp32 sums and rotation, the angle formed in fp64), rounded to bf16 and stored at slot
+ * p % 64 of page page_table[b][p / 64]: kv_pages[page][slot] = [c_KV | k].
+ *   x          bf16 [B, T, hidden]
+ *   W_DKV      bf16 [d_latent, hidden]    (a linear layer's weight: out x in)
+ *   W_KR       bf16 [d_rope, hidden]
+ *   page_table int32 [B, max_pages_per_seq], seq_lens int32 [B]: tokens already cached
+ *   kv_pages   bf16 [num_pages, 64, d_latent + d_rope], written at the new tokens' slots only
+ * seq_lens is not updated (the caller adds T after the call). A token whose position falls
+ * outside its page-table row (p >= max_pages_per_seq * 64) is not written; page ids are
+ * clamped into the pool. Sizes: hidden a multiple of 256, d_latent a multiple of 16, d_rope 8
+ * or a multiple of 16, B*T at most 2^20. Same conventions as above otherwise (enqueued on
+ * `stream`, no allocation, argument errors before anything is enqueued). The decode's q_rope
+ * must be rotated with the same pairing and base.
+ */
+typedef struct {
+    int32_t batch;             /* B sequences                                               */
+    int32_t q_len;             /* T new tokens per sequence; 0 means 1                      */
+    int32_t hidden;            /* width of x                                                */
+    int32_t d_latent;          /* d_c                                                       */
+    int32_t d_rope;            /* d_R                                                       */
+    int32_t page_size;         /* must be 64                                                */
+    int32_t max_pages_per_seq; /* row stride of page_table                                  */
+    int32_t num_pages;         /* pages in the pool                                         */
+    float rope_base;           /* RoPE base; <= 0 means 10000                               */
+} mla_append_dims_t;
+
+mla_status_t mla_cache_append(const mla_append_dims_t* dims, const void* x, const void* W_DKV,
+                              const void* W_KR, const int32_t* page_table,
+                              const int32_t* seq_lens, void* kv_pages, void* stream);
+
+/*
  * Logical copy of the paged cache, through the same page addressing and LDS staging the
  * attention kernel uses (a bit-exact test of the page loads).
  *   dst bf16 [B, S_max, d_latent + d_rope]; row t of sequence b is token t for t < S_b and

@@ -32,6 +32,15 @@ class Dims(ctypes.Structure):
                 ("q_len", ctypes.c_int32)]
 
 
+class AppendDims(ctypes.Structure):
+    """Mirror of mla_append_dims_t."""
+    _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("d_latent", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("rope_base", ctypes.c_float)]
+
+
 class MlaError(RuntimeError):
     def __init__(self, code, text):
         super().__init__("%s: %s" % (STATUS.get(code, code), text))
@@ -57,6 +66,8 @@ def lib():
         L.mla_decode.argtypes = [dp] + [vp] * 10 + [sz, vp]
         L.mla_decode_timed.restype = c_int
         L.mla_decode_timed.argtypes = [dp] + [vp] * 10 + [sz, vp, ctypes.POINTER(vp)]
+        L.mla_cache_append.restype = c_int
+        L.mla_cache_append.argtypes = [ctypes.POINTER(AppendDims)] + [vp] * 7
         L.mla_gather_pages.restype = c_int
         L.mla_gather_pages.argtypes = [dp, vp, vp, vp, vp, vp]
         L.mla_status_str.restype = ctypes.c_char_p
@@ -193,6 +204,40 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
         code = lib().mla_decode_timed(*args, ev)
     _check(code)
     return (out, lse) if return_lse else out
+
+
+def cache_append(x, W_DKV, W_KR, kv_pages, page_table, seq_lens, rope_base=10000.0,
+                 stream=None):
+    """Writes [c_KV | RoPE(k_R)] of the new tokens into kv_pages in place (mla_cache_append).
+
+    x bf16 [B,T,hidden] (or [B,hidden] for one token), W_DKV bf16 [d_c,hidden], W_KR bf16
+    [d_R,hidden], kv_pages bf16 [P,64,d_c+d_R], page_table int32 [B,max_pages], seq_lens int32
+    [B] (tokens already cached; token i of sequence b goes to position seq_lens[b] + i).
+    """
+    dev = kv_pages.device
+    bf = torch.bfloat16
+    _want(x, "x", bf, x.dim() if x.dim() in (2, 3) else 3, dev)
+    _want(W_DKV, "W_DKV", bf, 2, dev)
+    _want(W_KR, "W_KR", bf, 2, dev)
+    _want(kv_pages, "kv_pages", bf, 3, dev)
+    _want(page_table, "page_table", torch.int32, 2, dev)
+    _want(seq_lens, "seq_lens", torch.int32, 1, dev)
+    d = AppendDims()
+    d.batch = x.shape[0]
+    d.q_len = x.shape[1] if x.dim() == 3 else 1
+    d.hidden = x.shape[-1]
+    d.d_latent, d.d_rope = W_DKV.shape[0], W_KR.shape[0]
+    if W_DKV.shape[1] != d.hidden or W_KR.shape[1] != d.hidden or \
+            kv_pages.shape[2] != d.d_latent + d.d_rope or page_table.shape[0] != d.batch:
+        raise ValueError("inconsistent shapes")
+    d.page_size = kv_pages.shape[1]
+    d.max_pages_per_seq = page_table.shape[1]
+    d.num_pages = kv_pages.shape[0]
+    d.rope_base = float(rope_base)
+    _check(lib().mla_cache_append(ctypes.byref(d), _ptr(x), _ptr(W_DKV), _ptr(W_KR),
+                                  _ptr(page_table), _ptr(seq_lens), _ptr(kv_pages),
+                                  _stream(stream, dev)))
+    return kv_pages
 
 
 def gather_pages(kv_pages, page_table, seq_lens, d_latent, max_seq_len=None, stream=None):

@@ -200,6 +200,29 @@ mla_status_t mla_gather_pages(const mla_dims_t* dims, const void* kv_pages,
                                        (hipStream_t)stream));
 }
 
+mla_status_t mla_cache_append(const mla_append_dims_t* d, const void* x, const void* W_DKV,
+                              const void* W_KR, const int32_t* page_table,
+                              const int32_t* seq_lens, void* kv_pages, void* stream) {
+  if (!d) return MLA_ERR_NULL_ARG;
+  const int T = d->q_len > 1 ? d->q_len : 1;
+  if (d->batch < 1 || d->q_len < 0 || (int64_t)d->batch * T > (1 << 20) || d->hidden < 1 ||
+      d->d_latent < 1 || d->d_rope < 1 || d->max_pages_per_seq < 1 || d->num_pages < 1 ||
+      (int64_t)d->batch * d->max_pages_per_seq > (int64_t)1 << 29 || d->page_size < 1)
+    return MLA_ERR_BAD_DIMS;
+  if (d->page_size != mla::kPage || d->hidden % 256 != 0 || d->hidden > (1 << 20) ||
+      d->d_latent % 16 != 0 || !(d->d_rope == 8 || d->d_rope % 16 == 0))
+    return MLA_ERR_UNSUPPORTED;
+  if (!x || !W_DKV || !W_KR || !page_table || !seq_lens || !kv_pages) return MLA_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(W_DKV) || !aligned16(W_KR) || !aligned16(page_table) ||
+      !aligned16(seq_lens) || !aligned16(kv_pages))
+    return MLA_ERR_MISALIGNED;
+  const double base = d->rope_base > 0.f ? (double)d->rope_base : 10000.0;
+  return hip_status(mla::launch_append(x, W_DKV, W_KR, page_table, seq_lens, kv_pages, d->batch,
+                                       T, d->hidden, d->d_latent, d->d_rope,
+                                       d->max_pages_per_seq, d->num_pages, base,
+                                       (hipStream_t)stream));
+}
+
 const char* mla_status_str(mla_status_t s) {
   switch (s) {
     case MLA_OK: return "ok";

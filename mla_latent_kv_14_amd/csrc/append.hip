@@ -1,0 +1,155 @@
+// Cache append: the latent and the decoupled RoPE key of new tokens, written into their page
+// slots (lpnh.cn/news/2494972 S2.1: c_kv = x W_dkv, and a RoPE key that is not decompressed;
+// bhfrc.com/news/60867 S1 cache format [c_KV | k_R], S3 RoPE computed in fp32, 64-token pages).
+//
+// For every new token (sequence b, i-th of its T new tokens, position p = S_b + i):
+//   c_KV[c] = sum_k x[k] W_DKV[c][k]                        (W_DKV [d_latent, hidden])
+//   k[j]    = sum_k x[k] W_KR[j][k]                         (W_KR  [d_rope, hidden])
+//   (k[j], k[j + d_rope/2]) rotated by p * base^(-2j/d_rope) (pairs of the two halves)
+// rounded to bf16 and stored at slot p % 64 of page page_table[b][p / 64].
+//
+// One work group per block of 16 output columns and eight waves; wave w sums the hidden slice
+// [w * hidden/8, (w+1) * hidden/8) on 16x16x32 bf16 MFMA (A = 16 weight rows, B = up to 64
+// token rows), the waves' partial sums meet in LDS, and four waves finish 16 token rows each.
+// The RoPE columns are grouped so that the two elements of every rotated pair sit in one
+// block: block q of the RoPE part holds pairs j in [Pq, Pq + P) in columns 0 .. P-1 (first
+// elements) and P .. 2P-1 (second elements), P = min(8, d_rope/2). The rotation angle is formed
+// in fp64 (an fp32 product p * inv_freq would carry an error of up to 2^-8 rad at p near
+// 65536); the rotation itself is fp32.
+#include <math.h>
+
+#include "device.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace app {
+constexpr int NW = 8;      // waves per work group
+constexpr int ROWS = 64;   // token rows per pass (four MFMA blocks of 16)
+}  // namespace app
+
+__global__ void __launch_bounds__(64 * app::NW)
+append_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W_DKV,
+              const uint16_t* __restrict__ W_KR, const int32_t* __restrict__ page_table,
+              const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ kv, int B, int T,
+              int hidden, int d_c, int d_R, int max_pages, int num_pages, double log2_base) {
+  using namespace app;
+  __shared__ __attribute__((aligned(16))) float red[NW][4][4][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = B * T;
+  const int W = d_c + d_R;              // elements per cached token
+  const int lat_blocks = d_c / 16;
+  const int P = d_R / 2 < 8 ? d_R / 2 : 8;  // RoPE pairs per block
+  const int cb = blockIdx.x;
+  const bool rope = cb >= lat_blocks;
+  const int q = cb - lat_blocks;        // RoPE block index
+  // weight row and output column of local column c (-1: no column)
+  auto column = [&](int c, int& out_col) -> const uint16_t* {
+    if (!rope) {
+      out_col = 16 * cb + c;
+      return W_DKV + (size_t)(16 * cb + c) * hidden;
+    }
+    int j;
+    if (c < P) j = P * q + c;
+    else if (c < 2 * P) j = P * q + (c - P) + d_R / 2;
+    else {
+      out_col = -1;
+      return W_KR;  // a valid row, its result is dropped
+    }
+    out_col = d_c + j;
+    return W_KR + (size_t)j * hidden;
+  };
+  const int G16 = lane >> 4, q16 = lane & 15;
+  int my_col;
+  const uint16_t* wrow = column(q16, my_col);  // A operand row of this lane
+  const int ksw = hidden / 32 / NW;            // 32-wide steps per wave
+  const int k0 = wave * ksw * 32 + 8 * G16;
+
+  for (int r0 = 0; r0 < R; r0 += ROWS) {
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[4] = {zero4, zero4, zero4, zero4};
+    const uint16_t* xrow[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r = r0 + 16 * m + q16;
+      xrow[m] = x + (size_t)(r < R ? r : R - 1) * hidden;  // rows past R: a valid row, dropped
+    }
+    for (int s = 0; s < ksw; ++s) {
+      const int k = k0 + 32 * s;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow + k);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (r0 + 16 * m < R) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(xrow[m] + k);
+          acc[m] = mfma_16x16x32(a, b, acc[m]);
+        }
+      }
+    }
+    // partial sums of the waves meet in LDS; wave m < 4 finishes token rows 16m .. 16m+15
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave][m][e][lane] = acc[m][e];
+    __syncthreads();
+    if (wave < 4) {
+      const int m = wave;
+      const int r = r0 + 16 * m + q16;  // token row of this lane (D column)
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) t += red[w][m][e][lane];
+        v[e] = t;  // output local column 4 * G16 + e
+      }
+      const int b = r < R ? r / T : 0, i = r < R ? r - (r / T) * T : 0;
+      const int pos = clamp_len(seq_lens[b], max_pages) + i;
+      if (rope) {
+        // pair partner: local column c +- P, which is P/4 lane groups of 16 away, same e
+        const int sh = 16 * (P / 4);
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = __shfl_xor(v[e], sh, 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 4 * G16 + e;
+          if (c < 2 * P) {
+            const int j = P * q + (c < P ? c : c - P);
+            const double theta = (double)pos * exp2(-(2.0 * j / d_R) * log2_base);
+            const float cs = (float)cos(theta), sn = (float)sin(theta);
+            // first element: x1 cos - x2 sin; second: x1 sin + x2 cos
+            v[e] = c < P ? v[e] * cs - pv[e] * sn : pv[e] * sn + v[e] * cs;
+          }
+        }
+      }
+      if (r < R && pos < max_pages * kPage) {
+        int page = page_table[(size_t)b * max_pages + pos / kPage];
+        page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+        uint16_t* dst = kv + ((size_t)page * kPage + pos % kPage) * W;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int col;
+          column(4 * G16 + e, col);
+          if (col >= 0) dst[col] = bf16_bits((__bf16)v[e]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_append(const void* x, const void* W_DKV, const void* W_KR,
+                         const int32_t* page_table, const int32_t* seq_lens, void* kv, int B,
+                         int T, int hidden, int d_c, int d_R, int max_pages, int num_pages,
+                         double rope_base, hipStream_t stream) {
+  const int P = d_R / 2 < 8 ? d_R / 2 : 8;
+  const int blocks = d_c / 16 + (d_R / 2 + P - 1) / P;
+  return launch_kernel(append_kernel, dim3(blocks), dim3(64 * app::NW), Launch{stream},
+                       (const uint16_t*)x, (const uint16_t*)W_DKV, (const uint16_t*)W_KR,
+                       page_table, seq_lens, (uint16_t*)kv, B, T, hidden, d_c, d_R, max_pages,
+                       num_pages, log2(rope_base));
+}
+
+}  // namespace mla

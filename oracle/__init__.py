@@ -164,6 +164,49 @@ class Oracle:
         return dst
 
 
+def rope_rotate(k, pos, base=10000.0):
+    """Rotary position encoding of one vector k [d] (d even) at position pos, in fp64: the
+    pairs (k[j], k[j + d/2]) turn by the angle pos * base^(-2j/d) (lpnh.cn/news/2494972 S2.1
+    RoPE on the decoupled key; pairing of the two halves is this library's reading)."""
+    k = np.asarray(k, dtype=np.float64)
+    d = k.shape[-1]
+    h = d // 2
+    out = np.empty_like(k)
+    for j in range(h):
+        a = pos * base ** (-2.0 * j / d)
+        c, s = np.cos(a), np.sin(a)
+        out[..., j] = k[..., j] * c - k[..., j + h] * s
+        out[..., j + h] = k[..., j] * s + k[..., j + h] * c
+    return out
+
+
+def cache_append(x, W_DKV, W_KR, page_table, seq_lens, base=10000.0):
+    """Cache append in fp64 (lpnh.cn/news/2494972 S2.1: c_kv = x W_dkv, and the decoupled
+    RoPE key; bhfrc.com/news/60867 S1 [c_KV | k_R] format): for token i of sequence b, at
+    position p = seq_lens[b] + i, the row [x W_DKV^T | rope(x W_KR^T, p)]. x is uint16 bf16
+    bits [B, T, hidden]; W_DKV [d_c, hidden], W_KR [d_R, hidden]. Returns rows [B, T, d_c+d_R]
+    (fp64, not rounded) and, per (b, i), its (page, slot) from the page table."""
+    x = _f64(_u16(x))
+    Wd, Wr = _f64(_u16(W_DKV)), _f64(_u16(W_KR))
+    B, T = x.shape[:2]
+    pt, sl = _i32(page_table), _i32(seq_lens)
+    P = 64
+    rows = np.zeros((B, T, Wd.shape[0] + Wr.shape[0]))
+    where = np.zeros((B, T, 2), dtype=np.int64)
+    for b in range(B):
+        for i in range(T):
+            p = int(sl[b]) + i
+            rows[b, i, :Wd.shape[0]] = Wd @ x[b, i]
+            rows[b, i, Wd.shape[0]:] = rope_rotate(Wr @ x[b, i], p, base)
+            where[b, i] = (pt[b, p // P], p % P)
+    return rows, where
+
+
+def _f64(u16):
+    """Exact fp64 value of bf16 bit patterns."""
+    return (np.asarray(u16, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 _DEFAULT = None
 
 

@@ -8,8 +8,8 @@ import pytest
 import mla_latent_kv_14_amd as M
 from mla_latent_kv_14_amd.binding import STATUS_CODE
 
-EXPECTED = ["mla_decode", "mla_decode_timed", "mla_decode_workspace_bytes", "mla_gather_pages",
-            "mla_last_hip_error", "mla_status_str"]
+EXPECTED = ["mla_cache_append", "mla_decode", "mla_decode_timed", "mla_decode_workspace_bytes",
+            "mla_gather_pages", "mla_last_hip_error", "mla_status_str"]
 
 
 def test_header_declares_the_boundary():
@@ -76,7 +76,8 @@ def test_workspace_bytes_closed_form():
     ("page_size", 16, "MLA_ERR_UNSUPPORTED"), ("batch", 0, "MLA_ERR_BAD_DIMS"),
     ("max_pages_per_seq", 0, "MLA_ERR_BAD_DIMS"), ("num_pages", 0, "MLA_ERR_BAD_DIMS"),
     ("max_seq_len", 64 * 64 + 1, "MLA_ERR_BAD_DIMS"), ("num_units", -1, "MLA_ERR_BAD_DIMS"),
-    ("num_units", 65537, "MLA_ERR_BAD_DIMS")])
+    ("num_units", 65537, "MLA_ERR_BAD_DIMS"), ("q_len", -1, "MLA_ERR_BAD_DIMS"),
+    ("q_len", 257, "MLA_ERR_BAD_DIMS")])
 def test_bad_dims(field, value, status):
     d = ds_dims(max_seq_len=0)  # 0: bounded by the page table alone
     setattr(d, field, value)
@@ -122,6 +123,55 @@ def test_gather_rejects_bad_args():
                               ctypes.c_void_p(0)) == STATUS_CODE["MLA_ERR_NULL_ARG"]
     assert L.mla_gather_pages(ctypes.byref(d), ctypes.c_void_p(0x100002), _al(2), _al(3), _al(4),
                               ctypes.c_void_p(0)) == STATUS_CODE["MLA_ERR_MISALIGNED"]
+
+
+def test_workspace_grows_with_query_tokens():
+    # T query tokens per sequence: B*T rows of queries and partial slots, units capped by the
+    # tiles of B*T rows
+    def plan(B, G):
+        return (16 + 4 * B + 31) // 32 * 32 + 32 * G
+    def al(x):
+        return (x + 255) // 256 * 256
+    d = ds_dims(B=4, max_pages=8, num_pages=32, max_seq_len=512)
+    d.q_len = 3
+    rows, units = 12, min(128, 12 * 16)
+    slots = units + rows
+    assert M.workspace_bytes(d) == (al(plan(rows, units)) + al(rows * 128 * 512 * 2)
+                                    + al(slots * 128 * 4) + al(slots * 128 * 512 * 2))
+
+
+def _append_dims(B=16, T=1, hidden=7168, d_c=512, d_R=64):
+    d = M.AppendDims()
+    d.batch, d.q_len, d.hidden, d.d_latent, d.d_rope = B, T, hidden, d_c, d_R
+    d.page_size, d.max_pages_per_seq, d.num_pages, d.rope_base = 64, 64, 1024, 10000.0
+    return d
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, "MLA_ERR_BAD_DIMS"), ("q_len", -1, "MLA_ERR_BAD_DIMS"),
+    ("hidden", 1000, "MLA_ERR_UNSUPPORTED"), ("d_latent", 500, "MLA_ERR_UNSUPPORTED"),
+    ("d_rope", 12, "MLA_ERR_UNSUPPORTED"), ("page_size", 16, "MLA_ERR_UNSUPPORTED"),
+    ("num_pages", 0, "MLA_ERR_BAD_DIMS")])
+def test_append_rejects_bad_dims(field, value, status):
+    d = _append_dims()
+    setattr(d, field, value)
+    p = [_al(k + 1) for k in range(6)]
+    assert M.lib().mla_cache_append(ctypes.byref(d), *p, ctypes.c_void_p(0)) == \
+        STATUS_CODE[status]
+
+
+def test_append_rejects_null_and_misaligned():
+    L = M.lib()
+    assert L.mla_cache_append(None, *[_al(k + 1) for k in range(6)], None) == \
+        STATUS_CODE["MLA_ERR_NULL_ARG"]
+    for i in range(6):
+        p = [_al(k + 1) for k in range(6)]
+        p[i] = ctypes.c_void_p(0)
+        assert L.mla_cache_append(ctypes.byref(_append_dims()), *p, None) == \
+            STATUS_CODE["MLA_ERR_NULL_ARG"], i
+        p[i] = ctypes.c_void_p(0x100008)
+        assert L.mla_cache_append(ctypes.byref(_append_dims()), *p, None) == \
+            STATUS_CODE["MLA_ERR_MISALIGNED"], i
 
 
 def test_status_strings():
