@@ -259,16 +259,28 @@ def run_append(args):
     pt = inp["page_table"].to(dev)
     # room for the new tokens: append before each sequence's last T tokens
     before = (inp["seq_lens"] - T).clamp(min=0).to(torch.int32).to(dev)
+    M.cache_append(x, Wd, Wr, kv, pt, before)  # checks the arguments once
+    # then the C entry point directly, with prebuilt arguments (per-call Python checks would
+    # make the loop host-bound)
+    lib = M.lib()
+    d = M.AppendDims()
+    d.batch, d.q_len, d.hidden, d.d_latent, d.d_rope = B, T, hidden, d_c, d_R
+    d.page_size, d.max_pages_per_seq, d.num_pages = 64, pt.shape[1], kv.shape[0]
+    d.rope_base = 10000.0
+    stream = torch.cuda.current_stream(dev)
+    vp = ctypes.c_void_p
+    call = [ctypes.byref(d)] + [vp(t.data_ptr()) for t in (x, Wd, Wr, pt, before, kv)] + \
+        [vp(stream.cuda_stream)]
     for _ in range(args.warmup):
-        M.cache_append(x, Wd, Wr, kv, pt, before)
+        lib.mla_cache_append(*call)
     hip = Hip()
     e0, e1 = hip.event(), hip.event()
-    stream = torch.cuda.current_stream(dev)
     hip.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     torch.cuda.synchronize()
     hip.L.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
     for _ in range(args.steps):
-        M.cache_append(x, Wd, Wr, kv, pt, before)
+        if lib.mla_cache_append(*call) != 0:
+            raise RuntimeError("mla_cache_append failed")
     hip.L.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     us = hip.ms(e0, e1) * 1e3 / args.steps

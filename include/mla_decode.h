@@ -150,8 +150,8 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
  *   kv_pages   bf16 [num_pages, 64, d_latent + d_rope], written at the new tokens' slots only
  * seq_lens is not updated (the caller adds T after the call). A token whose position falls
  * outside its page-table row (p >= max_pages_per_seq * 64) is not written; page ids are
- * clamped into the pool. Sizes: hidden a multiple of 256, d_latent a multiple of 16, d_rope 8
- * or a multiple of 16, B*T at most 2^20. Same conventions as above otherwise (enqueued on
+ * clamped into the pool. Sizes: hidden a multiple of 1024, d_latent and d_rope multiples of
+ * 4, B*T at most 2^20. Same conventions as above otherwise (enqueued on
  * `stream`, no allocation, argument errors before anything is enqueued). The decode's q_rope
  * must be rotated with the same pairing and base.
  */

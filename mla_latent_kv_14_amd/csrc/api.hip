@@ -209,8 +209,8 @@ mla_status_t mla_cache_append(const mla_append_dims_t* d, const void* x, const v
       d->d_latent < 1 || d->d_rope < 1 || d->max_pages_per_seq < 1 || d->num_pages < 1 ||
       (int64_t)d->batch * d->max_pages_per_seq > (int64_t)1 << 29 || d->page_size < 1)
     return MLA_ERR_BAD_DIMS;
-  if (d->page_size != mla::kPage || d->hidden % 256 != 0 || d->hidden > (1 << 20) ||
-      d->d_latent % 16 != 0 || !(d->d_rope == 8 || d->d_rope % 16 == 0))
+  if (d->page_size != mla::kPage || d->hidden % 1024 != 0 || d->hidden > (1 << 20) ||
+      d->d_latent % 4 != 0 || d->d_rope % 4 != 0)
     return MLA_ERR_UNSUPPORTED;
   if (!x || !W_DKV || !W_KR || !page_table || !seq_lens || !kv_pages) return MLA_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(W_DKV) || !aligned16(W_KR) || !aligned16(page_table) ||

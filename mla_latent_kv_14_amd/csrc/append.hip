@@ -8,14 +8,15 @@
 //   (k[j], k[j + d_rope/2]) rotated by p * base^(-2j/d_rope) (pairs of the two halves)
 // rounded to bf16 and stored at slot p % 64 of page page_table[b][p / 64].
 //
-// One work group per block of 16 output columns and eight waves; wave w sums the hidden slice
-// [w * hidden/8, (w+1) * hidden/8) on 16x16x32 bf16 MFMA (A = 16 weight rows, B = up to 64
-// token rows), the waves' partial sums meet in LDS, and four waves finish 16 token rows each.
-// The RoPE columns are grouped so that the two elements of every rotated pair sit in one
-// block: block q of the RoPE part holds pairs j in [Pq, Pq + P) in columns 0 .. P-1 (first
-// elements) and P .. 2P-1 (second elements), P = min(8, d_rope/2). The rotation angle is formed
-// in fp64 (an fp32 product p * inv_freq would carry an error of up to 2^-8 rad at p near
-// 65536); the rotation itself is fp32.
+// One work group per block of 4 output columns (144 work groups at the DeepSeek widths) and
+// eight waves; wave w sums the hidden slice [w * hidden/8, (w+1) * hidden/8) on 16x16x32 bf16
+// MFMA (A = the block's weight rows, each repeated four times to fill the MFMA's 16 rows;
+// B = up to 64 token rows in four blocks), four contraction steps' loads in flight at once.
+// The waves' partial sums meet in LDS, and four waves finish 16 token rows each. The RoPE
+// columns are grouped so that both elements of a rotated pair sit in one block and in one
+// lane: block q of the RoPE part holds pairs j = 2q, 2q+1 as columns 0, 1 (first elements) and
+// 2, 3 (second elements). The rotation angle is formed in fp64 (an fp32 product p * inv_freq
+// would carry an error of up to 2^-8 rad at p near 65536); the rotation itself is fp32.
 #include <math.h>
 
 #include "device.h"
@@ -24,8 +25,10 @@
 namespace mla {
 
 namespace app {
-constexpr int NW = 8;      // waves per work group
-constexpr int ROWS = 64;   // token rows per pass (four MFMA blocks of 16)
+constexpr int NW = 8;     // waves per work group
+constexpr int CB = 4;     // output columns per work group
+constexpr int ROWS = 64;  // token rows per pass (four MFMA blocks of 16)
+constexpr int U = 4;      // contraction steps whose loads are issued together
 }  // namespace app
 
 __global__ void __launch_bounds__(64 * app::NW)
@@ -40,31 +43,22 @@ append_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W_DKV
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int R = B * T;
   const int W = d_c + d_R;              // elements per cached token
-  const int lat_blocks = d_c / 16;
-  const int P = d_R / 2 < 8 ? d_R / 2 : 8;  // RoPE pairs per block
+  const int lat_blocks = d_c / CB;
   const int cb = blockIdx.x;
   const bool rope = cb >= lat_blocks;
-  const int q = cb - lat_blocks;        // RoPE block index
-  // weight row and output column of local column c (-1: no column)
-  auto column = [&](int c, int& out_col) -> const uint16_t* {
-    if (!rope) {
-      out_col = 16 * cb + c;
-      return W_DKV + (size_t)(16 * cb + c) * hidden;
-    }
-    int j;
-    if (c < P) j = P * q + c;
-    else if (c < 2 * P) j = P * q + (c - P) + d_R / 2;
-    else {
-      out_col = -1;
-      return W_KR;  // a valid row, its result is dropped
-    }
-    out_col = d_c + j;
-    return W_KR + (size_t)j * hidden;
+  const int q = cb - lat_blocks;        // RoPE block: pairs 2q, 2q+1
+  // output column of local column c, and its weight row
+  auto column = [&](int c) -> int {
+    if (!rope) return CB * cb + c;
+    return d_c + 2 * q + (c & 1) + (c >= 2 ? d_R / 2 : 0);
+  };
+  auto weight_row = [&](int c) -> const uint16_t* {
+    const int col = column(c);
+    return col < d_c ? W_DKV + (size_t)col * hidden : W_KR + (size_t)(col - d_c) * hidden;
   };
   const int G16 = lane >> 4, q16 = lane & 15;
-  int my_col;
-  const uint16_t* wrow = column(q16, my_col);  // A operand row of this lane
-  const int ksw = hidden / 32 / NW;            // 32-wide steps per wave
+  const uint16_t* wrow = weight_row(q16 % CB);  // A operand row (MFMA rows 4..15 repeat 0..3)
+  const int ksw = hidden / 32 / NW;             // 32-wide steps per wave (a multiple of U)
   const int k0 = wave * ksw * 32 + 8 * G16;
 
   for (int r0 = 0; r0 < R; r0 += ROWS) {
@@ -76,16 +70,21 @@ append_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W_DKV
       const int r = r0 + 16 * m + q16;
       xrow[m] = x + (size_t)(r < R ? r : R - 1) * hidden;  // rows past R: a valid row, dropped
     }
-    for (int s = 0; s < ksw; ++s) {
-      const int k = k0 + 32 * s;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow + k);
+    for (int s0 = 0; s0 < ksw; s0 += U) {
+      bf16x8 a[U], bx[U][4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (r0 + 16 * m < R) {
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(xrow[m] + k);
-          acc[m] = mfma_16x16x32(a, b, acc[m]);
-        }
-      }
+      for (int u = 0; u < U; ++u) a[u] = *reinterpret_cast<const bf16x8*>(wrow + k0 + 32 * (s0 + u));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          if (r0 + 16 * m < R)
+            bx[u][m] = *reinterpret_cast<const bf16x8*>(xrow[m] + k0 + 32 * (s0 + u));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          if (r0 + 16 * m < R) acc[m] = mfma_16x16x32(a[u], bx[u][m], acc[m]);
     }
     // partial sums of the waves meet in LDS; wave m < 4 finishes token rows 16m .. 16m+15
 #pragma unroll
@@ -93,35 +92,28 @@ append_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W_DKV
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[wave][m][e][lane] = acc[m][e];
     __syncthreads();
-    if (wave < 4) {
+    if (wave < 4 && G16 == 0) {  // lanes 0..15 hold MFMA rows 0..3, the block's 4 columns
       const int m = wave;
-      const int r = r0 + 16 * m + q16;  // token row of this lane (D column)
+      const int r = r0 + 16 * m + q16;  // token row of this lane
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float t = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) t += red[w][m][e][lane];
-        v[e] = t;  // output local column 4 * G16 + e
+        v[e] = t;  // local column e
       }
       const int b = r < R ? r / T : 0, i = r < R ? r - (r / T) * T : 0;
       const int pos = clamp_len(seq_lens[b], max_pages) + i;
       if (rope) {
-        // pair partner: local column c +- P, which is P/4 lane groups of 16 away, same e
-        const int sh = 16 * (P / 4);
-        float pv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = __shfl_xor(v[e], sh, 64);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = 4 * G16 + e;
-          if (c < 2 * P) {
-            const int j = P * q + (c < P ? c : c - P);
-            const double theta = (double)pos * exp2(-(2.0 * j / d_R) * log2_base);
-            const float cs = (float)cos(theta), sn = (float)sin(theta);
-            // first element: x1 cos - x2 sin; second: x1 sin + x2 cos
-            v[e] = c < P ? v[e] * cs - pv[e] * sn : pv[e] * sn + v[e] * cs;
-          }
+        for (int e = 0; e < 2; ++e) {  // pair j = 2q + e: (v[e], v[e + 2])
+          const int j = 2 * q + e;
+          const double theta = (double)pos * exp2(-(2.0 * j / d_R) * log2_base);
+          const float cs = (float)cos(theta), sn = (float)sin(theta);
+          const float x1 = v[e], x2 = v[e + 2];
+          v[e] = x1 * cs - x2 * sn;
+          v[e + 2] = x1 * sn + x2 * cs;
         }
       }
       if (r < R && pos < max_pages * kPage) {
@@ -129,11 +121,7 @@ append_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W_DKV
         page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
         uint16_t* dst = kv + ((size_t)page * kPage + pos % kPage) * W;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          int col;
-          column(4 * G16 + e, col);
-          if (col >= 0) dst[col] = bf16_bits((__bf16)v[e]);
-        }
+        for (int e = 0; e < 4; ++e) dst[column(e)] = bf16_bits((__bf16)v[e]);
       }
     }
     __syncthreads();
@@ -144,8 +132,7 @@ hipError_t launch_append(const void* x, const void* W_DKV, const void* W_KR,
                          const int32_t* page_table, const int32_t* seq_lens, void* kv, int B,
                          int T, int hidden, int d_c, int d_R, int max_pages, int num_pages,
                          double rope_base, hipStream_t stream) {
-  const int P = d_R / 2 < 8 ? d_R / 2 : 8;
-  const int blocks = d_c / 16 + (d_R / 2 + P - 1) / P;
+  const int blocks = d_c / app::CB + d_R / 4;
   return launch_kernel(append_kernel, dim3(blocks), dim3(64 * app::NW), Launch{stream},
                        (const uint16_t*)x, (const uint16_t*)W_DKV, (const uint16_t*)W_KR,
                        page_table, seq_lens, (uint16_t*)kv, B, T, hidden, d_c, d_R, max_pages,

@@ -54,8 +54,7 @@ hipError_t launch_check(const int32_t* seq_lens, const int32_t* page_table, int 
                         int num_pages, int max_len, int* flag, hipStream_t stream);
 
 // Writes [c_KV | RoPE(k_R)] of B*T new tokens (token i of sequence b at position
-// seq_lens[b] + i). Needs d_c % 16 == 0, d_R / 2 a multiple of 8 or equal to 4, and
-// hidden % 256 == 0.
+// seq_lens[b] + i). Needs d_c % 4 == 0, d_R % 4 == 0 and hidden % 1024 == 0.
 hipError_t launch_append(const void* x, const void* W_DKV, const void* W_KR,
                          const int32_t* page_table, const int32_t* seq_lens, void* kv, int B,
                          int T, int hidden, int d_c, int d_R, int max_pages, int num_pages,

@@ -149,8 +149,8 @@ def _append_dims(B=16, T=1, hidden=7168, d_c=512, d_R=64):
 
 @pytest.mark.parametrize("field,value,status", [
     ("batch", 0, "MLA_ERR_BAD_DIMS"), ("q_len", -1, "MLA_ERR_BAD_DIMS"),
-    ("hidden", 1000, "MLA_ERR_UNSUPPORTED"), ("d_latent", 500, "MLA_ERR_UNSUPPORTED"),
-    ("d_rope", 12, "MLA_ERR_UNSUPPORTED"), ("page_size", 16, "MLA_ERR_UNSUPPORTED"),
+    ("hidden", 1000, "MLA_ERR_UNSUPPORTED"), ("hidden", 1536, "MLA_ERR_UNSUPPORTED"), ("d_latent", 510, "MLA_ERR_UNSUPPORTED"),
+    ("d_rope", 10, "MLA_ERR_UNSUPPORTED"), ("page_size", 16, "MLA_ERR_UNSUPPORTED"),
     ("num_pages", 0, "MLA_ERR_BAD_DIMS")])
 def test_append_rejects_bad_dims(field, value, status):
     d = _append_dims()
