@@ -331,19 +331,49 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
     };
     {
       // Tile 0 goes out at once with the page from the unit record. Beside it, the page window
-      // of the sequence is loaded for the next tiles; that load is not tracked by the compiler
-      // and is waited for explicitly (loads complete in order: it is older than tile 0's).
+      // of the sequence is loaded for the next tiles. The window load, tile 0's loads and the
+      // wait for the window (loads complete in order: it is the oldest) form one asm
+      // statement, so the window register is complete when the compiler first sees it and no
+      // instruction can read it while the load is in flight (it is early-clobber: no input
+      // shares its register). M0, the LDS destination, steps by 4 KiB per instruction.
+      static_assert(IPW == 9, "nine loads per wave per tile");
       pw_b = lc.b;
       pw_base = lc.j / Tile::TPP;
       const int idx = pw_base + lane < max_pages ? pw_base + lane : max_pages - 1;
       const int32_t* src = page_table + (size_t)virt_row(lc.b, q_len) * max_pages + idx;
-      asm volatile("global_load_dword %0, %1, off" : "=v"(pw_v) : "v"(src) : "memory");
       nbase = Tile::base_of(kv, us.page, lc.j, num_pages);
       nvalid = min(kSub, lc.S - lc.j * kSub);
       ndst = tiles;
-      Tile::issue<4>(nbase, nvalid, dmo, ndst, vw, lane);
+      uint32_t o[IPW];
+#pragma unroll
+      for (int k = 0; k < IPW; ++k)
+        o[k] = nvalid >= kSub ? dmo[k] : Tile::src_off(vw + 4 * k, lane, nvalid);
+      uint32_t m0 = (uint32_t)(uintptr_t)(ndst + vw * 1024);
+      asm volatile(
+          "global_load_dword %0, %2, off\n\t"
+          "global_load_lds_dwordx4 %4, %3\n\t"
+          "s_add_u32 m0, m0, 0x1000\n\t"
+          "global_load_lds_dwordx4 %5, %3\n\t"
+          "s_add_u32 m0, m0, 0x1000\n\t"
+          "global_load_lds_dwordx4 %6, %3\n\t"
+          "s_add_u32 m0, m0, 0x1000\n\t"
+          "global_load_lds_dwordx4 %7, %3\n\t"
+          "s_add_u32 m0, m0, 0x1000\n\t"
+          "global_load_lds_dwordx4 %8, %3\n\t"
+          "s_add_u32 m0, m0, 0x1000\n\t"
+          "global_load_lds_dwordx4 %9, %3\n\t"
+          "s_add_u32 m0, m0, 0x1000\n\t"
+          "global_load_lds_dwordx4 %10, %3\n\t"
+          "s_add_u32 m0, m0, 0x1000\n\t"
+          "global_load_lds_dwordx4 %11, %3\n\t"
+          "s_add_u32 m0, m0, 0x1000\n\t"
+          "global_load_lds_dwordx4 %12, %3\n\t"
+          "s_waitcnt vmcnt(9)"
+          : "=&v"(pw_v), "+{m0}"(m0)
+          : "v"(src), "s"(nbase), "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]),
+            "v"(o[5]), "v"(o[6]), "v"(o[7]), "v"(o[8])
+          : "memory", "scc");
       advance();
-      asm volatile("s_waitcnt vmcnt(%1)" : "+v"(pw_v) : "n"(IPW) : "memory");
     }
     while (issued < 3 && issued < n) issue_next();
     wait_tiles_after<IPW>(issued - 1);  // tile 0 landed
