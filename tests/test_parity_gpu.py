@@ -170,3 +170,17 @@ def test_query_tokens_without_context(M):
     rel, mx = errors(out[:, 2].float().cpu().numpy()[:1], ref[:1])
     assert rel <= 5e-3 and mx <= 2e-2, (rel, mx)
     assert np.max(np.abs(lse[0, 2].cpu().numpy() - ref_lse[0])) <= 1e-2
+
+
+def test_more_sequences_than_the_plan_keeps_in_lds(M):
+    # over 4096 sequences: the plan builder walks the units from each sequence instead of
+    # searching offsets held in LDS
+    lens = [1 + (13 * i) % 40 for i in range(4200)]
+    check_against_oracle(M, _inp(DS, lens, 39), label="deepseek 4200 short")
+
+
+def test_query_tokens_over_4096_rows(M):
+    # 2100 sequences x 2 query tokens = 4200 virtual sequences (the same plan path)
+    lens = [2 + (7 * i) % 30 for i in range(2100)]
+    inp = _with_tokens(_inp(M2, lens, 40), 2, 41)
+    check_against_oracle(M, inp, label="mha2mla 2100 x 2 query tokens")
