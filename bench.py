@@ -237,6 +237,66 @@ def run(args):
     return res
 
 
+def run_out(args):
+    """Times mla_decode_out (the decode with the merged output projection W_UVO
+    [hidden, H*d_c]) on the workload, cold (input sets rotated as in the decode bench), with
+    HIP events around K plain calls."""
+    import torch
+    import mla_latent_kv_14_amd as M
+    import workloads as W
+
+    cfg = W.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hidden = args.out_proj
+    base = W.config_inputs(args.workload)
+    alg = algorithmic(base)
+    K = base["H"] * base["d_c"]
+    wbytes = 2 * hidden * K
+    n_sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / (alg["bytes"] + wbytes)))
+    sets = []
+    for i in range(n_sets):
+        inp = base if i == 0 else W.config_inputs(args.workload, seed=cfg["seed"] + 1000 * i)
+        g = torch.Generator().manual_seed(cfg["seed"] + 1000 * i + 9)
+        inp = dict(inp)
+        inp["W_UVO"] = (torch.randn(hidden, K, generator=g) / K ** 0.5).to(torch.bfloat16)
+        sets.append({k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()})
+    d0 = sets[0]
+    dims = M.make_dims(d0["q_nope"], d0["q_rope"], d0["W_UK"], d0["W_UV"], d0["kv_pages"],
+                       d0["page_table"])
+    ws_bytes = M.workspace_bytes(dims)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = [torch.empty((d["B"], hidden), dtype=torch.bfloat16, device=dev) for d in sets]
+    stream = torch.cuda.current_stream(dev)
+    vp = ctypes.c_void_p
+    lib = M.lib()
+    calls = [[ctypes.byref(dims), ctypes.c_int32(hidden)] +
+             [vp(d[k].data_ptr()) for k in ("q_nope", "q_rope", "W_UK", "W_UVO", "kv_pages",
+                                            "page_table", "seq_lens")] +
+             [vp(o.data_ptr()), vp(0), vp(ws.data_ptr()), ctypes.c_size_t(ws_bytes),
+              vp(stream.cuda_stream)] for d, o in zip(sets, outs)]
+    for i in range(args.warmup):
+        lib.mla_decode_out(*calls[i % n_sets])
+    hip = Hip()
+    e0, e1 = hip.event(), hip.event()
+    hip.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    hip.L.hipEventRecord(e0, vp(stream.cuda_stream))
+    for i in range(args.steps):
+        if lib.mla_decode_out(*calls[i % n_sets]) != 0:
+            raise RuntimeError("mla_decode_out failed")
+    hip.L.hipEventRecord(e1, vp(stream.cuda_stream))
+    torch.cuda.synchronize()
+    sec = hip.ms(e0, e1) * 1e-3 / args.steps
+    nbytes = alg["bytes"] - 2 * base["H"] * base["d_c"] * base["d_v"] + wbytes \
+        - 2 * base["B"] * base["H"] * base["d_v"] + 2 * base["B"] * hidden
+    return {"metric": "MLA decode with merged output projection, KV-tokens/s",
+            "value": round(alg["sumS"] / sec, 1), "unit": "KV-tokens/s",
+            "ms_per_step": round(sec * 1e3, 5), "steps": args.steps, "warmup": args.warmup,
+            "config": {"workload": cfg["name"], "hidden": hidden, "input_sets_rotated": n_sets},
+            "gbps": round(nbytes / sec / 1e9, 1)}
+
+
 def run_append(args):
     """Times mla_cache_append (one new token per sequence of the workload, T = --q-len) with
     HIP events on the library's stream; algorithmic bytes = both weights + x + the written
@@ -331,6 +391,8 @@ def main():
     ap.add_argument("--q-len", type=int, default=1, help="query tokens per sequence (the "
                     "sequence's newest tokens, causal among themselves); with more than one, "
                     "value counts (query token, cached token) pairs per second")
+    ap.add_argument("--out-proj", type=int, default=0, metavar="HIDDEN",
+                    help="time mla_decode_out (merged W_UV W_O to width HIDDEN) instead")
     ap.add_argument("--append", action="store_true", help="time the cache append "
                     "(mla_cache_append) of --q-len new tokens per sequence of the workload "
                     "instead of the decode")
@@ -354,7 +416,13 @@ def main():
         print("bench.py measures one GPU: the decode runs on a single MI355X and has "
               "no multi-GPU path (got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
-    print(json.dumps(run_append(args) if args.append else run(args)), flush=True)
+    if args.append:
+        res = run_append(args)
+    elif args.out_proj:
+        res = run_out(args)
+    else:
+        res = run(args)
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

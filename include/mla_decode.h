@@ -132,6 +132,24 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
                               void* stream, void* const* stage_events);
 
 /*
+ * The decode with the output projection merged into the up-projection (lpnh.cn/news/2494972
+ * S2.2: W_uv and W_o are merged into one matrix offline): instead of out[b,h,:] = o_lat W_UV[h]
+ * it returns
+ *   out_hidden[b, n] = sum_h sum_c o_lat[b,h,c] * W_UVO[n, h*d_latent + c]
+ * where the caller has formed W_UVO[n, h*d_latent + c] = sum_e W_UV[h,c,e] W_O[h*d_v + e, n].
+ *   W_UVO      bf16 [hidden, H * d_latent]            (replaces W_UV)
+ *   out_hidden bf16 [B, T, hidden]                     written
+ * Every other argument, the workspace size (mla_decode_workspace_bytes) and the conventions
+ * are those of mla_decode. Needs hidden a multiple of 16 (at most 2^20) and H * d_latent a
+ * multiple of 1024 (both supported shapes are). Returns MLA_ERR_BAD_DIMS for hidden < 1.
+ */
+mla_status_t mla_decode_out(const mla_dims_t* dims, int32_t hidden, const void* q_nope,
+                            const void* q_rope, const void* W_UK, const void* W_UVO,
+                            const void* kv_pages, const int32_t* page_table,
+                            const int32_t* seq_lens, void* out_hidden, float* lse_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Cache append (the step before the decode): the latent and the decoupled RoPE key of new
  * tokens, written into their page slots (lpnh.cn/news/2494972 S2.1: c_kv = x W_dkv and a
  * RoPE key taken from the hidden state; bhfrc.com/news/60867 S1 [c_KV | k_R] format, S3

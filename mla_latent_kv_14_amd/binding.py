@@ -66,6 +66,8 @@ def lib():
         L.mla_decode.argtypes = [dp] + [vp] * 10 + [sz, vp]
         L.mla_decode_timed.restype = c_int
         L.mla_decode_timed.argtypes = [dp] + [vp] * 10 + [sz, vp, ctypes.POINTER(vp)]
+        L.mla_decode_out.restype = c_int
+        L.mla_decode_out.argtypes = [dp, ctypes.c_int32] + [vp] * 10 + [sz, vp]
         L.mla_cache_append.restype = c_int
         L.mla_cache_append.argtypes = [ctypes.POINTER(AppendDims)] + [vp] * 7
         L.mla_gather_pages.restype = c_int
@@ -203,6 +205,51 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
         ev = (ctypes.c_void_p * 6)(*[e or None for e in kernel_events])
         code = lib().mla_decode_timed(*args, ev)
     _check(code)
+    return (out, lse) if return_lse else out
+
+
+def decode_out(q_nope, q_rope, W_UK, W_UVO, kv_pages, page_table, seq_lens, out=None,
+               lse=None, max_seq_len=None, softmax_scale=None, num_units=0, workspace=None,
+               stream=None, return_lse=False):
+    """The decode with the merged output projection (mla_decode_out): W_UVO bf16
+    [hidden, H*d_c] replaces W_UV; returns out bf16 [B, hidden] ([B, T, hidden] for 4-d
+    queries), and lse fp32 [B, H] ([B, T, H]) when return_lse."""
+    dev = q_nope.device
+    if dev.type != "cuda":
+        raise ValueError("mla decode runs on a HIP device; got %s" % dev)
+    bf, i32 = torch.bfloat16, torch.int32
+    nq = q_nope.dim() if isinstance(q_nope, torch.Tensor) else 3
+    if nq not in (3, 4):
+        raise ValueError("q_nope must be [B,H,d_n] or [B,T,H,d_n]")
+    for t, n, dt, nd in ((q_nope, "q_nope", bf, nq), (q_rope, "q_rope", bf, nq),
+                         (W_UK, "W_UK", bf, 3), (W_UVO, "W_UVO", bf, 2),
+                         (kv_pages, "kv_pages", bf, 3), (page_table, "page_table", i32, 2),
+                         (seq_lens, "seq_lens", i32, 1)):
+        _want(t, n, dt, nd, dev)
+    H, d_c = W_UK.shape[0], W_UK.shape[2]
+    hidden = W_UVO.shape[0]
+    if W_UVO.shape[1] != H * d_c:
+        raise ValueError("W_UVO must be [hidden, H*d_c] = [*, %d]" % (H * d_c))
+    # d_v does not enter this call; the dims carry the width of the supported shapes
+    dims = make_dims(q_nope, q_rope, W_UK, torch.empty((H, d_c, 128), dtype=bf, device="meta"),
+                     kv_pages, page_table, max_seq_len, softmax_scale, num_units)
+    B = dims.batch
+    lead = (B,) if nq == 3 else (B, dims.q_len)
+    if out is None:
+        out = torch.empty(lead + (hidden,), dtype=bf, device=dev)
+    else:
+        _want(out, "out", bf, nq - 1, dev)
+    if return_lse and lse is None:
+        lse = torch.empty(lead + (H,), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _want(lse, "lse", torch.float32, nq - 1, dev)
+    nbytes = workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().mla_decode_out(ctypes.byref(dims), hidden, _ptr(q_nope), _ptr(q_rope),
+                                _ptr(W_UK), _ptr(W_UVO), _ptr(kv_pages), _ptr(page_table),
+                                _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace),
+                                workspace.numel(), _stream(stream, dev)))
     return (out, lse) if return_lse else out
 
 

@@ -111,14 +111,24 @@ size_t mla_decode_workspace_bytes(const mla_dims_t* dims) {
   return layout(dims, s).total;
 }
 
-mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
-                              const void* W_UK, const void* W_UV, const void* kv_pages,
-                              const int32_t* page_table, const int32_t* seq_lens, void* out,
-                              float* lse_out, void* workspace, size_t workspace_bytes,
-                              void* stream, void* const* stage_events) {
+}  // extern "C"
+
+namespace {
+
+// The decode. hidden == 0: W_up is W_UV and out is [rows][H][d_v]. hidden > 0: W_up is the
+// merged W_UVO [hidden][H * d_latent] and out is [rows][hidden] (the combine writes the merged
+// latent rows into the query region of the workspace, dead by then, and a product with W_UVO
+// follows).
+mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
+                         const void* q_rope, const void* W_UK, const void* W_UV,
+                         const void* kv_pages, const int32_t* page_table,
+                         const int32_t* seq_lens, void* out, float* lse_out, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* stage_events) {
   ShapeInfo s;
   mla_status_t st = check_dims(dims, &s);
   if (st != MLA_OK) return st;
+  if (hidden < 0 || hidden > (1 << 20)) return MLA_ERR_BAD_DIMS;
+  if (hidden > 0 && (hidden % 16 != 0 || (s.H * s.DC) % 1024 != 0)) return MLA_ERR_UNSUPPORTED;
   if (!q_nope || !q_rope || !W_UK || !W_UV || !kv_pages || !page_table || !seq_lens || !out)
     return MLA_ERR_NULL_ARG;
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(W_UK) || !aligned16(W_UV) ||
@@ -166,9 +176,39 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
                                         scale_log2, ws + L.part_o, (float*)(ws + L.part_lse),
                                         ctx(1)));
   if (st != MLA_OK) return st;
-  return hip_status(mla::launch_combine(s.shape, ws + L.part_o, (const float*)(ws + L.part_lse),
-                                        ws + L.plan, seq_lens, W_UV, out, lse_out, R, s.H, mp,
-                                        ctx(2)));
+  if (hidden == 0)
+    return hip_status(mla::launch_combine(s.shape, ws + L.part_o,
+                                          (const float*)(ws + L.part_lse), ws + L.plan, seq_lens,
+                                          W_UV, out, lse_out, R, s.H, mp, ctx(2)));
+  st = hip_status(mla::launch_combine_latent(s.shape, ws + L.part_o,
+                                             (const float*)(ws + L.part_lse), ws + L.plan,
+                                             ws + L.q_abs, lse_out, R, s.H, ctx(2)));
+  if (st != MLA_OK) return st;
+  return hip_status(mla::launch_linear(ws + L.q_abs, W_UV, out, R, s.H * s.DC, hidden,
+                                       mla::Launch{hs}));
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                              const void* W_UK, const void* W_UV, const void* kv_pages,
+                              const int32_t* page_table, const int32_t* seq_lens, void* out,
+                              float* lse_out, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* stage_events) {
+  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out,
+                     lse_out, workspace, workspace_bytes, stream, stage_events);
+}
+
+mla_status_t mla_decode_out(const mla_dims_t* dims, int32_t hidden, const void* q_nope,
+                            const void* q_rope, const void* W_UK, const void* W_UVO,
+                            const void* kv_pages, const int32_t* page_table,
+                            const int32_t* seq_lens, void* out_hidden, float* lse_out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (hidden < 1) return MLA_ERR_BAD_DIMS;
+  return decode_call(dims, hidden, q_nope, q_rope, W_UK, W_UVO, kv_pages, page_table, seq_lens,
+                     out_hidden, lse_out, workspace, workspace_bytes, stream, nullptr);
 }
 
 mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* q_rope,

@@ -33,7 +33,9 @@ constexpr int CAP = 8;    // slots per thread whose loads are issued together
 constexpr int kWholeHeadGroups = 256;
 }  // namespace comb
 
-template <int H, int DC, int DV, int EB>
+// LAT: write the merged latent rows o_lat [B][H][DC] (bf16) to `out` instead of applying W_UV
+// (the output projection then runs as a separate product with a merged weight).
+template <int H, int DC, int DV, int EB, bool LAT = false>
 __global__ void __launch_bounds__(comb::NT)
 combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
                const Plan* __restrict__ plan, const uint16_t* __restrict__ W_UV,
@@ -66,6 +68,7 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
 
   // ---- stage W_UV[h][:, eblk*EB : +EB] (completes during the merge)
   const char* Wg = reinterpret_cast<const char*>(W_UV + (size_t)h * DC * DV + (size_t)eblk * EB);
+  if (!LAT)
   for (int k = wave; k < NCHUNK / 64; k += NT / 64) {
     const int q = k * 64 + lane;
     const int row = q / (ROWB / 16), p = q % (ROWB / 16);
@@ -190,10 +193,15 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
       bf16x8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (__bf16)a[e];
-      *reinterpret_cast<MLA_LDS bf16x8*>(ol + bi * OPITCH + ch * 16) = o;
+      if (LAT) {
+        if (b < B) *reinterpret_cast<bf16x8*>(out + ((size_t)b * H + h) * DC + ch * 8) = o;
+      } else {
+        *reinterpret_cast<MLA_LDS bf16x8*>(ol + bi * OPITCH + ch * 16) = o;
+      }
       if (ch == 0 && eblk == 0 && b < B && lse_out) lse_out[(size_t)b * H + h] = L;
     }
   }
+  if (LAT) return;
   wait_vmcnt<0>();  // W block
   block_sync();
 
@@ -217,6 +225,20 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
       *reinterpret_cast<bf16x4*>(out + ((size_t)b * H + h) * DV + e0) = o;
     }
   }
+}
+
+hipError_t launch_combine_latent(int shape, const void* part_o, const float* part_lse,
+                                 const void* plan, void* o_lat, float* lse_out, int B, int H,
+                                 const Launch& L) {
+  const int groups = H * ((B + comb::SEQ - 1) / comb::SEQ);
+  const uint16_t* po = (const uint16_t*)part_o;
+  const Plan* pl = (const Plan*)plan;
+  uint16_t* o = (uint16_t*)o_lat;
+  if (shape == kShapeDeepSeek)
+    return launch_kernel(combine_kernel<128, 512, 128, 128, true>, dim3(groups), dim3(comb::NT), L,
+                         po, part_lse, pl, (const uint16_t*)nullptr, o, lse_out, B, groups);
+  return launch_kernel(combine_kernel<32, 64, 128, 128, true>, dim3(groups), dim3(comb::NT), L, po,
+                       part_lse, pl, (const uint16_t*)nullptr, o, lse_out, B, groups);
 }
 
 hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, const void* plan,

@@ -49,6 +49,16 @@ hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, 
                           const int32_t* seq_lens, const void* W_UV, void* out, float* lse_out,
                           int B, int H, int max_pages, const Launch& L);
 
+// The combine kernel's latent-output mode: merged latent rows o_lat bf16 [B][H][d_latent]
+// (B virtual sequences), no up-projection.
+hipError_t launch_combine_latent(int shape, const void* part_o, const float* part_lse,
+                                 const void* plan, void* o_lat, float* lse_out, int B, int H,
+                                 const Launch& L);
+
+// out bf16 [R][N] = x bf16 [R][K] * W bf16 [N][K]^T. Needs K % 1024 == 0 and N % 16 == 0.
+hipError_t launch_linear(const void* x, const void* W, void* out, int R, int K, int N,
+                         const Launch& L);
+
 // Sets bits of *flag (cleared first) for out-of-range lengths (1) or used page ids (2).
 hipError_t launch_check(const int32_t* seq_lens, const int32_t* page_table, int B, int max_pages,
                         int num_pages, int max_len, int* flag, hipStream_t stream);

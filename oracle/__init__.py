@@ -164,6 +164,30 @@ class Oracle:
         return dst
 
 
+def decode_out(q_nope, q_rope, W_UK, W_UVO, kv_pages, page_table, seq_lens, scale=0.0,
+               threads=0):
+    """The decode followed by the merged output projection (lpnh.cn/news/2494972 S2.2: W_uv
+    and W_o merged offline): out[b, n] = sum_{h,c} o_lat[b,h,c] W_UVO[n, h*d_c + c], with
+    o_lat the latent attention output (the decode's result before W_UV). W_UVO is uint16 bf16
+    bits [hidden, H*d_c] or an fp64 array. Queries [B,H,.] or [B,T,H,.]. Returns
+    (out [.., hidden], lse [.., H])."""
+    q_nope = _u16(q_nope)
+    H, d_c = W_UK.shape[0], W_UK.shape[2]
+    # o_lat: the decode with W_UV = identity per head (exact in fp64)
+    eye = np.zeros((H, d_c, d_c), dtype=np.uint16)
+    eye[:, np.arange(d_c), np.arange(d_c)] = 0x3F80  # bf16 1.0
+    if q_nope.ndim == 4:
+        o_lat, lse = default().decode_tokens(q_nope, q_rope, W_UK, eye, kv_pages, page_table,
+                                             seq_lens, scale=scale, threads=threads)
+    else:
+        o_lat, lse = default().decode(q_nope, q_rope, W_UK, eye, kv_pages, page_table, seq_lens,
+                                      scale=scale, threads=threads)
+    W = np.asarray(W_UVO)
+    W = _f64(W) if W.dtype == np.uint16 else W.astype(np.float64)
+    out = o_lat.reshape(o_lat.shape[:-2] + (H * d_c,)) @ W.T
+    return out, lse
+
+
 def rope_rotate(k, pos, base=10000.0):
     """Rotary position encoding of one vector k [d] (d even) at position pos, in fp64: the
     pairs (k[j], k[j + d/2]) turn by the angle pos * base^(-2j/d) (lpnh.cn/news/2494972 S2.1

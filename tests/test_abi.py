@@ -8,8 +8,9 @@ import pytest
 import mla_latent_kv_14_amd as M
 from mla_latent_kv_14_amd.binding import STATUS_CODE
 
-EXPECTED = ["mla_cache_append", "mla_decode", "mla_decode_timed", "mla_decode_workspace_bytes",
-            "mla_gather_pages", "mla_last_hip_error", "mla_status_str"]
+EXPECTED = ["mla_cache_append", "mla_decode", "mla_decode_out", "mla_decode_timed",
+            "mla_decode_workspace_bytes", "mla_gather_pages", "mla_last_hip_error",
+            "mla_status_str"]
 
 
 def test_header_declares_the_boundary():
@@ -138,6 +139,16 @@ def test_workspace_grows_with_query_tokens():
     slots = units + rows
     assert M.workspace_bytes(d) == (al(plan(rows, units)) + al(rows * 128 * 512 * 2)
                                     + al(slots * 128 * 4) + al(slots * 128 * 512 * 2))
+
+
+def test_decode_out_rejects_bad_hidden():
+    L = M.lib()
+    d = ds_dims()
+    p = [_al(k + 1) for k in range(8)]
+    for hidden, status in ((0, "MLA_ERR_BAD_DIMS"), (-4, "MLA_ERR_BAD_DIMS"),
+                           (100, "MLA_ERR_UNSUPPORTED")):
+        assert L.mla_decode_out(ctypes.byref(d), hidden, *p, ctypes.c_void_p(0), _al(9),
+                                M.workspace_bytes(d), ctypes.c_void_p(0)) == STATUS_CODE[status]
 
 
 def _append_dims(B=16, T=1, hidden=7168, d_c=512, d_R=64):
