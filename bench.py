@@ -47,9 +47,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 ATTN_SOURCES = ["attn.hip", "paged_tile.h", "device.h"]
 
 
-def algorithmic(inp, T=1):
+def algorithmic(inp, T=1, row_bytes=None):
     """Algorithmic work of one call with T query tokens per sequence (query token i of
-    sequence b attends to S_b - T + 1 + i tokens; the cache is read once)."""
+    sequence b attends to S_b - T + 1 + i tokens; the cache is read once). row_bytes: cache
+    bytes per token (default the bf16 row, (d_c + d_R) * 2)."""
     B, H = inp["B"], inp["H"]
     d_n, d_c, d_R, d_v = inp["d_n"], inp["d_c"], inp["d_R"], inp["d_v"]
     lens = [int(x) for x in inp["seq_lens"]]
@@ -57,10 +58,11 @@ def algorithmic(inp, T=1):
     A = sum(max(0, s - T + 1 + i) for s in lens for i in range(T))  # (query, token) pairs
     Q = B * T                                                        # query tokens
     mp = inp["max_pages"]
+    rb = (d_c + d_R) * 2 if row_bytes is None else row_bytes
     flops = 2 * Q * H * d_n * d_c + 2 * H * (d_c + d_R) * A + 2 * H * d_c * A + 2 * Q * H * d_c * d_v
-    nbytes = (S * (d_c + d_R) * 2 + 2 * H * d_c * (d_n + d_v) + 2 * Q * H * (d_n + d_R)
+    nbytes = (S * rb + 2 * H * d_c * (d_n + d_v) + 2 * Q * H * (d_n + d_R)
               + 2 * Q * H * d_v + 4 * (B * mp + B))
-    attn_bytes = S * (d_c + d_R) * 2 + 2 * Q * H * (d_c + d_R) + 4 * (B * mp + B)
+    attn_bytes = S * rb + 2 * Q * H * (d_c + d_R) + 4 * (B * mp + B)
     attn_flops = 2 * H * (d_c + d_R) * A + 2 * H * d_c * A
     return dict(sumS=A, flops=flops, bytes=nbytes, attn_bytes=attn_bytes, attn_flops=attn_flops)
 
@@ -137,17 +139,28 @@ def run(args):
             inp["q_rope"] = torch.randn(B, T, H, inp["d_R"], generator=g).to(torch.bfloat16)
         return inp
 
-    base = with_tokens(W.config_inputs(args.workload), cfg["seed"] + 500)
-    alg = algorithmic(base, T)
+    def with_fp8(inp, seed):  # the FP8 copy of the cache, with per-token scales
+        if args.kv_fp8:
+            kv8, sc = W.fp8_cache(inp, seed=seed)
+            inp["kv_pages"], inp["kv_scales"] = kv8, sc
+        return inp
+
+    fp8_row = cfg["d_c"] + 2 * cfg["d_R"] + 4  # FP8 c_KV + bf16 k_R + fp32 scale
+    base = with_fp8(with_tokens(W.config_inputs(args.workload), cfg["seed"] + 500),
+                    cfg["seed"] + 700)
+    alg = algorithmic(base, T, fp8_row if args.kv_fp8 else None)
     n_sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / alg["bytes"]))
     sets = []
     for i in range(n_sets):
-        inp = base if i == 0 else with_tokens(
-            W.config_inputs(args.workload, seed=cfg["seed"] + 1000 * i), cfg["seed"] + 1000 * i + 500)
+        inp = base if i == 0 else with_fp8(with_tokens(
+            W.config_inputs(args.workload, seed=cfg["seed"] + 1000 * i),
+            cfg["seed"] + 1000 * i + 500), cfg["seed"] + 1000 * i + 700)
         sets.append({k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()})
     d0 = sets[0]
     dims = M.make_dims(d0["q_nope"], d0["q_rope"], d0["W_UK"], d0["W_UV"], d0["kv_pages"],
                        d0["page_table"])
+    if args.kv_fp8 and cfg["H"] != 32:
+        raise SystemExit("--kv-fp8 is built for the MHA2MLA widths (--workload 5)")
     ws_bytes = M.workspace_bytes(dims)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     outs = [torch.empty(((d["B"],) if T == 1 else (d["B"], T)) + (d["H"], d["d_v"]),
@@ -155,10 +168,12 @@ def run(args):
     stream = torch.cuda.current_stream(dev)
     vp = ctypes.c_void_p
 
+    names = ("q_nope", "q_rope", "W_UK", "W_UV", "kv_pages") + \
+        (("kv_scales",) if args.kv_fp8 else ()) + ("page_table", "seq_lens")
+
     def argv(i):
         d = sets[i]
-        return [vp(d[k].data_ptr()) for k in ("q_nope", "q_rope", "W_UK", "W_UV", "kv_pages",
-                                               "page_table", "seq_lens")] + \
+        return [vp(d[k].data_ptr()) for k in names] + \
             [vp(outs[i].data_ptr()), vp(0), vp(ws.data_ptr()), ctypes.c_size_t(ws_bytes),
              vp(stream.cuda_stream)]
     call_args = [argv(i) for i in range(n_sets)]
@@ -169,8 +184,10 @@ def run(args):
     ev_arr = [(vp * 6)(*e) for e in ev]
     nullev = ctypes.POINTER(vp)()
 
+    entry = lib.mla_decode_fp8 if args.kv_fp8 else lib.mla_decode_timed
+
     def step(i, events=nullev):
-        rc = lib.mla_decode_timed(dref, *call_args[i % n_sets], events)
+        rc = entry(dref, *call_args[i % n_sets], events)
         if rc != 0:
             raise RuntimeError("mla_decode failed: %s" % lib.mla_status_str(rc).decode())
 
@@ -197,7 +214,7 @@ def run(args):
 
     attn_s = stage_ms[1] * 1e-3
     achieved = alg["attn_bytes"] / attn_s / 1e9
-    traffic = measured_traffic(cfg["name"])
+    traffic = None if args.kv_fp8 else measured_traffic(cfg["name"])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": "attn_deepseek_kernel" if cfg["H"] == 128
@@ -213,7 +230,9 @@ def run(args):
                    "heads": cfg["H"], "d_nope": cfg["d_n"], "d_latent": cfg["d_c"],
                    "d_rope": cfg["d_R"], "d_v": cfg["d_v"], "page_size": 64,
                    "page_table": cfg["layout"], "input_sets_rotated": n_sets,
-                   "query_tokens_per_seq": T},
+                   "query_tokens_per_seq": T,
+                   "kv_cache": ("fp8_e4m3 c_KV + bf16 k_R + fp32 scale per token, %d B"
+                                % fp8_row) if args.kv_fp8 else "bf16"},
         "tflops": round(alg["flops"] / sec / 1e12, 2),
         "gbps": round(alg["bytes"] / sec / 1e9, 1),
         "roofline_frac_call": round(call_frac, 4),
@@ -230,7 +249,7 @@ def run(args):
     for e in ev:
         for x in e:
             hip.destroy(x)
-    if not args.no_cpu and T == 1:
+    if not args.no_cpu and T == 1 and not args.kv_fp8:
         res["cpu_baseline"] = cpu_baseline(base, alg)
     else:
         res["cpu_baseline"] = None
@@ -264,6 +283,8 @@ def run_out(args):
     d0 = sets[0]
     dims = M.make_dims(d0["q_nope"], d0["q_rope"], d0["W_UK"], d0["W_UV"], d0["kv_pages"],
                        d0["page_table"])
+    if args.kv_fp8 and cfg["H"] != 32:
+        raise SystemExit("--kv-fp8 is built for the MHA2MLA widths (--workload 5)")
     ws_bytes = M.workspace_bytes(dims)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     outs = [torch.empty((d["B"], hidden), dtype=torch.bfloat16, device=dev) for d in sets]
@@ -396,6 +417,8 @@ def main():
     ap.add_argument("--append", action="store_true", help="time the cache append "
                     "(mla_cache_append) of --q-len new tokens per sequence of the workload "
                     "instead of the decode")
+    ap.add_argument("--kv-fp8", action="store_true", help="decode over an FP8 copy of the "
+                    "cache with per-token scales (MHA2MLA widths: --workload 5)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold-only", action="store_true", help="skip the single-set warm run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

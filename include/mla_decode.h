@@ -132,6 +132,29 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
                               void* stream, void* const* stage_events);
 
 /*
+ * The decode over a quantised latent cache: c_KV stored as 8-bit floats with a scale per token
+ * (bhfrc.com/news/60867 S1 and S5 quantise the latent cache that the decode gathers; this is
+ * the FP8 form of that cache). Built for the MHA2MLA widths (H=32, d_nope=120, d_latent=64,
+ * d_rope=8, d_v=128) only; other widths return MLA_ERR_UNSUPPORTED.
+ *   kv_pages   uint8 [num_pages, 64, d_latent + 2*d_rope]  token row = [c_KV as d_latent
+ *              FP8 E4M3 bytes (OCP format: 4 exponent bits, bias 7, 3 mantissa bits, no
+ *              infinities, S.1111.111 = NaN) | k_R as d_rope bf16 values]
+ *   kv_scales  fp32 [num_pages, 64]                      the scale of the token in each slot:
+ *              c_KV[c] = value(byte c) * kv_scales[page][slot]
+ * The kernel forms each c_KV element as the fp32 product rounded to bf16 (RNE) and then runs
+ * the bf16 decode, so with power-of-two scales the result is that of mla_decode on the bf16
+ * cache holding the products exactly. Slots at or past S_b (bytes and scales) are never read
+ * into the result. kv_scales must be 16-byte aligned and non-NULL; everything else, including
+ * q_len, the workspace size and stage_events (NULL or six events, as for mla_decode_timed),
+ * is as for mla_decode_timed.
+ */
+mla_status_t mla_decode_fp8(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                            const void* W_UK, const void* W_UV, const void* kv_pages,
+                            const float* kv_scales, const int32_t* page_table,
+                            const int32_t* seq_lens, void* out, float* lse_out, void* workspace,
+                            size_t workspace_bytes, void* stream, void* const* stage_events);
+
+/*
  * The decode with the output projection merged into the up-projection (lpnh.cn/news/2494972
  * S2.2: W_uv and W_o are merged into one matrix offline): instead of out[b,h,:] = o_lat W_UV[h]
  * it returns

@@ -66,6 +66,8 @@ def lib():
         L.mla_decode.argtypes = [dp] + [vp] * 10 + [sz, vp]
         L.mla_decode_timed.restype = c_int
         L.mla_decode_timed.argtypes = [dp] + [vp] * 10 + [sz, vp, ctypes.POINTER(vp)]
+        L.mla_decode_fp8.restype = c_int
+        L.mla_decode_fp8.argtypes = [dp] + [vp] * 11 + [sz, vp, ctypes.POINTER(vp)]
         L.mla_decode_out.restype = c_int
         L.mla_decode_out.argtypes = [dp, ctypes.c_int32] + [vp] * 10 + [sz, vp]
         L.mla_cache_append.restype = c_int
@@ -148,7 +150,7 @@ def _want(t, name, dtype, ndim, device):
 
 def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None, lse=None,
            max_seq_len=None, softmax_scale=None, num_units=0, workspace=None, stream=None,
-           return_lse=False, kernel_events=None):
+           return_lse=False, kernel_events=None, kv_scales=None):
     """Absorbed MLA decode through mla_decode(). Tensors live on one HIP device.
 
     q_nope bf16 [B,H,d_n], q_rope bf16 [B,H,d_R], W_UK bf16 [H,d_n,d_c], W_UV bf16 [H,d_c,d_v],
@@ -160,6 +162,9 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
     kernel_events: optional six raw hipEvent_t handles (int or None), passed to
     mla_decode_timed, which binds them to the start and end of the absorb, attention and
     combine kernels.
+    kv_scales: an FP8 cache (mla_decode_fp8): kv_pages is then uint8 [P,64,d_c+2*d_R], token
+    = [c_KV as FP8 e4m3 bytes | k_R bf16], and kv_scales fp32 [P,64] holds each token's c_KV
+    scale.
     """
     dev = q_nope.device
     if dev.type != "cuda":
@@ -170,7 +175,8 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
         raise ValueError("q_nope must be [B,H,d_n] or [B,T,H,d_n]")
     for t, n, dt, nd in ((q_nope, "q_nope", bf, nq), (q_rope, "q_rope", bf, nq),
                          (W_UK, "W_UK", bf, 3), (W_UV, "W_UV", bf, 3),
-                         (kv_pages, "kv_pages", bf, 3), (page_table, "page_table", i32, 2),
+                         (kv_pages, "kv_pages", bf if kv_scales is None else torch.uint8, 3),
+                         (page_table, "page_table", i32, 2),
                          (seq_lens, "seq_lens", i32, 1)):
         _want(t, n, dt, nd, dev)
     dims = make_dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, max_seq_len,
@@ -188,6 +194,13 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
         lse = torch.empty(lead + (H,), dtype=torch.float32, device=dev)
     if lse is not None:
         _want(lse, "lse", torch.float32, nq - 1, dev)
+    if kv_scales is not None:
+        _want(kv_scales, "kv_scales", torch.float32, 2, dev)
+        if tuple(kv_scales.shape) != tuple(kv_pages.shape[:2]):
+            raise ValueError("kv_scales %s must be [pages, 64] like kv_pages %s"
+                             % (tuple(kv_scales.shape), tuple(kv_pages.shape)))
+        if kv_pages.shape[2] != dims.d_latent + 2 * dims.d_rope:
+            raise ValueError("an FP8 token row is d_c + 2*d_R bytes")
     nbytes = workspace_bytes(dims)
     if nbytes == 0:
         _check(lib().mla_decode(ctypes.byref(dims), *([ctypes.c_void_p(0)] * 10), 0,
@@ -197,12 +210,16 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
     args = (ctypes.byref(dims), _ptr(q_nope), _ptr(q_rope), _ptr(W_UK), _ptr(W_UV),
             _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
             _ptr(workspace), workspace.numel(), _stream(stream, dev))
-    if kernel_events is None:
-        code = lib().mla_decode(*args)
-    else:
+    ev = None
+    if kernel_events is not None:
         if len(kernel_events) != 6:
             raise ValueError("kernel_events needs six entries (start, end of three kernels)")
         ev = (ctypes.c_void_p * 6)(*[e or None for e in kernel_events])
+    if kv_scales is not None:
+        code = lib().mla_decode_fp8(*args[:6], _ptr(kv_scales), *args[6:], ev)
+    elif ev is None:
+        code = lib().mla_decode(*args)
+    else:
         code = lib().mla_decode_timed(*args, ev)
     _check(code)
     return (out, lse) if return_lse else out
@@ -223,7 +240,8 @@ def decode_out(q_nope, q_rope, W_UK, W_UVO, kv_pages, page_table, seq_lens, out=
         raise ValueError("q_nope must be [B,H,d_n] or [B,T,H,d_n]")
     for t, n, dt, nd in ((q_nope, "q_nope", bf, nq), (q_rope, "q_rope", bf, nq),
                          (W_UK, "W_UK", bf, 3), (W_UVO, "W_UVO", bf, 2),
-                         (kv_pages, "kv_pages", bf, 3), (page_table, "page_table", i32, 2),
+                         (kv_pages, "kv_pages", bf if kv_scales is None else torch.uint8, 3),
+                         (page_table, "page_table", i32, 2),
                          (seq_lens, "seq_lens", i32, 1)):
         _want(t, n, dt, nd, dev)
     H, d_c = W_UK.shape[0], W_UK.shape[2]
@@ -243,6 +261,13 @@ def decode_out(q_nope, q_rope, W_UK, W_UVO, kv_pages, page_table, seq_lens, out=
         lse = torch.empty(lead + (H,), dtype=torch.float32, device=dev)
     if lse is not None:
         _want(lse, "lse", torch.float32, nq - 1, dev)
+    if kv_scales is not None:
+        _want(kv_scales, "kv_scales", torch.float32, 2, dev)
+        if tuple(kv_scales.shape) != tuple(kv_pages.shape[:2]):
+            raise ValueError("kv_scales %s must be [pages, 64] like kv_pages %s"
+                             % (tuple(kv_scales.shape), tuple(kv_pages.shape)))
+        if kv_pages.shape[2] != dims.d_latent + 2 * dims.d_rope:
+            raise ValueError("an FP8 token row is d_c + 2*d_R bytes")
     nbytes = workspace_bytes(dims)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)

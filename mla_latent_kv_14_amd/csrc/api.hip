@@ -119,14 +119,18 @@ namespace {
 // merged W_UVO [hidden][H * d_latent] and out is [rows][hidden] (the combine writes the merged
 // latent rows into the query region of the workspace, dead by then, and a product with W_UVO
 // follows).
+// kv_scales: NULL for the bf16 cache; the per-token scales of an FP8 cache otherwise.
 mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
                          const void* q_rope, const void* W_UK, const void* W_UV,
-                         const void* kv_pages, const int32_t* page_table,
-                         const int32_t* seq_lens, void* out, float* lse_out, void* workspace,
-                         size_t workspace_bytes, void* stream, void* const* stage_events) {
+                         const void* kv_pages, const float* kv_scales,
+                         const int32_t* page_table, const int32_t* seq_lens, void* out,
+                         float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* stage_events) {
   ShapeInfo s;
   mla_status_t st = check_dims(dims, &s);
   if (st != MLA_OK) return st;
+  if (kv_scales && s.shape != mla::kShapeMha2Mla) return MLA_ERR_UNSUPPORTED;
+  if (kv_scales && !aligned16(kv_scales)) return MLA_ERR_MISALIGNED;
   if (hidden < 0 || hidden > (1 << 20)) return MLA_ERR_BAD_DIMS;
   if (hidden > 0 && (hidden % 16 != 0 || (s.H * s.DC) % 1024 != 0)) return MLA_ERR_UNSUPPORTED;
   if (!q_nope || !q_rope || !W_UK || !W_UV || !kv_pages || !page_table || !seq_lens || !out)
@@ -174,7 +178,7 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
   st = hip_status(mla::launch_attention(s.shape, ws + L.q_abs, q_rope, kv_pages, page_table,
                                         seq_lens, R, mp, T, dims->num_pages, ws + L.plan, G,
                                         scale_log2, ws + L.part_o, (float*)(ws + L.part_lse),
-                                        ctx(1)));
+                                        kv_scales, ctx(1)));
   if (st != MLA_OK) return st;
   if (hidden == 0)
     return hip_status(mla::launch_combine(s.shape, ws + L.part_o,
@@ -197,8 +201,18 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
                               const int32_t* page_table, const int32_t* seq_lens, void* out,
                               float* lse_out, void* workspace, size_t workspace_bytes,
                               void* stream, void* const* stage_events) {
-  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out,
-                     lse_out, workspace, workspace_bytes, stream, stage_events);
+  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, nullptr, page_table,
+                     seq_lens, out, lse_out, workspace, workspace_bytes, stream, stage_events);
+}
+
+mla_status_t mla_decode_fp8(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                            const void* W_UK, const void* W_UV, const void* kv_pages,
+                            const float* kv_scales, const int32_t* page_table,
+                            const int32_t* seq_lens, void* out, float* lse_out, void* workspace,
+                            size_t workspace_bytes, void* stream, void* const* stage_events) {
+  if (!kv_scales) return MLA_ERR_NULL_ARG;
+  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, kv_scales, page_table,
+                     seq_lens, out, lse_out, workspace, workspace_bytes, stream, stage_events);
 }
 
 mla_status_t mla_decode_out(const mla_dims_t* dims, int32_t hidden, const void* q_nope,
@@ -207,8 +221,8 @@ mla_status_t mla_decode_out(const mla_dims_t* dims, int32_t hidden, const void* 
                             const int32_t* seq_lens, void* out_hidden, float* lse_out,
                             void* workspace, size_t workspace_bytes, void* stream) {
   if (hidden < 1) return MLA_ERR_BAD_DIMS;
-  return decode_call(dims, hidden, q_nope, q_rope, W_UK, W_UVO, kv_pages, page_table, seq_lens,
-                     out_hidden, lse_out, workspace, workspace_bytes, stream, nullptr);
+  return decode_call(dims, hidden, q_nope, q_rope, W_UK, W_UVO, kv_pages, nullptr, page_table,
+                     seq_lens, out_hidden, lse_out, workspace, workspace_bytes, stream, nullptr);
 }
 
 mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* q_rope,

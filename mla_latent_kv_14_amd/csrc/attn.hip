@@ -17,6 +17,8 @@
 // so the weights that multiply the values are exactly normalised; at the MHA2MLA widths l sums
 // the fp32 weights (one instruction less per weight; the two sums differ by bf16 rounding noise
 // that averages out over the tokens).
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 #include "paged_tile.h"
@@ -506,17 +508,43 @@ constexpr int TT = kPage;  // tokens per tile: one page
 using Tile = PagedTile<TT, ROWB>;
 constexpr int IPW = Tile::INSTR;  // the wave issues the whole tile
 constexpr float kRescale = 64.f;  // log2 headroom before the running max must move
+// FP8 cache: a token row is [c_KV as FP8 e4m3 (64 bytes) | k_R bf16 (16 bytes)], 80 bytes,
+// and each token has an fp32 scale in a separate array of the same page geometry. A loaded
+// tile is its 5 KiB of rows followed by its 64 scales (256 bytes); a five-deep ring holds four
+// in flight. When its turn comes, a tile is dequantised into one bf16 tile of the layout above
+// (lane l: token row l, c_KV * scale rounded to bf16, k_R copied), which the compute then reads.
+constexpr int ROWB8 = DC + 2 * DR;
+using Tile8 = PagedTile<TT, ROWB8>;
+constexpr int NS = 5;
+constexpr int SB8 = Tile8::BYTES + 4 * TT;  // bytes of one loaded FP8 tile with its scales
 }  // namespace m2
 
+// Waits until at most `after` (0..4) tiles of N load instructions each are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_tiles_upto4(int after) {
+  if (after >= 4) wait_vmcnt<4 * N>();
+  else if (after == 3) wait_vmcnt<3 * N>();
+  else if (after == 2) wait_vmcnt<2 * N>();
+  else if (after == 1) wait_vmcnt<N>();
+  else wait_vmcnt<0>();
+}
+
+template <bool FP8>
 __global__ void __launch_bounds__(256)
 attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
                     const char* __restrict__ kv, const int32_t* __restrict__ page_table,
                     const int32_t* __restrict__ seq_lens, int B, int max_pages, int q_len,
                     int num_pages,
                     const Plan* __restrict__ plan, int G, float scale_log2,
-                    uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
+                    uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
+                    const float* __restrict__ kv_scales) {
   using namespace m2;
-  __shared__ __attribute__((aligned(1024))) char lds_tiles[kAttnWavesMha2Mla][NBUF * Tile::BYTES];
+  using TileL = typename std::conditional<FP8, Tile8, Tile>::type;  // the format as loaded
+  constexpr int NB = FP8 ? NS : NBUF;                     // ring of loaded tiles
+  constexpr int LB = FP8 ? SB8 : Tile::BYTES;             // bytes of one ring entry
+  constexpr int IPW = TileL::INSTR + (FP8 ? 1 : 0);       // load instructions per tile
+  constexpr int WAVE_LDS = FP8 ? NS * SB8 + Tile::BYTES : NBUF * Tile::BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds_tiles[kAttnWavesMha2Mla][WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -525,12 +553,13 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   const int n = g < G ? us.n : 0;  // tiles of this unit
   if (n <= 0) return;
   MLA_LDS char* tiles = (MLA_LDS char*)lds_tiles[wave];
+  MLA_LDS char* conv = tiles + NS * SB8;  // FP8: the dequantised bf16 tile
 
   Cursor lc = {us.b, us.j, us.nj, us.S};
   Cursor cc = lc;
   uint32_t dmo[IPW];  // lane offsets of a full-tile load
 #pragma unroll
-  for (int k = 0; k < IPW; ++k) dmo[k] = Tile::src_off(k, lane, TT);
+  for (int k = 0; k < TileL::INSTR; ++k) dmo[k] = TileL::src_off(k, lane, TT);
   // The wave keeps 64 page-table entries of the current sequence in one VGPR (lane l: entry
   // pw_base + l) and picks them with readlane, so issuing a tile needs no scalar load (whose
   // wait would stall the wave before every tile). A refill is one asm statement, load and wait,
@@ -546,9 +575,38 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)"
                    : "=v"(pw_v) : "v"(src) : "memory");
     }
-    const char* base =
-        Tile::base_of(kv, __builtin_amdgcn_readlane(pw_v, p - pw_base), c.j, num_pages);
-    Tile::issue<1>(base, min(TT, c.S - c.j * TT), dmo, tiles + buf * Tile::BYTES, 0, lane);
+    int page = __builtin_amdgcn_readlane(pw_v, p - pw_base);
+    page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+    const int valid = min(TT, c.S - c.j * TT);
+    MLA_LDS char* dst = tiles + buf * LB;
+    TileL::template issue<1>(TileL::base_of(kv, page, c.j, num_pages), valid, dmo, dst, 0, lane);
+    if constexpr (FP8)  // the tile's scales (slots past the end repeat the last valid one)
+      load_lds_4(kv_scales + (size_t)page * kPage + (c.j % Tile8::TPP) * TT,
+                 4u * (uint32_t)min(lane, valid - 1), dst + Tile8::BYTES);
+  };
+  // FP8: lane l dequantises token row l of a loaded tile into the bf16 tile
+  auto convert = [&](const MLA_LDS char* src) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const MLA_LDS char* row = src + lane * ROWB8;
+    const float sc = *reinterpret_cast<const MLA_LDS float*>(src + Tile8::BYTES + 4 * lane);
+#pragma unroll
+    for (int q = 0; q < DC / 16; ++q) {  // 16 FP8 values -> two chunks of 8 bf16
+      const u32x4 w = *reinterpret_cast<const MLA_LDS u32x4*>(row + 16 * q);
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);  // values 4i, 4i+1
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);   // values 4i+2, 4i+3
+        o[2 * i] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+        o[2 * i + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+      }
+      *reinterpret_cast<MLA_LDS u32x4*>(conv + Tile::lds_off(lane, 2 * q)) =
+          u32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<MLA_LDS u32x4*>(conv + Tile::lds_off(lane, 2 * q + 1)) =
+          u32x4{o[4], o[5], o[6], o[7]};
+    }
+    *reinterpret_cast<MLA_LDS u32x4*>(conv + Tile::lds_off(lane, DC / 8)) =
+        *reinterpret_cast<const MLA_LDS u32x4*>(row + DC);
   };
 
   const int t32 = lane & 31, hi = lane >> 5;
@@ -574,8 +632,8 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   bool seg_start = false;
 
   int issued = 0;
-  for (; issued < NBUF - 1 && issued < n; ++issued) {
-    issue(lc, issued % NBUF);
+  for (; issued < NB - 1 && issued < n; ++issued) {
+    issue(lc, issued % NB);
     cursor_next(lc, plan, seq_lens, B, max_pages, q_len);
   }
   for (int it = 0; it < n; ++it) {
@@ -583,16 +641,19 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       start_segment(cc.b);
       seg_start = false;
     }
-    const int after = issued - it - 1;
-    if (after >= 2) wait_vmcnt<2 * IPW>();
-    else if (after == 1) wait_vmcnt<IPW>();
-    else wait_vmcnt<0>();
-    if (issued < n) {
-      issue(lc, issued % NBUF);
+    wait_tiles_upto4<IPW>(issued - it - 1);  // tile it landed
+    if (issued < n) {  // into the buffer of tile it-1, done with in the last pass
+      issue(lc, issued % NB);
       cursor_next(lc, plan, seq_lens, B, max_pages, q_len);
       ++issued;
     }
-    const MLA_LDS char* kb = tiles + (it % NBUF) * Tile::BYTES;
+    const MLA_LDS char* kb;
+    if constexpr (FP8) {
+      convert(tiles + (it % NB) * LB);  // the last pass's reads of conv came first
+      kb = conv;
+    } else {
+      kb = tiles + (it % NB) * Tile::BYTES;
+    }
 
     // ---- scores for tokens [32*mb2, 32*mb2 + 32)
     f32x16 s[2];
@@ -702,8 +763,10 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
 hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, const void* kv,
                             const int32_t* page_table, const int32_t* seq_lens, int B,
                             int max_pages, int q_len, int num_pages, const void* plan, int G,
-                            float scale_log2, void* part_o, float* part_lse, const Launch& L) {
+                            float scale_log2, void* part_o, float* part_lse,
+                            const float* kv_scales, const Launch& L) {
   if (shape == kShapeDeepSeek) {
+    if (kv_scales) return hipErrorInvalidValue;  // the FP8 cache is built for MHA2MLA only
     // two head halves per tile stream, paired 8 ids apart; ids padded to whole groups of 16
     const int blocks = 16 * ((G + 7) / 8);
     return launch_kernel(attn_deepseek_kernel, dim3(blocks), dim3(64 * ds::NW), L,
@@ -712,10 +775,16 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
                          scale_log2, (uint16_t*)part_o, part_lse);
   }
   const int blocks = (G + kAttnWavesMha2Mla - 1) / kAttnWavesMha2Mla;
-  return launch_kernel(attn_mha2mla_kernel, dim3(blocks), dim3(64 * kAttnWavesMha2Mla), L,
+  if (kv_scales)
+    return launch_kernel(attn_mha2mla_kernel<true>, dim3(blocks), dim3(64 * kAttnWavesMha2Mla), L,
+                         (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv,
+                         page_table, seq_lens, B, max_pages, q_len, num_pages,
+                         (const Plan*)plan, G, scale_log2, (uint16_t*)part_o, part_lse,
+                         kv_scales);
+  return launch_kernel(attn_mha2mla_kernel<false>, dim3(blocks), dim3(64 * kAttnWavesMha2Mla), L,
                        (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv,
                        page_table, seq_lens, B, max_pages, q_len, num_pages, (const Plan*)plan, G,
-                       scale_log2, (uint16_t*)part_o, part_lse);
+                       scale_log2, (uint16_t*)part_o, part_lse, (const float*)nullptr);
 }
 
 }  // namespace mla

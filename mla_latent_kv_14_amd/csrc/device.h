@@ -62,6 +62,12 @@ __device__ __forceinline__ void load_lds_16(const void* base, uint32_t off, MLA_
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 
+// The same with 4 bytes per lane: LDS bytes [lds + 4*lane, +4) <- base + off.
+__device__ __forceinline__ void load_lds_4(const void* base, uint32_t off, MLA_LDS void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+
 // Work-group barrier for LDS traffic only: waits for this wave's LDS operations, not for its
 // outstanding global loads (the prefetched tiles stay in flight across the barrier).
 __device__ __forceinline__ void block_sync() {

@@ -43,7 +43,8 @@ hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* 
 hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, const void* kv,
                             const int32_t* page_table, const int32_t* seq_lens, int B,
                             int max_pages, int q_len, int num_pages, const void* plan, int G,
-                            float scale_log2, void* part_o, float* part_lse, const Launch& L);
+                            float scale_log2, void* part_o, float* part_lse,
+                            const float* kv_scales, const Launch& L);
 
 hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, const void* plan,
                           const int32_t* seq_lens, const void* W_UV, void* out, float* lse_out,

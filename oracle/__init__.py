@@ -226,6 +226,42 @@ def cache_append(x, W_DKV, W_KR, page_table, seq_lens, base=10000.0):
     return rows, where
 
 
+def fp8_e4m3_value(code):
+    """Exact value of FP8 E4M3 bytes (the OCP 8-bit float format with 4 exponent bits, bias 7,
+    and 3 mantissa bits; no infinities, S.1111.111 is NaN), as fp64. This is the element format
+    of the quantised latent cache (the pages' quantised gather of the latent cache,
+    bhfrc.com/news/60867 S1 and S5, read as an 8-bit float cache with per-token scales)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    subnormal = (m / 8.0) * 2.0 ** -6
+    v = sign * np.where(e == 0, subnormal, normal)
+    return np.where((e == 15) & (c & 0x7 == 7), np.nan, v)
+
+
+def dequant_fp8_cache(kv8, scales, d_c):
+    """The bf16 cache that an FP8 cache stands for: token row [c_KV bytes (d_c) | k_R bf16
+    (2*d_R bytes)] with an fp32 scale per token slot; c_KV[c] = value(byte c) * scale, k_R
+    copied. Returns uint16 bf16 bits [P, 64, d_c + d_R]. The products must be bf16 values
+    (power-of-two scales make them so); anything else raises, since the result would not be
+    the same cache."""
+    kv8 = np.ascontiguousarray(kv8, dtype=np.uint8)
+    P, ps, w8 = kv8.shape
+    d_R = (w8 - d_c) // 2
+    v = fp8_e4m3_value(kv8[:, :, :d_c]) * np.asarray(scales, dtype=np.float64)[:, :, None]
+    f = v.astype(np.float32)
+    ok = np.isnan(v) | (f.astype(np.float64) == v)
+    bits = f.view(np.uint32)
+    if not np.all(ok) or np.any((bits[~np.isnan(v)] & 0xFFFF) != 0):
+        raise ValueError("dequantised c_KV is not exactly a bf16 value")
+    out = np.empty((P, ps, d_c + d_R), dtype=np.uint16)
+    out[:, :, :d_c] = np.where(np.isnan(v), 0x7FC0, bits >> 16).astype(np.uint16)
+    out[:, :, d_c:] = kv8[:, :, d_c:].copy().view(np.uint16).reshape(P, ps, d_R)
+    return out
+
+
 def _f64(u16):
     """Exact fp64 value of bf16 bit patterns."""
     return (np.asarray(u16, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -8,7 +8,8 @@ import pytest
 import mla_latent_kv_14_amd as M
 from mla_latent_kv_14_amd.binding import STATUS_CODE
 
-EXPECTED = ["mla_cache_append", "mla_decode", "mla_decode_out", "mla_decode_timed",
+EXPECTED = ["mla_cache_append", "mla_decode", "mla_decode_fp8", "mla_decode_out",
+            "mla_decode_timed",
             "mla_decode_workspace_bytes", "mla_gather_pages", "mla_last_hip_error",
             "mla_status_str"]
 
@@ -197,3 +198,20 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         M.decode(x, x, x, x, x, torch.zeros(1, 1, dtype=torch.int32),
                  torch.ones(1, dtype=torch.int32))
+
+
+def test_decode_fp8_rejects_before_enqueueing():
+    L = M.lib()
+    ptrs = [_al(k + 1) for k in range(5)]           # q_nope, q_rope, W_UK, W_UV, kv_pages
+    rest = [_al(7), _al(8), _al(9), ctypes.c_void_p(0)]  # page_table, seq_lens, out, lse
+    def call(d, scales):
+        return L.mla_decode_fp8(ctypes.byref(d), *ptrs, scales, *rest, _al(10),
+                                M.workspace_bytes(d), ctypes.c_void_p(0), None)
+    assert call(m2_dims(), ctypes.c_void_p(0)) == STATUS_CODE["MLA_ERR_NULL_ARG"]
+    # the FP8 cache is built for the MHA2MLA widths only
+    assert call(ds_dims(), _al(6)) == STATUS_CODE["MLA_ERR_UNSUPPORTED"]
+    assert call(m2_dims(), ctypes.c_void_p(_al(6).value + 4)) == \
+        STATUS_CODE["MLA_ERR_MISALIGNED"]
+    bad = m2_dims()
+    bad.batch = 0
+    assert call(bad, _al(6)) == STATUS_CODE["MLA_ERR_BAD_DIMS"]

@@ -1,0 +1,119 @@
+"""GPU parity of the FP8 latent cache (MHA2MLA widths): the decode over an FP8 e4m3 cache with
+per-token power-of-two scales, through mla_decode_fp8, against the fp64 oracle run on the bf16
+cache that the FP8 one stands for (oracle.dequant_fp8_cache; with power-of-two scales every
+dequantised value is a bf16 value, so both sides see the same numbers and the bf16 bounds
+apply unchanged)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_helpers import LSE_ABS, MAX_ABS, REL_L2, errors, need_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+M2 = dict(H=32, d_n=120, d_c=64, d_R=8, d_v=128)
+
+
+@pytest.fixture(scope="module")
+def M():
+    return need_gpu()
+
+
+def _inp(lens, seed, **kw):
+    return W.make_inputs(len(lens), M2["H"], M2["d_n"], M2["d_c"], M2["d_R"], M2["d_v"], lens,
+                         seed, **kw)
+
+
+def check_fp8(M, inp, units=0, pairs=None, poison=False, label="", seed=5):
+    kv8, sc = W.fp8_cache(inp, seed=seed, poison=poison)
+    say(label, "fp8 B=%d units=%d T=%d" % (inp["B"], units,
+                                            inp["q_nope"].shape[1] if inp["q_nope"].dim() == 4
+                                            else 1))
+    d = to_dev(inp)
+    out, lse = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8.cuda(),
+                        d["page_table"], d["seq_lens"], num_units=units, return_lse=True,
+                        kv_scales=sc.cuda())
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    args = list(W.oracle_args(inp))
+    args[4] = oracle.dequant_fp8_cache(kv8.numpy(), sc.numpy(), inp["d_c"])
+    if inp["q_nope"].dim() == 4:
+        ref, ref_lse = oracle.decode_tokens(*args)
+    else:
+        ref, ref_lse = oracle.decode(*args, pairs=pairs)
+    if pairs is not None:
+        idx = np.asarray(pairs)
+        out, lse = out[idx[:, 0], idx[:, 1]], lse[idx[:, 0], idx[:, 1]]
+    rel, mx = errors(out, ref)
+    lerr = float(np.max(np.abs(lse - ref_lse)))
+    say(label, "rel_l2=%.3e max_abs=%.3e lse_err=%.3e" % (rel, mx, lerr))
+    assert np.all(np.isfinite(out))
+    assert rel <= REL_L2 and mx <= MAX_ABS and lerr <= LSE_ABS, (label, rel, mx, lerr)
+    return out
+
+
+@pytest.mark.parametrize("units", [0, 1, 2, 3, 7, 40])
+def test_fp8_ragged(M, units):
+    inp = _inp([1, 63, 64, 65, 1000, 130], 12, poison=True)
+    check_fp8(M, inp, units=units, poison=True, label="fp8 ragged")
+
+
+@pytest.mark.parametrize("units", [1, 2])
+def test_fp8_long_sequences_few_units(M, units):
+    # a unit walks more than 64 pages of one sequence and crosses into the next
+    check_fp8(M, _inp([64 * 150 + 7, 64 * 70], 17), units=units, label="fp8 long")
+
+
+def test_fp8_many_short_sequences(M):
+    lens = [1 + (11 * i) % 200 for i in range(200)]
+    check_fp8(M, _inp(lens, 14), label="fp8 200 short")
+
+
+def test_fp8_wide_scale_range(M):
+    # scales from 2^-6 to 2^-2: small |c_KV| lands on FP8 subnormals and zero
+    inp = _inp([500, 77, 2048], 21)
+    check_fp8(M, inp, label="fp8 scale range")
+
+
+@pytest.mark.parametrize("T", [2, 4])
+def test_fp8_query_tokens(M, T):
+    inp = _inp([70, T, 200, 64 * 3 + 1], 31)
+    g = torch.Generator().manual_seed(32)
+    B = inp["B"]
+    inp["q_nope"] = torch.randn(B, T, 32, 120, generator=g).to(torch.bfloat16)
+    inp["q_rope"] = torch.randn(B, T, 32, 8, generator=g).to(torch.bfloat16)
+    check_fp8(M, inp, label="fp8 %d query tokens" % T)
+
+
+def test_fp8_equals_bf16_on_the_same_values(M):
+    # with the bf16 cache holding exactly the dequantised values, the two paths compute the
+    # same numbers from the same bf16 operands: results agree to fp32 summation-order noise
+    inp = _inp([300, 64, 1000], 41)
+    kv8, sc = W.fp8_cache(inp, seed=2)
+    deq = oracle.dequant_fp8_cache(kv8.numpy(), sc.numpy(), inp["d_c"])
+    inp["kv_pages"] = torch.from_numpy(deq.view(np.int16)).view(torch.bfloat16)
+    d = to_dev(inp)
+    a = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8.cuda(), d["page_table"],
+                 d["seq_lens"], kv_scales=sc.cuda())
+    b = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], d["kv_pages"],
+                 d["page_table"], d["seq_lens"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_fp8_workload_full_size(M):
+    # the MHA2MLA workload (B=32, S=32768) over an FP8 copy of its cache, every (b, h)
+    inp = W.config_inputs(5)
+    check_fp8(M, inp, label="fp8 workload 5")
+
+
+def test_fp8_rejected_for_deepseek_widths(M):
+    inp = W.make_inputs(1, 128, 128, 512, 64, 128, [64], 3)
+    kv8, sc = W.fp8_cache(inp)
+    d = to_dev(inp)
+    with pytest.raises(M.MlaError) as e:
+        M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8.cuda(), d["page_table"],
+                 d["seq_lens"], kv_scales=sc.cuda())
+    assert e.value.code == 5  # MLA_ERR_UNSUPPORTED

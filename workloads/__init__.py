@@ -127,3 +127,35 @@ def oracle_args(inp):
     """The eight inputs as the numpy arrays the oracle takes."""
     return (u16(inp["q_nope"]), u16(inp["q_rope"]), u16(inp["W_UK"]), u16(inp["W_UV"]),
             u16(inp["kv_pages"]), inp["page_table"].numpy(), inp["seq_lens"].numpy())
+
+
+FP8_NAN = 0x7F  # an e4m3 NaN byte
+
+
+def fp8_cache(inp, seed=0, exps=(-6, -2), poison=False):
+    """An FP8 copy of the cache of ``inp``: each token's c_KV is divided by a power of two
+    2^k, k drawn uniformly from [exps[0], exps[1]] per token slot (seeded), and cast to FP8
+    e4m3 by torch (RNE); k_R stays bf16. Returns (kv8 uint8 [P, 64, d_c + 2*d_R] with rows
+    [c_KV bytes | k_R bf16 bytes], scales fp32 [P, 64] = 2^k). With poison=True every slot that
+    is not part of a sequence holds NaN bytes and a NaN scale."""
+    kv = inp["kv_pages"]
+    P, ps, w = kv.shape
+    d_c = inp["d_c"]
+    g = torch.Generator().manual_seed(int(seed))
+    k = torch.randint(int(exps[0]), int(exps[1]) + 1, (P, ps), generator=g)
+    scales = torch.pow(2.0, k.to(torch.float64)).to(torch.float32)
+    c = kv[:, :, :d_c].float() / scales[:, :, None]
+    codes = c.to(torch.float8_e4m3fn).view(torch.uint8)
+    kr = kv[:, :, d_c:].contiguous().view(torch.uint8).reshape(P, ps, 2 * (w - d_c))
+    kv8 = torch.cat([codes, kr], dim=2).contiguous()
+    if bool((((codes & 0x7F) == 0x7F) & ~torch.isnan(c)).any()):  # NaN past 464
+        raise ValueError("c_KV out of the FP8 range for these scales")
+    if poison:
+        used = torch.zeros(P, ps, dtype=torch.bool)
+        for b in range(inp["B"]):
+            S = int(inp["seq_lens"][b])
+            for t in range(S):
+                used[int(inp["page_table"][b, t // ps]), t % ps] = True
+        kv8[~used] = FP8_NAN
+        scales[~used] = float("nan")
+    return kv8, scales
