@@ -79,7 +79,8 @@ typedef struct {
                                   tiles of all sequences are dealt to this many units in
                                   order. 0 = automatic (fills the 256 compute units: 128 for
                                   the DeepSeek widths, one unit = two work groups; 1024 for
-                                  MHA2MLA, one unit = one wave). At most 65536.            */
+                                  MHA2MLA, one unit = one wave; 2048 for MHA2MLA with the
+                                  FP8 cache, two work groups to a CU). At most 65536.      */
     int32_t q_len;             /* T: query tokens per sequence, 0 or 1 = one (plain decode),
                                   at most 256, B*T at most 2^20. With T > 1 the T query
                                   tokens of sequence b are its T newest tokens, whose
@@ -91,8 +92,9 @@ typedef struct {
                                   lse = -inf.                                              */
 } mla_dims_t;
 
-/* Bytes of scratch a call with these dims needs (pure function of the dims, host only).
- * Returns 0 when the dims are invalid or unsupported. */
+/* Bytes of scratch a call with these dims needs (pure function of the dims, host only), for
+ * either cache format (mla_decode and mla_decode_fp8). Returns 0 when the dims are invalid or
+ * unsupported. */
 size_t mla_decode_workspace_bytes(const mla_dims_t* dims);
 
 /*
@@ -140,10 +142,13 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
  *              FP8 E4M3 bytes (OCP format: 4 exponent bits, bias 7, 3 mantissa bits, no
  *              infinities, S.1111.111 = NaN) | k_R as d_rope bf16 values]
  *   kv_scales  fp32 [num_pages, 64]                      the scale of the token in each slot:
- *              c_KV[c] = value(byte c) * kv_scales[page][slot]
- * The kernel forms each c_KV element as the fp32 product rounded to bf16 (RNE) and then runs
- * the bf16 decode, so with power-of-two scales the result is that of mla_decode on the bf16
- * cache holding the products exactly. Slots at or past S_b (bytes and scales) are never read
+ *              c_KV[c] = value(byte c) * kv_scales[page][slot]. Scales are positive normal
+ *              powers of two (exponent-only, as in the microscaling formats); any other
+ *              positive normal value acts as the power of two of its binary exponent,
+ *              2^floor(log2 s), its mantissa bits ignored.
+ * Each dequantised c_KV element (an E4M3 value times a power of two) is a bf16 value, formed
+ * exactly, and the decode then runs as in mla_decode: the result is that of mla_decode on the
+ * bf16 cache holding those values. Slots at or past S_b (bytes and scales) are never read
  * into the result. kv_scales must be 16-byte aligned and non-NULL; everything else, including
  * q_len, the workspace size and stage_events (NULL or six events, as for mla_decode_timed),
  * is as for mla_decode_timed.

@@ -240,8 +240,7 @@ def decode_out(q_nope, q_rope, W_UK, W_UVO, kv_pages, page_table, seq_lens, out=
         raise ValueError("q_nope must be [B,H,d_n] or [B,T,H,d_n]")
     for t, n, dt, nd in ((q_nope, "q_nope", bf, nq), (q_rope, "q_rope", bf, nq),
                          (W_UK, "W_UK", bf, 3), (W_UVO, "W_UVO", bf, 2),
-                         (kv_pages, "kv_pages", bf if kv_scales is None else torch.uint8, 3),
-                         (page_table, "page_table", i32, 2),
+                         (kv_pages, "kv_pages", bf, 3), (page_table, "page_table", i32, 2),
                          (seq_lens, "seq_lens", i32, 1)):
         _want(t, n, dt, nd, dev)
     H, d_c = W_UK.shape[0], W_UK.shape[2]
@@ -261,13 +260,6 @@ def decode_out(q_nope, q_rope, W_UK, W_UVO, kv_pages, page_table, seq_lens, out=
         lse = torch.empty(lead + (H,), dtype=torch.float32, device=dev)
     if lse is not None:
         _want(lse, "lse", torch.float32, nq - 1, dev)
-    if kv_scales is not None:
-        _want(kv_scales, "kv_scales", torch.float32, 2, dev)
-        if tuple(kv_scales.shape) != tuple(kv_pages.shape[:2]):
-            raise ValueError("kv_scales %s must be [pages, 64] like kv_pages %s"
-                             % (tuple(kv_scales.shape), tuple(kv_pages.shape)))
-        if kv_pages.shape[2] != dims.d_latent + 2 * dims.d_rope:
-            raise ValueError("an FP8 token row is d_c + 2*d_R bytes")
     nbytes = workspace_bytes(dims)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)

@@ -60,12 +60,16 @@ int max_len(const mla_dims_t* d) {
 }
 
 // Plan units sharing the cache stream: tile streams served by two work groups (DeepSeek
-// widths) or single waves (MHA2MLA). The automatic count fills 256 compute units; it is capped
-// by the tiles that can exist so that no unit is sure to be idle.
-int plan_units(const mla_dims_t* d, const ShapeInfo& s) {
+// widths) or single waves (MHA2MLA). The automatic count fills 256 compute units (with the FP8
+// cache two work groups fit on one); it is capped by the tiles that can exist so that no unit
+// is sure to be idle.
+int plan_units(const mla_dims_t* d, const ShapeInfo& s, bool fp8) {
   const int64_t upper = (int64_t)rows(d) * ((max_len(d) + s.TT - 1) / s.TT);
   int64_t g = d->num_units;
-  if (g == 0) g = s.shape == mla::kShapeDeepSeek ? 128 : 256 * mla::kAttnWavesMha2Mla;
+  if (g == 0)
+    g = s.shape == mla::kShapeDeepSeek
+            ? 128
+            : 256 * mla::kAttnWavesMha2Mla * (fp8 ? mla::kGroupsPerCuFp8 : 1);
   if (g > upper) g = upper;
   return g < 1 ? 1 : (int)g;
 }
@@ -82,11 +86,11 @@ struct Layout {
   size_t plan, q_abs, part_lse, part_o, total;
 };
 
-Layout layout(const mla_dims_t* d, const ShapeInfo& s) {
-  const size_t B = (size_t)rows(d), slots = (size_t)plan_units(d, s) + B;
+Layout layout(const mla_dims_t* d, const ShapeInfo& s, bool fp8) {
+  const size_t B = (size_t)rows(d), slots = (size_t)plan_units(d, s, fp8) + B;
   Layout L;
   L.plan = 0;
-  L.q_abs = align256(mla::plan_bytes((int)B, plan_units(d, s)));
+  L.q_abs = align256(mla::plan_bytes((int)B, plan_units(d, s, fp8)));
   L.part_lse = L.q_abs + align256(B * s.H * s.DC * 2);
   L.part_o = L.part_lse + align256(slots * s.H * 4);
   L.total = L.part_o + align256(slots * s.H * s.DC * 2);
@@ -108,7 +112,11 @@ extern "C" {
 size_t mla_decode_workspace_bytes(const mla_dims_t* dims) {
   ShapeInfo s;
   if (check_dims(dims, &s) != MLA_OK) return 0;
-  return layout(dims, s).total;
+  // enough for either cache format (the FP8 one may use more plan units)
+  const size_t a = layout(dims, s, false).total;
+  if (s.shape != mla::kShapeMha2Mla) return a;
+  const size_t b = layout(dims, s, true).total;
+  return a > b ? a : b;
 }
 
 }  // extern "C"
@@ -140,7 +148,8 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
       !aligned16(out) || (lse_out && !aligned16(lse_out)) ||
       (workspace && ((uintptr_t)workspace & 255) != 0))
     return MLA_ERR_MISALIGNED;
-  const Layout L = layout(dims, s);
+  const bool fp8 = kv_scales != nullptr;
+  const Layout L = layout(dims, s, fp8);
   if (!workspace || workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
 
   const hipStream_t hs = (hipStream_t)stream;
@@ -159,7 +168,7 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
     if ((st = hip_status(hipStreamSynchronize(hs))) != MLA_OK) return st;
     if (host_flag != 0) return MLA_ERR_DEVICE_CHECK;
   }
-  const int G = plan_units(dims, s);
+  const int G = plan_units(dims, s, fp8);
   const float scale = dims->softmax_scale > 0.f ? dims->softmax_scale
                                                 : 1.0f / sqrtf((float)(s.DN + s.DR));
   const float scale_log2 = scale * mla::kLog2e;

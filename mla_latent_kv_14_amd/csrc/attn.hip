@@ -510,12 +510,12 @@ constexpr int IPW = Tile::INSTR;  // the wave issues the whole tile
 constexpr float kRescale = 64.f;  // log2 headroom before the running max must move
 // FP8 cache: a token row is [c_KV as FP8 e4m3 (64 bytes) | k_R bf16 (16 bytes)], 80 bytes,
 // and each token has an fp32 scale in a separate array of the same page geometry. A loaded
-// tile is its 5 KiB of rows followed by its 64 scales (256 bytes); a five-deep ring holds four
-// in flight. When its turn comes, a tile is dequantised into one bf16 tile of the layout above
-// (lane l: token row l, c_KV * scale rounded to bf16, k_R copied), which the compute then reads.
+// tile is its 5 KiB of rows followed by its 64 scales (256 bytes), in a two-deep ring (one in
+// flight while the other is used); the wave's 20 KiB of LDS let two work groups share a CU. When its turn comes, a tile is dequantised into one bf16 tile of the layout above
+// (lane l: token row l, c_KV * scale, exact for the power-of-two scales of the format; k_R
+// copied), which the compute then reads.
 constexpr int ROWB8 = DC + 2 * DR;
 using Tile8 = PagedTile<TT, ROWB8>;
-constexpr int NS = 5;
 constexpr int SB8 = Tile8::BYTES + 4 * TT;  // bytes of one loaded FP8 tile with its scales
 }  // namespace m2
 
@@ -529,7 +529,7 @@ __device__ __forceinline__ void wait_tiles_upto4(int after) {
   else wait_vmcnt<0>();
 }
 
-template <bool FP8>
+template <bool FP8, int NB>
 __global__ void __launch_bounds__(256)
 attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
                     const char* __restrict__ kv, const int32_t* __restrict__ page_table,
@@ -540,10 +540,9 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
                     const float* __restrict__ kv_scales) {
   using namespace m2;
   using TileL = typename std::conditional<FP8, Tile8, Tile>::type;  // the format as loaded
-  constexpr int NB = FP8 ? NS : NBUF;                     // ring of loaded tiles
   constexpr int LB = FP8 ? SB8 : Tile::BYTES;             // bytes of one ring entry
   constexpr int IPW = TileL::INSTR + (FP8 ? 1 : 0);       // load instructions per tile
-  constexpr int WAVE_LDS = FP8 ? NS * SB8 + Tile::BYTES : NBUF * Tile::BYTES;
+  constexpr int WAVE_LDS = FP8 ? NB * SB8 + Tile::BYTES : NB * Tile::BYTES;
   __shared__ __attribute__((aligned(1024))) char lds_tiles[kAttnWavesMha2Mla][WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
@@ -553,7 +552,7 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   const int n = g < G ? us.n : 0;  // tiles of this unit
   if (n <= 0) return;
   MLA_LDS char* tiles = (MLA_LDS char*)lds_tiles[wave];
-  MLA_LDS char* conv = tiles + NS * SB8;  // FP8: the dequantised bf16 tile
+  MLA_LDS char* conv = tiles + NB * SB8;  // FP8: the dequantised bf16 tile
 
   Cursor lc = {us.b, us.j, us.nj, us.S};
   Cursor cc = lc;
@@ -584,9 +583,10 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       load_lds_4(kv_scales + (size_t)page * kPage + (c.j % Tile8::TPP) * TT,
                  4u * (uint32_t)min(lane, valid - 1), dst + Tile8::BYTES);
   };
-  // FP8: lane l dequantises token row l of a loaded tile into the bf16 tile
+  // FP8: lane l dequantises token row l of a loaded tile into the bf16 tile. The scaled
+  // conversion multiplies by 2^(exponent of the fp32 scale), exactly: a power-of-two scale is
+  // applied as is (the mantissa bits of any other value are ignored).
   auto convert = [&](const MLA_LDS char* src) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
     const MLA_LDS char* row = src + lane * ROWB8;
     const float sc = *reinterpret_cast<const MLA_LDS float*>(src + Tile8::BYTES + 4 * lane);
 #pragma unroll
@@ -594,11 +594,11 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       const u32x4 w = *reinterpret_cast<const MLA_LDS u32x4*>(row + 16 * q);
       uint32_t o[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);  // values 4i, 4i+1
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);   // values 4i+2, 4i+3
-        o[2 * i] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
-        o[2 * i + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+      for (int i = 0; i < 4; ++i) {  // bytes 0,1 and 2,3 of word i
+        o[2 * i] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, false));
+        o[2 * i + 1] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, true));
       }
       *reinterpret_cast<MLA_LDS u32x4*>(conv + Tile::lds_off(lane, 2 * q)) =
           u32x4{o[0], o[1], o[2], o[3]};
@@ -775,16 +775,16 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
                          scale_log2, (uint16_t*)part_o, part_lse);
   }
   const int blocks = (G + kAttnWavesMha2Mla - 1) / kAttnWavesMha2Mla;
-  if (kv_scales)
-    return launch_kernel(attn_mha2mla_kernel<true>, dim3(blocks), dim3(64 * kAttnWavesMha2Mla), L,
+  auto go = [&](auto kernel) {
+    return launch_kernel(kernel, dim3(blocks), dim3(64 * kAttnWavesMha2Mla), L,
                          (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv,
                          page_table, seq_lens, B, max_pages, q_len, num_pages,
                          (const Plan*)plan, G, scale_log2, (uint16_t*)part_o, part_lse,
                          kv_scales);
-  return launch_kernel(attn_mha2mla_kernel<false>, dim3(blocks), dim3(64 * kAttnWavesMha2Mla), L,
-                       (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv,
-                       page_table, seq_lens, B, max_pages, q_len, num_pages, (const Plan*)plan, G,
-                       scale_log2, (uint16_t*)part_o, part_lse, (const float*)nullptr);
+  };
+  // FP8: a two-deep ring (20 KiB a wave) lets two work groups share a CU, two waves a SIMD
+  if (kv_scales) return go(attn_mha2mla_kernel<true, kRingFp8>);
+  return go(attn_mha2mla_kernel<false, m2::NBUF>);
 }
 
 }  // namespace mla

@@ -33,6 +33,9 @@ enum Shape : int {
 // MHA2MLA attention: waves per work group; each wave is one plan unit. (DeepSeek widths: one
 // plan unit is served by two work groups, one per half of the heads.)
 constexpr int kAttnWavesMha2Mla = 4;
+// FP8 cache (MHA2MLA widths): ring depth of the attention kernel, and its work groups per CU
+constexpr int kRingFp8 = 2;
+constexpr int kGroupsPerCuFp8 = 2;
 
 // B counts virtual sequences (sequences x query tokens, q_len per sequence) in the three
 // decode launches; seq_lens and page_table stay per sequence.

@@ -63,9 +63,11 @@ def test_workspace_bytes_closed_form():
     slots = 128 + 16
     assert M.workspace_bytes(d) == (al(plan(16, 128)) + al(16 * 128 * 512 * 2) + al(slots * 128 * 4)
                                     + al(slots * 128 * 512 * 2))
+    # MHA2MLA widths: sized for the FP8 cache's plan, 2048 units (two work groups per CU),
+    # which also covers the bf16 cache's 1024
     d = m2_dims()
-    slots = 1024 + 32
-    assert M.workspace_bytes(d) == (al(plan(32, 1024)) + al(32 * 32 * 64 * 2) + al(slots * 32 * 4)
+    slots = 2048 + 32
+    assert M.workspace_bytes(d) == (al(plan(32, 2048)) + al(32 * 32 * 64 * 2) + al(slots * 32 * 4)
                                     + al(slots * 32 * 64 * 2))
     # units are capped by the tiles that can exist: B=1, S=512 -> 16 tiles of 32 tokens
     d = ds_dims(B=1, max_pages=8, num_pages=8, max_seq_len=512)
@@ -109,8 +111,17 @@ def test_workspace_too_small_or_missing():
     need = M.workspace_bytes(d)
     assert call(d, ws_bytes=need - 1) == STATUS_CODE["MLA_ERR_WORKSPACE"]
     assert call(d, ws=ctypes.c_void_p(0)) == STATUS_CODE["MLA_ERR_WORKSPACE"]
+    # MHA2MLA widths: the bf16 cache needs its own plan's bytes (1024 units), the FP8 cache
+    # the full mla_decode_workspace_bytes (2048 units)
     d = m2_dims()
-    assert call(d, ws_bytes=M.workspace_bytes(d) - 256) == STATUS_CODE["MLA_ERR_WORKSPACE"]
+    al = lambda x: (x + 255) // 256 * 256
+    bf16_need = (al((16 + 4 * 32 + 31) // 32 * 32 + 32 * 1024) + al(32 * 32 * 64 * 2)
+                 + al(1056 * 32 * 4) + al(1056 * 32 * 64 * 2))
+    assert call(d, ws_bytes=bf16_need - 256) == STATUS_CODE["MLA_ERR_WORKSPACE"]
+    p = [_al(k + 1) for k in range(5)] + [_al(6)] + [_al(k + 7) for k in range(3)]
+    assert M.lib().mla_decode_fp8(ctypes.byref(d), *p, ctypes.c_void_p(0), _al(10),
+                                  M.workspace_bytes(d) - 256, ctypes.c_void_p(0), None) == \
+        STATUS_CODE["MLA_ERR_WORKSPACE"]
 
 
 def test_gather_rejects_bad_args():

@@ -103,6 +103,21 @@ def test_fp8_equals_bf16_on_the_same_values(M):
     assert torch.equal(a, b)
 
 
+def test_fp8_scale_mantissa_is_ignored(M):
+    # a scale that is not a power of two acts as the power of two of its exponent: scaling
+    # each token's scale by a factor in [1, 2) leaves the result bit for bit the same
+    inp = _inp([300, 64, 129], 51)
+    kv8, sc = W.fp8_cache(inp, seed=6)
+    g = torch.Generator().manual_seed(7)
+    sc2 = sc * (1.0 + torch.rand(sc.shape, generator=g) * 0.999)
+    assert not torch.equal(sc, sc2)
+    d = to_dev(inp)
+    a, b = (M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8.cuda(),
+                     d["page_table"], d["seq_lens"], kv_scales=s.cuda()) for s in (sc, sc2))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 def test_fp8_workload_full_size(M):
     # the MHA2MLA workload (B=32, S=32768) over an FP8 copy of its cache, every (b, h)
     inp = W.config_inputs(5)
