@@ -214,7 +214,7 @@ def run(args):
 
     attn_s = stage_ms[1] * 1e-3
     achieved = alg["attn_bytes"] / attn_s / 1e9
-    traffic = None if args.kv_fp8 else measured_traffic(cfg["name"])
+    traffic = measured_traffic(cfg["name"] + ("_fp8" if args.kv_fp8 else ""))
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": "attn_deepseek_kernel" if cfg["H"] == 128

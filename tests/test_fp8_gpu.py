@@ -132,3 +132,112 @@ def test_fp8_rejected_for_deepseek_widths(M):
         M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8.cuda(), d["page_table"],
                  d["seq_lens"], kv_scales=sc.cuda())
     assert e.value.code == 5  # MLA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("units", [1, 5, 33])
+def test_fp8_query_tokens_split_plans(M, units):
+    # three query tokens per sequence over split plans: a unit's tiles cross virtual sequences
+    inp = _inp([200, 3, 64 * 5 + 9], 61, poison=True)
+    g = torch.Generator().manual_seed(62)
+    inp["q_nope"] = torch.randn(3, 3, 32, 120, generator=g).to(torch.bfloat16)
+    inp["q_rope"] = torch.randn(3, 3, 32, 8, generator=g).to(torch.bfloat16)
+    check_fp8(M, inp, units=units, poison=True, label="fp8 3 tokens, %d units" % units)
+
+
+def test_fp8_empty_sequence_gives_zero_and_neg_inf(M):
+    inp = _inp([100, 5, 64], 63)
+    kv8, sc = W.fp8_cache(inp, seed=1)
+    d = to_dev(inp)
+    d["seq_lens"][1] = 0
+    say("fp8 empty sequence")
+    out, lse = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8.cuda(),
+                        d["page_table"], d["seq_lens"], return_lse=True, kv_scales=sc.cuda())
+    torch.cuda.synchronize()
+    assert torch.all(out[1].float() == 0)
+    assert torch.all(torch.isneginf(lse[1]))
+    assert torch.isfinite(out[0].float()).all() and torch.isfinite(out[2].float()).all()
+
+
+def test_fp8_check_mode_decodes_as_without(M):
+    import os
+    inp = _inp([1, 65, 300, 128], 64)
+    kv8, sc = W.fp8_cache(inp, seed=2)
+    d = to_dev(inp)
+    kv8, sc = kv8.cuda(), sc.cuda()
+
+    def run():
+        o = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8, d["page_table"],
+                     d["seq_lens"], kv_scales=sc)
+        torch.cuda.synchronize()
+        return o
+
+    ref = run()
+    os.environ["MLA_CHECK"] = "1"
+    try:
+        got = run()
+        good = d["seq_lens"].clone()
+        d["seq_lens"][2] = 64 * d["page_table"].shape[1] + 1  # past the page table
+        with pytest.raises(M.MlaError) as e:
+            run()
+        assert e.value.code == 7  # MLA_ERR_DEVICE_CHECK
+        d["seq_lens"].copy_(good)
+    finally:
+        del os.environ["MLA_CHECK"]
+    assert torch.equal(got, ref)
+
+
+def test_fp8_graph_replays_match_eager(M):
+    # the FP8 decode captured in a HIP graph: replays with refilled inputs (other values, same
+    # shapes), eager decodes in between, each replay bit-identical to the eager call
+    lens = [1, 33, 100, 190, 700]
+    sets = {}
+    for name, seed in (("a", 71), ("b", 72)):
+        inp = _inp(lens, seed)
+        kv8, sc = W.fp8_cache(inp, seed=seed)
+        dd = to_dev(inp)
+        dd["kv_pages"], dd["kv_scales"] = kv8.cuda(), sc.cuda()
+        sets[name] = dd
+    keys = ("q_nope", "q_rope", "W_UK", "W_UV", "kv_pages", "kv_scales", "page_table",
+            "seq_lens")
+
+    def call(d, **kw):
+        return M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], d["kv_pages"],
+                        d["page_table"], d["seq_lens"], kv_scales=d["kv_scales"], **kw)
+
+    def eager(d):
+        o, l = call(d, return_lse=True)
+        torch.cuda.synchronize()
+        return o, l
+
+    ref = {k: eager(v) for k, v in sets.items()}
+    assert not torch.equal(ref["a"][0], ref["b"][0])
+    st = {k: sets["a"][k].clone() for k in keys}
+    B = len(lens)
+    out = torch.empty((B, 32, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 32), dtype=torch.float32, device="cuda")
+    dm = M.make_dims(st["q_nope"], st["q_rope"], st["W_UK"], st["W_UV"], st["kv_pages"],
+                     st["page_table"])
+    ws = torch.empty(M.workspace_bytes(dm), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(st, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say("fp8 graph capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(st, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for rep, name in enumerate(["a", "b", "b", "a", "b"]):
+        for k in keys:
+            st[k].copy_(sets[name][k])
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("fp8 graph replay", rep, name)
+        assert torch.equal(out.view(torch.int16), ref[name][0].view(torch.int16)), (rep, name)
+        assert torch.equal(lse.view(torch.int32), ref[name][1].view(torch.int32)), (rep, name)
+        eager(sets["b" if name == "a" else "a"])
