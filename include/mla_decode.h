@@ -17,7 +17,9 @@
  *
  * Supported shapes: (num_heads, d_nope, d_latent, d_rope, d_v) = (128, 128, 512, 64, 128),
  * the DeepSeek-V2/V3 widths (bhfrc.com/news/60867 S3), and (32, 120, 64, 8, 128), the MHA2MLA
- * Llama-2-7B attention config (lpnh.cn/news/2494972 S3.2). page_size must be 64.
+ * Llama-2-7B attention config (lpnh.cn/news/2494972 S3.2). page_size must be 64. The cache is
+ * bf16 (mla_decode, mla_decode_timed, mla_decode_out) or, at the MHA2MLA widths, FP8 E4M3 with
+ * a power-of-two scale per token (mla_decode_fp8).
  *
  * Conventions for every entry point:
  *   - tensors are dense row-major, in device memory, 16-byte aligned; bf16 is stored as its
@@ -32,10 +34,10 @@
  *   - device-resident values are clamped, never trusted: seq_lens[b] is clamped to
  *     [0, max_pages_per_seq * 64] and page ids to [0, num_pages - 1], so a bad table gives
  *     wrong numbers, not a memory fault. A sequence with S_b <= 0 gets out = 0, lse = -inf.
- *   - with MLA_CHECK=1 in the environment, mla_decode and mla_decode_timed first validate
- *     seq_lens and the page-table entries the sequences use on the device, synchronise the
- *     stream, and return MLA_ERR_DEVICE_CHECK (with nothing else enqueued) when one is out of
- *     range. This debugging mode is the only case in which the library synchronises.
+ *   - with MLA_CHECK=1 in the environment, every decode entry point first validates
+ *     seq_lens and the page-table entries the sequences use on the device, synchronises the
+ *     stream, and returns MLA_ERR_DEVICE_CHECK (with nothing else enqueued) when one is out
+ *     of range. This debugging mode is the only case in which the library synchronises.
  *   - page-table entries at or past ceil(S_b / 64) and cache slots at or past S_b are never
  *     read into the result (they may hold anything, including NaN).
  */
