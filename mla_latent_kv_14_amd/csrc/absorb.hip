@@ -9,9 +9,12 @@
 // straight from global memory (8 consecutive d per lane), fp32 accumulation, bf16 (RNE) out.
 // The kernel streams 2*H*d_n*d_c bytes of weight once; it is HBM-bound.
 //
-// One extra block (the first, so that it is dispatched at once: its chain of dependent loads is
-// the longest in the kernel) writes the work plan for the attention kernel (see Plan in
-// device.h), in parallel with the others.
+// Extra blocks (the first ones, so that they are dispatched at once: their chain of dependent
+// loads is the longest in the kernel) write the work plan for the attention kernel (see Plan in
+// device.h), in parallel with the others. Each plan block redoes the prefix sum over the
+// sequences (cheap up to a few thousand) and resolves every thread's share of the units, at
+// most one unit per thread where the block count allows: a unit costs a search, a dependent
+// page-table load and a store, and a second round of them a few microseconds.
 #include "device.h"
 #include "kernels.h"
 
@@ -26,7 +29,7 @@ constexpr int kPlanLdsBytes = (2 * kSeqInLds + 8) * 4;
 __device__ void build_plan(const int32_t* __restrict__ seq_lens,
                            const int32_t* __restrict__ page_table, int B, int max_pages,
                            int q_len, int G, int TT, Plan* __restrict__ plan,
-                           MLA_LDS char* scratch) {
+                           MLA_LDS char* scratch, int part, int parts) {
   MLA_LDS int32_t* seq_off = (MLA_LDS int32_t*)scratch;
   MLA_LDS int32_t* seq_len = seq_off + kSeqInLds;
   MLA_LDS int32_t* wave_tot = seq_len + kSeqInLds;
@@ -53,7 +56,7 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens,
     int before = carry;
     for (int w = 0; w < wave; ++w) before += wave_tot[w];
     if (b < B) {
-      off[b] = before + x - n;
+      if (part == 0) off[b] = before + x - n;
       if (b < kSeqInLds) {
         seq_off[b] = before + x - n;
         seq_len[b] = S;
@@ -66,7 +69,7 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens,
   const int g = G < 1 ? 1 : G;
   const int total = carry;
   const int per = (total + g - 1) / g;
-  if (tid == 0) {
+  if (tid == 0 && part == 0) {
     plan->total = total;
     plan->per = per;
     plan->groups = g;
@@ -85,17 +88,17 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens,
     start[u] = rec;
   };
   // idle units (no tiles: u * per >= total) get an all-zero record
-  for (int u = tid; u < g; u += 256)
+  for (int u = part * 256 + tid; u < g; u += parts * 256)
     if ((long long)u * per >= total) start[u] = UnitStart{0, 0, 0, 0, 0, 0, {0, 0}};
   if (B <= kSeqInLds) {
     // every unit on its own: its sequence by binary search over the offsets in LDS (the last
     // b with off[b] <= u*per; sequences with no tiles share their successor's offset and are
     // skipped by taking the last), then the page of its first tile
-    for (int u0 = tid; u0 < g; u0 += 4 * 256) {
+    for (int u0 = part * 256 + tid; u0 < g; u0 += 4 * 256 * parts) {
       int ub[4], uj[4], page[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int u = u0 + k * 256;
+        const int u = u0 + k * 256 * parts;
         ub[k] = -1;
         uj[k] = 0;
         page[k] = 0;
@@ -113,9 +116,10 @@ __device__ void build_plan(const int32_t* __restrict__ seq_lens,
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if (ub[k] >= 0) write_unit(u0 + k * 256, ub[k], uj[k], seq_len[ub[k]], page[k]);
+        if (ub[k] >= 0)
+          write_unit(u0 + k * 256 * parts, ub[k], uj[k], seq_len[ub[k]], page[k]);
     }
-  } else {
+  } else if (part == 0) {  // (one plan block for large batches)
     // large batches: each thread walks the units that start in its sequences
     for (int b = tid; b < B; b += 256) {
       const int S = virt_len(clamp_len(seq_lens[virt_row(b, q_len)], max_pages), b, q_len);
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
                                                      const int32_t* __restrict__ seq_lens,
                                                      const int32_t* __restrict__ page_table,
                                                      int max_pages, int q_len, int G, int TT,
-                                                     Plan* plan) {
+                                                     Plan* plan, int plan_blocks) {
   constexpr int DNP = (DN + 31) / 32 * 32;  // contraction padded to the MFMA K of 32
   constexpr int ROWB = CB * 2;              // LDS bytes per W row
   constexpr int UNITS = ROWB / 32;          // 32-byte units per row (swizzle period)
@@ -150,11 +154,12 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = DC / CB;
-  if (blockIdx.x == 0) {  // the extra first block writes the work plan, nothing else
-    build_plan(seq_lens, page_table, B, max_pages, q_len, G, TT, plan, (MLA_LDS char*)wt);
+  if (blockIdx.x < plan_blocks) {  // the first blocks write the work plan, nothing else
+    build_plan(seq_lens, page_table, B, max_pages, q_len, G, TT, plan, (MLA_LDS char*)wt,
+               blockIdx.x, plan_blocks);
     return;
   }
-  const int h = (blockIdx.x - 1) / nblk, cblk = (blockIdx.x - 1) % nblk;
+  const int h = (blockIdx.x - plan_blocks) / nblk, cblk = (blockIdx.x - plan_blocks) % nblk;
 
   // ---- stage W_UK[h][0:DN][cblk*CB : +CB] in LDS
   const char* Wg = reinterpret_cast<const char*>(W_UK + (size_t)h * DN * DC + (size_t)cblk * CB);
@@ -235,16 +240,18 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 hipError_t launch_absorb(int shape, const void* q_nope, const void* W_UK, void* q_abs, int B,
                          int H, const int32_t* seq_lens, const int32_t* page_table, int max_pages,
                          int q_len, int G, void* plan, const Launch& L) {
+  // plan blocks: one per 256 units (up to 8) while the offsets fit in LDS, else one
+  const int PB = B <= kSeqInLds ? min(8, max(1, (G + 255) / 256)) : 1;
   if (shape == kShapeDeepSeek) {
     constexpr int DN = 128, DC = 512, CB = 128;
-    return launch_kernel(absorb_kernel<DN, DC, CB>, dim3(H * (DC / CB) + 1), dim3(256), L,
+    return launch_kernel(absorb_kernel<DN, DC, CB>, dim3(H * (DC / CB) + PB), dim3(256), L,
                          (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H,
-                         seq_lens, page_table, max_pages, q_len, G, (int)kSub, (Plan*)plan);
+                         seq_lens, page_table, max_pages, q_len, G, (int)kSub, (Plan*)plan, PB);
   }
   constexpr int DN = 120, DC = 64, CB = 64;
-  return launch_kernel(absorb_kernel<DN, DC, CB>, dim3(H * (DC / CB) + 1), dim3(256), L,
+  return launch_kernel(absorb_kernel<DN, DC, CB>, dim3(H * (DC / CB) + PB), dim3(256), L,
                        (const uint16_t*)q_nope, (const uint16_t*)W_UK, (uint16_t*)q_abs, B, H,
-                       seq_lens, page_table, max_pages, q_len, G, (int)kPage, (Plan*)plan);
+                       seq_lens, page_table, max_pages, q_len, G, (int)kPage, (Plan*)plan, PB);
 }
 
 }  // namespace mla
