@@ -123,6 +123,13 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
       ls[it][u] = s < count[it] ? l : -INFINITY;
     }
   }
+  int lse_at[IPT];  // lse_out index of this thread's item, or -1
+  float lse_val[IPT];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    lse_at[it] = -1;
+    lse_val[it] = 0.f;
+  }
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
     const int item = tid / J + it * (NT / J);
@@ -198,7 +205,13 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
       } else {
         *reinterpret_cast<MLA_LDS bf16x8*>(ol + bi * OPITCH + ch * 16) = o;
       }
-      if (ch == 0 && eblk == 0 && b < B && lse_out) lse_out[(size_t)b * H + h] = L;
+      if (ch == 0 && eblk == 0 && b < B && lse_out) {
+        // stored at the very end (a store counts like a load in the wait for the W block,
+        // and would hold every wave at that wait for its write latency)
+        if (LAT) lse_out[(size_t)b * H + h] = L;
+        lse_at[it] = (int)((size_t)b * H + h);
+        lse_val[it] = L;
+      }
     }
   }
   if (LAT) return;
@@ -225,6 +238,9 @@ combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ pa
       *reinterpret_cast<bf16x4*>(out + ((size_t)b * H + h) * DV + e0) = o;
     }
   }
+#pragma unroll
+  for (int it = 0; it < IPT; ++it)
+    if (lse_at[it] >= 0) lse_out[lse_at[it]] = lse_val[it];
 }
 
 hipError_t launch_combine_latent(int shape, const void* part_o, const float* part_lse,
