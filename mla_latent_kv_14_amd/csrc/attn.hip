@@ -509,11 +509,14 @@ using Tile = PagedTile<TT, ROWB>;
 constexpr int IPW = Tile::INSTR;  // the wave issues the whole tile
 constexpr float kRescale = 64.f;  // log2 headroom before the running max must move
 // FP8 cache: a token row is [c_KV as FP8 e4m3 (64 bytes) | k_R bf16 (16 bytes)], 80 bytes,
-// and each token has an fp32 scale in a separate array of the same page geometry. A loaded
-// tile is its 5 KiB of rows followed by its 64 scales (256 bytes), in a two-deep ring (one in
-// flight while the other is used); the wave's 20 KiB of LDS let two work groups share a CU. When its turn comes, a tile is dequantised into one bf16 tile of the layout above
-// (lane l: token row l, c_KV * scale, exact for the power-of-two scales of the format; k_R
-// copied), which the compute then reads.
+// and each token has an fp32 power-of-two scale in a separate array of the same page geometry.
+// A loaded tile is its 5 KiB of rows followed by its 64 scales (256 bytes), in a three-deep
+// ring (two in flight while one is used). The MFMA operands are formed from the FP8 bytes in
+// registers: the score operand (8 latent values of one token row) is converted with that
+// token's scale; the value operand (8 tokens of one latent column, from 8-bit transposing
+// reads) is converted unscaled, and each token's scale multiplies its softmax weight instead.
+// A power of two moves exactly between the two factors, so the products are those of the bf16
+// cache holding c_KV * scale.
 constexpr int ROWB8 = DC + 2 * DR;
 using Tile8 = PagedTile<TT, ROWB8>;
 constexpr int SB8 = Tile8::BYTES + 4 * TT;  // bytes of one loaded FP8 tile with its scales
@@ -542,7 +545,7 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   using TileL = typename std::conditional<FP8, Tile8, Tile>::type;  // the format as loaded
   constexpr int LB = FP8 ? SB8 : Tile::BYTES;             // bytes of one ring entry
   constexpr int IPW = TileL::INSTR + (FP8 ? 1 : 0);       // load instructions per tile
-  constexpr int WAVE_LDS = FP8 ? NB * SB8 + Tile::BYTES : NB * Tile::BYTES;
+  constexpr int WAVE_LDS = NB * LB;
   __shared__ __attribute__((aligned(1024))) char lds_tiles[kAttnWavesMha2Mla][WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
@@ -552,7 +555,6 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   const int n = g < G ? us.n : 0;  // tiles of this unit
   if (n <= 0) return;
   MLA_LDS char* tiles = (MLA_LDS char*)lds_tiles[wave];
-  MLA_LDS char* conv = tiles + NB * SB8;  // FP8: the dequantised bf16 tile
 
   Cursor lc = {us.b, us.j, us.nj, us.S};
   Cursor cc = lc;
@@ -583,30 +585,14 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       load_lds_4(kv_scales + (size_t)page * kPage + (c.j % Tile8::TPP) * TT,
                  4u * (uint32_t)min(lane, valid - 1), dst + Tile8::BYTES);
   };
-  // FP8: lane l dequantises token row l of a loaded tile into the bf16 tile. The scaled
-  // conversion multiplies by 2^(exponent of the fp32 scale), exactly: a power-of-two scale is
-  // applied as is (the mantissa bits of any other value are ignored).
-  auto convert = [&](const MLA_LDS char* src) {
-    const MLA_LDS char* row = src + lane * ROWB8;
-    const float sc = *reinterpret_cast<const MLA_LDS float*>(src + Tile8::BYTES + 4 * lane);
-#pragma unroll
-    for (int q = 0; q < DC / 16; ++q) {  // 16 FP8 values -> two chunks of 8 bf16
-      const u32x4 w = *reinterpret_cast<const MLA_LDS u32x4*>(row + 16 * q);
-      uint32_t o[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {  // bytes 0,1 and 2,3 of word i
-        o[2 * i] = __builtin_bit_cast(uint32_t,
-                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, false));
-        o[2 * i + 1] = __builtin_bit_cast(
-            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, true));
-      }
-      *reinterpret_cast<MLA_LDS u32x4*>(conv + Tile::lds_off(lane, 2 * q)) =
-          u32x4{o[0], o[1], o[2], o[3]};
-      *reinterpret_cast<MLA_LDS u32x4*>(conv + Tile::lds_off(lane, 2 * q + 1)) =
-          u32x4{o[4], o[5], o[6], o[7]};
-    }
-    *reinterpret_cast<MLA_LDS u32x4*>(conv + Tile::lds_off(lane, DC / 8)) =
-        *reinterpret_cast<const MLA_LDS u32x4*>(row + DC);
+  // FP8 -> bf16, 8 values from two words (bytes 0..7 in order), times 2^(exponent of sc)
+  auto cvt8 = [](uint32_t w0, uint32_t w1, float sc) {
+    const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
+    const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
+    const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
+    const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
+    return cat4(__builtin_shufflevector(a0, a1, 0, 1, 2, 3),
+                __builtin_shufflevector(a2, a3, 0, 1, 2, 3));
   };
 
   const int t32 = lane & 31, hi = lane >> 5;
@@ -647,13 +633,8 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       cursor_next(lc, plan, seq_lens, B, max_pages, q_len);
       ++issued;
     }
-    const MLA_LDS char* kb;
-    if constexpr (FP8) {
-      convert(tiles + (it % NB) * LB);  // the last pass's reads of conv came first
-      kb = conv;
-    } else {
-      kb = tiles + (it % NB) * Tile::BYTES;
-    }
+    const MLA_LDS char* kb = tiles + (it % NB) * LB;
+    const MLA_LDS float* ksc = reinterpret_cast<const MLA_LDS float*>(kb + Tile8::BYTES);
 
     // ---- scores for tokens [32*mb2, 32*mb2 + 32)
     f32x16 s[2];
@@ -661,11 +642,22 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
     for (int mb2 = 0; mb2 < 2; ++mb2) {
       const int row = 32 * mb2 + t32;
       f32x16 a = {};
+      i16x4 kr;
+      if constexpr (FP8) {  // latent values 16st + 8hi .. +8 of token row `row`, scaled
+        const MLA_LDS char* rp = kb + row * ROWB8;
+        const float sc = ksc[row];
 #pragma unroll
-      for (int st = 0; st < DC / 16; ++st)
-        a = mfma_32x32x16(lds_read_b128(kb, Tile::lds_off(row, 2 * st + hi)), qf[st], a);
-      const i16x4 kr = *reinterpret_cast<const MLA_LDS i16x4*>(
-          kb + Tile::lds_off(row, DC / 8) + 8 * hi);
+        for (int st = 0; st < DC / 16; ++st) {
+          const u32x2 w = *reinterpret_cast<const MLA_LDS u32x2*>(rp + 16 * st + 8 * hi);
+          a = mfma_32x32x16(cvt8(w[0], w[1], sc), qf[st], a);
+        }
+        kr = *reinterpret_cast<const MLA_LDS i16x4*>(rp + DC + 8 * hi);
+      } else {
+#pragma unroll
+        for (int st = 0; st < DC / 16; ++st)
+          a = mfma_32x32x16(lds_read_b128(kb, Tile::lds_off(row, 2 * st + hi)), qf[st], a);
+        kr = *reinterpret_cast<const MLA_LDS i16x4*>(kb + Tile::lds_off(row, DC / 8) + 8 * hi);
+      }
       s[mb2] = mfma_32x32x8(kr, qr4, a);
     }
     // ---- online softmax, lane = head t32 x 32 tokens
@@ -717,7 +709,15 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float p = exp2f_fast(__builtin_fmaf(s[mb2][8 * half + j], scale_log2, -m_used));
-          pa[2 * mb2 + half][j] = (__bf16)p;
+          if constexpr (FP8) {  // token 32mb2 + 16half + 8(j/4) + 4hi + j%4 carries its scale
+            // the scale's power of two (its exponent bits), as the conversion applies it
+            const float sc = __builtin_bit_cast(
+                float, __builtin_bit_cast(uint32_t, ksc[32 * mb2 + 16 * half + 8 * (j >> 2) +
+                                                        4 * hi + (j & 3)]) & 0x7F800000u);
+            pa[2 * mb2 + half][j] = (__bf16)(p * sc);
+          } else {
+            pa[2 * mb2 + half][j] = (__bf16)p;
+          }
           lsum += p;  // the unrounded weight: l differs from the sum of the bf16 weights by
                       // rounding noise of relative size 2^-9 / sqrt(tokens)
         }
@@ -729,6 +729,19 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
       const int mb2 = kk >> 1, half = kk & 1;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
+        if constexpr (FP8) {
+          // 8-bit transposing read: in each group of 16 lanes, lane w supplies the 8 bytes at
+          // (token T(w >> 1), columns 32nb + 16(G16 & 1) + 8(w & 1) ..+8), and lane l receives
+          // byte l % 8 of the segments of lanes 2b + ((l >> 3) & 1), b = 0..7: the column
+          // 32nb + (l & 31) of the tokens T(b) = 32mb2 + 16half + 8(b/4) + 4hi + b%4
+          const int w = q16, b = w >> 1;
+          const int t = 32 * mb2 + 16 * half + 8 * (b >> 2) + 4 * (G16 >> 1) + (b & 3);
+          typedef int v2i __attribute__((ext_vector_type(2)));
+          const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (MLA_LDS v2i*)(kb + t * ROWB8 + 32 * nb + 16 * (G16 & 1) + 8 * (w & 1)));
+          acc[nb] = mfma_32x32x16(pa[kk], cvt8((uint32_t)r[0], (uint32_t)r[1], 1.0f), acc[nb]);
+          continue;
+        }
         bf16x4 v2[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
@@ -782,7 +795,8 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
                          (const Plan*)plan, G, scale_log2, (uint16_t*)part_o, part_lse,
                          kv_scales);
   };
-  // FP8: a two-deep ring (20 KiB a wave) lets two work groups share a CU, two waves a SIMD
+  // FP8: a three-deep ring of 5.25 KiB tiles (16 KiB a wave) lets two work groups share a
+  // CU, two waves a SIMD
   if (kv_scales) return go(attn_mha2mla_kernel<true, kRingFp8>);
   return go(attn_mha2mla_kernel<false, m2::NBUF>);
 }

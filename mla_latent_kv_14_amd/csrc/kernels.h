@@ -34,7 +34,7 @@ enum Shape : int {
 // plan unit is served by two work groups, one per half of the heads.)
 constexpr int kAttnWavesMha2Mla = 4;
 // FP8 cache (MHA2MLA widths): ring depth of the attention kernel, and its work groups per CU
-constexpr int kRingFp8 = 2;
+constexpr int kRingFp8 = 3;
 constexpr int kGroupsPerCuFp8 = 2;
 
 // B counts virtual sequences (sequences x query tokens, q_len per sequence) in the three
