@@ -35,9 +35,10 @@
  *     [0, max_pages_per_seq * 64] and page ids to [0, num_pages - 1], so a bad table gives
  *     wrong numbers, not a memory fault. A sequence with S_b <= 0 gets out = 0, lse = -inf.
  *   - with MLA_CHECK=1 in the environment, every decode entry point first validates
- *     seq_lens and the page-table entries the sequences use on the device, synchronises the
- *     stream, and returns MLA_ERR_DEVICE_CHECK (with nothing else enqueued) when one is out
- *     of range. This debugging mode is the only case in which the library synchronises.
+ *     seq_lens, the page-table entries the sequences use and (FP8 cache) the scales of the
+ *     slots they use on the device, synchronises the stream, and returns
+ *     MLA_ERR_DEVICE_CHECK (with nothing else enqueued) when one is out of range. This
+ *     debugging mode is the only case in which the library synchronises.
  *   - page-table entries at or past ceil(S_b / 64) and cache slots at or past S_b are never
  *     read into the result (they may hold anything, including NaN).
  */
@@ -60,8 +61,10 @@ typedef enum {
     MLA_ERR_UNSUPPORTED = 5, /* head/width combination or page size not built             */
     MLA_ERR_HIP = 6,         /* the HIP runtime reported an error while enqueueing        */
     MLA_ERR_DEVICE_CHECK = 7 /* MLA_CHECK=1 only: a seq_lens value is outside
-                                [0, max_seq_len], or a page-table entry that its sequence uses
-                                is outside [0, num_pages); nothing else was enqueued         */
+                                [0, max_seq_len], a page-table entry that its sequence uses
+                                is outside [0, num_pages), or (FP8 cache) the scale of a slot
+                                a sequence uses is not a positive normal power of two;
+                                nothing else was enqueued                                   */
 } mla_status_t;
 
 typedef struct {
@@ -144,10 +147,11 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
  *              FP8 E4M3 bytes (OCP format: 4 exponent bits, bias 7, 3 mantissa bits, no
  *              infinities, S.1111.111 = NaN) | k_R as d_rope bf16 values]
  *   kv_scales  fp32 [num_pages, 64]                      the scale of the token in each slot:
- *              c_KV[c] = value(byte c) * kv_scales[page][slot]. Scales are positive normal
- *              powers of two (exponent-only, as in the microscaling formats); any other
- *              positive normal value acts as the power of two of its binary exponent,
- *              2^floor(log2 s), its mantissa bits ignored.
+ *              c_KV[c] = value(byte c) * kv_scales[page][slot]. Precondition: the scale of
+ *              every slot a sequence uses is a positive normal power of two, 2^e with
+ *              -126 <= e <= 127 (exponent-only, as in the microscaling formats). Other values
+ *              are not reinterpreted: the result is then unspecified, and the MLA_CHECK mode
+ *              reports them (MLA_ERR_DEVICE_CHECK). Slots no sequence uses may hold anything.
  * Each dequantised c_KV element (an E4M3 value times a power of two) is a bf16 value, formed
  * exactly, and the decode then runs as in mla_decode: the result is that of mla_decode on the
  * bf16 cache holding those values. Slots at or past S_b (bytes and scales) are never read
@@ -197,11 +201,15 @@ mla_status_t mla_decode_out(const mla_dims_t* dims, int32_t hidden, const void* 
  *   page_table int32 [B, max_pages_per_seq], seq_lens int32 [B]: tokens already cached
  *   kv_pages   bf16 [num_pages, 64, d_latent + d_rope], written at the new tokens' slots only
  * seq_lens is not updated (the caller adds T after the call). A token whose position falls
- * outside its page-table row (p >= max_pages_per_seq * 64) is not written; page ids are
- * clamped into the pool. Sizes: hidden a multiple of 1024, d_latent and d_rope multiples of
- * 4, B*T at most 2^20. Same conventions as above otherwise (enqueued on
- * `stream`, no allocation, argument errors before anything is enqueued). The decode's q_rope
- * must be rotated with the same pairing and base.
+ * outside its page-table row (p >= max_pages_per_seq * 64), or whose page-table entry is not
+ * a pool page (outside [0, num_pages), e.g. -1 for a page not allocated yet), is not written:
+ * no other slot changes. With MLA_CHECK=1 the call first copies seq_lens and the page table to
+ * the host, synchronises the stream, and returns MLA_ERR_DEVICE_CHECK (writing nothing) when
+ * an S_b is outside [0, max_pages_per_seq * 64] or such an entry of a new token is outside
+ * the pool. Sizes: hidden a multiple of 1024, d_latent and d_rope multiples of 4, B*T at most
+ * 2^20. Same conventions as above otherwise (enqueued on `stream`, no allocation, argument
+ * errors before anything is enqueued). The decode's q_rope must be rotated with the same
+ * pairing and base.
  */
 typedef struct {
     int32_t batch;             /* B sequences                                               */

@@ -5,7 +5,6 @@ dtypes/shapes/devices, allocates outputs and workspace with torch, and passes ra
 pointers plus the current HIP stream. If the library is missing the calls raise.
 """
 import ctypes
-import math
 import os
 import re
 
@@ -135,6 +134,12 @@ def _stream(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _shape(t, name, want):
+    """Raise ValueError unless tensor t has exactly the shape `want` (a tuple of ints)."""
+    if tuple(t.shape) != tuple(want):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(want)))
+
+
 def _want(t, name, dtype, ndim, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -166,41 +171,55 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
     = [c_KV as FP8 e4m3 bytes | k_R bf16], and kv_scales fp32 [P,64] holds each token's c_KV
     scale.
     """
-    dev = q_nope.device
-    if dev.type != "cuda":
-        raise ValueError("mla decode runs on a HIP device; got %s" % dev)
     bf, i32 = torch.bfloat16, torch.int32
     nq = q_nope.dim() if isinstance(q_nope, torch.Tensor) else 3
     if nq not in (3, 4):
         raise ValueError("q_nope must be [B,H,d_n] or [B,T,H,d_n]")
+    dev = q_nope.device
+    # dtype, rank and layout of every tensor, then the sizes they must agree on (the library
+    # only sees pointers: a short tensor here would be read or written past its end on the
+    # device), then the device
     for t, n, dt, nd in ((q_nope, "q_nope", bf, nq), (q_rope, "q_rope", bf, nq),
                          (W_UK, "W_UK", bf, 3), (W_UV, "W_UV", bf, 3),
                          (kv_pages, "kv_pages", bf if kv_scales is None else torch.uint8, 3),
                          (page_table, "page_table", i32, 2),
                          (seq_lens, "seq_lens", i32, 1)):
-        _want(t, n, dt, nd, dev)
+        _want(t, n, dt, nd, t.device)
     dims = make_dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, max_seq_len,
                      softmax_scale, num_units)
     B, H, d_v = dims.batch, dims.num_heads, dims.d_v
+    d_n, d_c, d_R = dims.d_nope, dims.d_latent, dims.d_rope
     lead = (B,) if nq == 3 else (B, dims.q_len)
-    if q_rope.shape[:-1] != q_nope.shape[:-1]:
-        raise ValueError("q_rope %s does not match q_nope %s" % (tuple(q_rope.shape),
-                                                                 tuple(q_nope.shape)))
+    _shape(q_rope, "q_rope", lead + (H, d_R))
+    _shape(W_UK, "W_UK", (H, d_n, d_c))
+    _shape(W_UV, "W_UV", (H, d_c, d_v))
+    row = d_c + d_R if kv_scales is None else d_c + 2 * d_R
+    _shape(kv_pages, "kv_pages", (kv_pages.shape[0], kv_pages.shape[1], row))
+    _shape(page_table, "page_table", (B, page_table.shape[1]))
+    _shape(seq_lens, "seq_lens", (B,))
+    if out is not None:
+        _want(out, "out", bf, nq, out.device)
+        _shape(out, "out", lead + (H, d_v))
+    if lse is not None:
+        _want(lse, "lse", torch.float32, nq - 1, lse.device)
+        _shape(lse, "lse", lead + (H,))
+    if kv_scales is not None:
+        _want(kv_scales, "kv_scales", torch.float32, 2, kv_scales.device)
+        _shape(kv_scales, "kv_scales", tuple(kv_pages.shape[:2]))
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or
+                                  not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor")
+    if dev.type != "cuda":
+        raise ValueError("mla decode runs on a HIP device; got %s" % dev)
+    for t, n in ((q_rope, "q_rope"), (W_UK, "W_UK"), (W_UV, "W_UV"), (kv_pages, "kv_pages"),
+                 (page_table, "page_table"), (seq_lens, "seq_lens"), (out, "out"), (lse, "lse"),
+                 (kv_scales, "kv_scales"), (workspace, "workspace")):
+        if t is not None and t.device != dev:
+            raise ValueError("%s is on %s, expected %s" % (n, t.device, dev))
     if out is None:
         out = torch.empty(lead + (H, d_v), dtype=bf, device=dev)
-    else:
-        _want(out, "out", bf, nq, dev)
     if return_lse and lse is None:
         lse = torch.empty(lead + (H,), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _want(lse, "lse", torch.float32, nq - 1, dev)
-    if kv_scales is not None:
-        _want(kv_scales, "kv_scales", torch.float32, 2, dev)
-        if tuple(kv_scales.shape) != tuple(kv_pages.shape[:2]):
-            raise ValueError("kv_scales %s must be [pages, 64] like kv_pages %s"
-                             % (tuple(kv_scales.shape), tuple(kv_pages.shape)))
-        if kv_pages.shape[2] != dims.d_latent + 2 * dims.d_rope:
-            raise ValueError("an FP8 token row is d_c + 2*d_R bytes")
     nbytes = workspace_bytes(dims)
     if nbytes == 0:
         _check(lib().mla_decode(ctypes.byref(dims), *([ctypes.c_void_p(0)] * 10), 0,
@@ -209,7 +228,7 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     args = (ctypes.byref(dims), _ptr(q_nope), _ptr(q_rope), _ptr(W_UK), _ptr(W_UV),
             _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
-            _ptr(workspace), workspace.numel(), _stream(stream, dev))
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
     ev = None
     if kernel_events is not None:
         if len(kernel_events) != 6:
@@ -231,42 +250,55 @@ def decode_out(q_nope, q_rope, W_UK, W_UVO, kv_pages, page_table, seq_lens, out=
     """The decode with the merged output projection (mla_decode_out): W_UVO bf16
     [hidden, H*d_c] replaces W_UV; returns out bf16 [B, hidden] ([B, T, hidden] for 4-d
     queries), and lse fp32 [B, H] ([B, T, H]) when return_lse."""
-    dev = q_nope.device
-    if dev.type != "cuda":
-        raise ValueError("mla decode runs on a HIP device; got %s" % dev)
     bf, i32 = torch.bfloat16, torch.int32
     nq = q_nope.dim() if isinstance(q_nope, torch.Tensor) else 3
     if nq not in (3, 4):
         raise ValueError("q_nope must be [B,H,d_n] or [B,T,H,d_n]")
+    dev = q_nope.device
     for t, n, dt, nd in ((q_nope, "q_nope", bf, nq), (q_rope, "q_rope", bf, nq),
                          (W_UK, "W_UK", bf, 3), (W_UVO, "W_UVO", bf, 2),
                          (kv_pages, "kv_pages", bf, 3), (page_table, "page_table", i32, 2),
                          (seq_lens, "seq_lens", i32, 1)):
-        _want(t, n, dt, nd, dev)
-    H, d_c = W_UK.shape[0], W_UK.shape[2]
+        _want(t, n, dt, nd, t.device)
+    H, d_n, d_c = W_UK.shape
     hidden = W_UVO.shape[0]
     if W_UVO.shape[1] != H * d_c:
         raise ValueError("W_UVO must be [hidden, H*d_c] = [*, %d]" % (H * d_c))
     # d_v does not enter this call; the dims carry the width of the supported shapes
     dims = make_dims(q_nope, q_rope, W_UK, torch.empty((H, d_c, 128), dtype=bf, device="meta"),
                      kv_pages, page_table, max_seq_len, softmax_scale, num_units)
-    B = dims.batch
+    B, d_R = dims.batch, dims.d_rope
     lead = (B,) if nq == 3 else (B, dims.q_len)
+    _shape(q_nope, "q_nope", lead + (H, d_n))
+    _shape(q_rope, "q_rope", lead + (H, d_R))
+    _shape(kv_pages, "kv_pages", (kv_pages.shape[0], kv_pages.shape[1], d_c + d_R))
+    _shape(page_table, "page_table", (B, page_table.shape[1]))
+    _shape(seq_lens, "seq_lens", (B,))
+    if out is not None:
+        _want(out, "out", bf, nq - 1, out.device)
+        _shape(out, "out", lead + (hidden,))
+    if lse is not None:
+        _want(lse, "lse", torch.float32, nq - 1, lse.device)
+        _shape(lse, "lse", lead + (H,))
+    if dev.type != "cuda":
+        raise ValueError("mla decode runs on a HIP device; got %s" % dev)
+    for t, n in ((q_rope, "q_rope"), (W_UK, "W_UK"), (W_UVO, "W_UVO"), (kv_pages, "kv_pages"),
+                 (page_table, "page_table"), (seq_lens, "seq_lens"), (out, "out"), (lse, "lse"),
+                 (workspace, "workspace")):
+        if t is not None and t.device != dev:
+            raise ValueError("%s is on %s, expected %s" % (n, t.device, dev))
     if out is None:
         out = torch.empty(lead + (hidden,), dtype=bf, device=dev)
-    else:
-        _want(out, "out", bf, nq - 1, dev)
     if return_lse and lse is None:
         lse = torch.empty(lead + (H,), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _want(lse, "lse", torch.float32, nq - 1, dev)
     nbytes = workspace_bytes(dims)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _check(lib().mla_decode_out(ctypes.byref(dims), hidden, _ptr(q_nope), _ptr(q_rope),
                                 _ptr(W_UK), _ptr(W_UVO), _ptr(kv_pages), _ptr(page_table),
                                 _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace),
-                                workspace.numel(), _stream(stream, dev)))
+                                workspace.numel() * workspace.element_size(),
+                                _stream(stream, dev)))
     return (out, lse) if return_lse else out
 
 
@@ -278,22 +310,30 @@ def cache_append(x, W_DKV, W_KR, kv_pages, page_table, seq_lens, rope_base=10000
     [d_R,hidden], kv_pages bf16 [P,64,d_c+d_R], page_table int32 [B,max_pages], seq_lens int32
     [B] (tokens already cached; token i of sequence b goes to position seq_lens[b] + i).
     """
-    dev = kv_pages.device
     bf = torch.bfloat16
-    _want(x, "x", bf, x.dim() if x.dim() in (2, 3) else 3, dev)
-    _want(W_DKV, "W_DKV", bf, 2, dev)
-    _want(W_KR, "W_KR", bf, 2, dev)
+    dev = kv_pages.device
+    _want(x, "x", bf, x.dim() if x.dim() in (2, 3) else 3, x.device)
+    _want(W_DKV, "W_DKV", bf, 2, W_DKV.device)
+    _want(W_KR, "W_KR", bf, 2, W_KR.device)
     _want(kv_pages, "kv_pages", bf, 3, dev)
-    _want(page_table, "page_table", torch.int32, 2, dev)
-    _want(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _want(page_table, "page_table", torch.int32, 2, page_table.device)
+    _want(seq_lens, "seq_lens", torch.int32, 1, seq_lens.device)
     d = AppendDims()
     d.batch = x.shape[0]
     d.q_len = x.shape[1] if x.dim() == 3 else 1
     d.hidden = x.shape[-1]
     d.d_latent, d.d_rope = W_DKV.shape[0], W_KR.shape[0]
-    if W_DKV.shape[1] != d.hidden or W_KR.shape[1] != d.hidden or \
-            kv_pages.shape[2] != d.d_latent + d.d_rope or page_table.shape[0] != d.batch:
-        raise ValueError("inconsistent shapes")
+    _shape(W_DKV, "W_DKV", (d.d_latent, d.hidden))
+    _shape(W_KR, "W_KR", (d.d_rope, d.hidden))
+    _shape(kv_pages, "kv_pages", (kv_pages.shape[0], kv_pages.shape[1], d.d_latent + d.d_rope))
+    _shape(page_table, "page_table", (d.batch, page_table.shape[1]))
+    _shape(seq_lens, "seq_lens", (d.batch,))
+    if dev.type != "cuda":
+        raise ValueError("the cache append runs on a HIP device; got %s" % dev)
+    for t, n in ((x, "x"), (W_DKV, "W_DKV"), (W_KR, "W_KR"), (page_table, "page_table"),
+                 (seq_lens, "seq_lens")):
+        if t.device != dev:
+            raise ValueError("%s is on %s, expected %s" % (n, t.device, dev))
     d.page_size = kv_pages.shape[1]
     d.max_pages_per_seq = page_table.shape[1]
     d.num_pages = kv_pages.shape[0]
@@ -311,6 +351,9 @@ def gather_pages(kv_pages, page_table, seq_lens, d_latent, max_seq_len=None, str
     _want(kv_pages, "kv_pages", torch.bfloat16, 3, dev)
     _want(page_table, "page_table", torch.int32, 2, dev)
     _want(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _shape(seq_lens, "seq_lens", (page_table.shape[0],))
+    if not 0 < int(d_latent) < kv_pages.shape[2]:
+        raise ValueError("d_latent must lie inside the token row (%d)" % kv_pages.shape[2])
     d = Dims()
     d.batch = page_table.shape[0]
     d.d_latent = int(d_latent)
@@ -324,7 +367,3 @@ def gather_pages(kv_pages, page_table, seq_lens, d_latent, max_seq_len=None, str
     _check(lib().mla_gather_pages(ctypes.byref(d), _ptr(kv_pages), _ptr(page_table),
                                   _ptr(seq_lens), _ptr(dst), _stream(stream, dev)))
     return dst
-
-
-def default_scale(d_nope, d_rope):
-    return 1.0 / math.sqrt(d_nope + d_rope)

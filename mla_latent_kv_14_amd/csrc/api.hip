@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <vector>
+
 #include "mla_decode.h"
 #include "device.h"
 #include "kernels.h"
@@ -161,7 +163,7 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
     int* flag = (int*)(ws + L.q_abs);
     int host_flag = 0;
     st = hip_status(mla::launch_check(seq_lens, page_table, B, mp, dims->num_pages,
-                                      max_len(dims), flag, hs));
+                                      max_len(dims), kv_scales, flag, hs));
     if (st != MLA_OK) return st;
     st = hip_status(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, hs));
     if (st != MLA_OK) return st;
@@ -279,11 +281,34 @@ mla_status_t mla_cache_append(const mla_append_dims_t* d, const void* x, const v
   if (!aligned16(x) || !aligned16(W_DKV) || !aligned16(W_KR) || !aligned16(page_table) ||
       !aligned16(seq_lens) || !aligned16(kv_pages))
     return MLA_ERR_MISALIGNED;
+  const hipStream_t hs = (hipStream_t)stream;
+  if (check_mode()) {
+    // validate on the host (the append takes no workspace for a device flag): every S_b in
+    // [0, max_pages_per_seq * 64], and the page-table entry of every new token that falls
+    // inside its row in [0, num_pages)
+    const int B = d->batch, mp = d->max_pages_per_seq;
+    std::vector<int32_t> lens(B), table((size_t)B * mp);
+    mla_status_t st = hip_status(hipMemcpyAsync(lens.data(), seq_lens, sizeof(int32_t) * B,
+                                                hipMemcpyDeviceToHost, hs));
+    if (st == MLA_OK)
+      st = hip_status(hipMemcpyAsync(table.data(), page_table, sizeof(int32_t) * table.size(),
+                                     hipMemcpyDeviceToHost, hs));
+    if (st == MLA_OK) st = hip_status(hipStreamSynchronize(hs));
+    if (st != MLA_OK) return st;
+    for (int b = 0; b < B; ++b) {
+      if (lens[b] < 0 || (int64_t)lens[b] > (int64_t)mp * mla::kPage) return MLA_ERR_DEVICE_CHECK;
+      for (int i = 0; i < T; ++i) {
+        const int64_t pos = (int64_t)lens[b] + i;
+        if (pos >= (int64_t)mp * mla::kPage) break;
+        const int32_t page = table[(size_t)b * mp + pos / mla::kPage];
+        if (page < 0 || page >= d->num_pages) return MLA_ERR_DEVICE_CHECK;
+      }
+    }
+  }
   const double base = d->rope_base > 0.f ? (double)d->rope_base : 10000.0;
   return hip_status(mla::launch_append(x, W_DKV, W_KR, page_table, seq_lens, kv_pages, d->batch,
                                        T, d->hidden, d->d_latent, d->d_rope,
-                                       d->max_pages_per_seq, d->num_pages, base,
-                                       (hipStream_t)stream));
+                                       d->max_pages_per_seq, d->num_pages, base, hs));
 }
 
 const char* mla_status_str(mla_status_t s) {

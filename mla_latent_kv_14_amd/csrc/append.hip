@@ -116,9 +116,13 @@ append_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W_DKV
           v[e + 2] = x1 * sn + x2 * cs;
         }
       }
-      if (r < R && pos < max_pages * kPage) {
-        int page = page_table[(size_t)b * max_pages + pos / kPage];
-        page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+      // a token whose position is past its page-table row, or whose page-table entry names
+      // no pool page (say -1, a page not allocated yet), is not written: a clamped write would
+      // overwrite another sequence's cached token
+      const int page = r < R && pos < max_pages * kPage
+                           ? page_table[(size_t)b * max_pages + pos / kPage]
+                           : -1;
+      if (page >= 0 && page < num_pages) {
         uint16_t* dst = kv + ((size_t)page * kPage + pos % kPage) * W;
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[column(e)] = bf16_bits((__bf16)v[e]);

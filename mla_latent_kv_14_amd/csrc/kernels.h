@@ -63,9 +63,11 @@ hipError_t launch_combine_latent(int shape, const void* part_o, const float* par
 hipError_t launch_linear(const void* x, const void* W, void* out, int R, int K, int N,
                          const Launch& L);
 
-// Sets bits of *flag (cleared first) for out-of-range lengths (1) or used page ids (2).
+// Sets bits of *flag (cleared first) for out-of-range lengths (1), used page ids (2) or, with
+// an FP8 cache (kv_scales not NULL), used scales that are not positive normal powers of two (4).
 hipError_t launch_check(const int32_t* seq_lens, const int32_t* page_table, int B, int max_pages,
-                        int num_pages, int max_len, int* flag, hipStream_t stream);
+                        int num_pages, int max_len, const float* kv_scales, int* flag,
+                        hipStream_t stream);
 
 // Writes [c_KV | RoPE(k_R)] of B*T new tokens (token i of sequence b at position
 // seq_lens[b] + i). Needs d_c % 4 == 0, d_R % 4 == 0 and hidden % 1024 == 0.

@@ -241,26 +241,34 @@ def fp8_e4m3_value(code):
     return np.where((e == 15) & (c & 0x7 == 7), np.nan, v)
 
 
-def scale_pow2(scales):
-    """The power of two a per-token scale stands for: scales are powers of two (exponent-only,
-    as in the microscaling formats); a positive value that is not one counts as the power of two
-    of its binary exponent, 2^floor(log2 s). NaN stays NaN."""
+def check_scales(scales):
+    """The per-token scales of an FP8 cache as fp64, after checking the format's contract:
+    every scale is a positive normal power of two (exponent-only, as in the microscaling
+    formats), i.e. 2^e with -126 <= e <= 127. NaN is accepted (a slot no sequence uses may
+    hold anything); any other value raises ValueError."""
     s = np.asarray(scales, dtype=np.float64)
+    ok = np.isnan(s)
     with np.errstate(invalid="ignore"):
-        m, e = np.frexp(s)
-    return np.where(np.isnan(s), np.nan, np.ldexp(1.0, e - 1))
+        m, e = np.frexp(np.where(ok, 1.0, s))
+    pow2 = (m == 0.5) & (e - 1 >= -126) & (e - 1 <= 127) & (s > 0)
+    if not np.all(ok | pow2):
+        bad = s[~(ok | pow2)]
+        raise ValueError("FP8 cache scales must be positive normal powers of two; got %r"
+                         % (bad[:4].tolist(),))
+    return s
 
 
 def dequant_fp8_cache(kv8, scales, d_c):
     """The bf16 cache that an FP8 cache stands for: token row [c_KV bytes (d_c) | k_R bf16
-    (2*d_R bytes)] with a positive fp32 power-of-two scale per token slot (scale_pow2);
+    (2*d_R bytes)] with a positive normal fp32 power-of-two scale per token slot
+    (check_scales);
     c_KV[c] = value(byte c) * scale, k_R copied. Returns uint16 bf16 bits [P, 64, d_c + d_R].
     Every product is a bf16 value (an E4M3 value times a power of two, in range); the function
     checks that rather than assume it."""
     kv8 = np.ascontiguousarray(kv8, dtype=np.uint8)
     P, ps, w8 = kv8.shape
     d_R = (w8 - d_c) // 2
-    v = fp8_e4m3_value(kv8[:, :, :d_c]) * scale_pow2(scales)[:, :, None]
+    v = fp8_e4m3_value(kv8[:, :, :d_c]) * check_scales(scales)[:, :, None]
     f = v.astype(np.float32)
     ok = np.isnan(v) | (f.astype(np.float64) == v)
     bits = f.view(np.uint32)

@@ -334,8 +334,17 @@ int oracle_gather_pages(int B, int d_c, int d_R, int page_size, int max_pages,
         if (seq_lens[b] < 0 || seq_lens[b] > S_max) return -2;
         for (int t = 0; t < S_max; ++t) {
             uint16_t *d = dst + ((size_t)b * S_max + t) * w;
-            if (t < seq_lens[b])
-                memcpy(d, token(&D, kv, page_table, b, t), sizeof(uint16_t) * (size_t)w);
+            int live = t < seq_lens[b];
+#if ORACLE_MUTANT == 9 /* zero fill starts one row late */
+            live = t < seq_lens[b] + 1 && t < S_max;
+#endif
+            int copy = w;
+#if ORACLE_MUTANT == 10 /* the RoPE part of each row is not copied */
+            copy = d_c;
+            memset(d, 0, sizeof(uint16_t) * (size_t)w);
+#endif
+            if (live)
+                memcpy(d, token(&D, kv, page_table, b, t), sizeof(uint16_t) * (size_t)copy);
             else
                 memset(d, 0, sizeof(uint16_t) * (size_t)w);
         }

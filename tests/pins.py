@@ -20,6 +20,10 @@ Pins, and the passage or fact each one rests on:
                          sit in the pool (bhfrc.com/news/60867 S3 paged layout).
   split_combine          cutting the tokens into ranges and merging by log-sum-exp gives the
                          single-pass result.
+  gather_numpy           the logical copy of the paged cache equals an independent numpy
+                         gather (page_table[b, t // page_size], slot t % page_size, zero past
+                         S_b) byte for byte, on a shuffled pool with NaN-poisoned unused slots
+                         and pages (bhfrc.com/news/60867 S3 paged layout).
   tokens_causal_sdpa     several query tokens per sequence (the sequence's newest tokens):
                          torch's scaled_dot_product_attention in float64 with an explicit
                          causal mask (query token i of T sees tokens 0 .. S - T + i) on the
@@ -245,5 +249,30 @@ def tokens_causal_sdpa(O):
     assert np.array_equal(o1, o2[:, 0]) and np.array_equal(l1, l2[:, 0])
 
 
+def gather_numpy(O):
+    for seed, (seq, kw) in enumerate([([37, 64, 100], {}), ([1, 4, 9, 130], dict(d_c=16, d_R=4)),
+                                      ([63, 65, 0, 128], {})]):
+        B = len(seq)
+        d = dict(TINY)
+        d.update(kw)
+        inp = W.make_inputs(B, d["H"], d["d_n"], d["d_c"], d["d_R"], d["d_v"], seq, 1300 + seed,
+                            layout="shuffled", poison=True, page_size=4)
+        kv = W.u16(inp["kv_pages"])
+        pt = inp["page_table"].numpy().astype(np.int64)
+        sl = inp["seq_lens"].numpy().astype(np.int64)
+        P = inp["page_size"]
+        S_max = pt.shape[1] * P
+        # independent gather: numpy advanced indexing over every (b, t), then a zero mask
+        t = np.arange(S_max)
+        pages = pt[:, t // P]                                    # [B, S_max]
+        ref = kv[pages, (t % P)[None, :]]                        # [B, S_max, d_c + d_R]
+        ref = np.where((t[None, :] < sl[:, None])[:, :, None], ref, np.uint16(0))
+        got = O.gather_pages(kv, inp["page_table"].numpy(), inp["seq_lens"].numpy(), S_max,
+                             d["d_c"])
+        assert got.dtype == np.uint16 and got.shape == ref.shape
+        assert np.array_equal(got, ref), ("gather", seed)
+
+
 ALL = [naive_equals_absorbed, sdpa_library, rows_sum_to_one, single_token, zero_query,
-       identical_tokens, dominant_rope, permutation, split_combine, tokens_causal_sdpa]
+       identical_tokens, dominant_rope, permutation, split_combine, gather_numpy,
+       tokens_causal_sdpa]

@@ -226,3 +226,58 @@ def test_decode_fp8_rejects_before_enqueueing():
     bad = m2_dims()
     bad.batch = 0
     assert call(bad, _al(6)) == STATUS_CODE["MLA_ERR_BAD_DIMS"]
+
+
+def _small_decode_args(B=2, T=None, H=32, d_n=120, d_c=64, d_R=8, d_v=128, P=4, mp=2):
+    import torch
+    bf = torch.bfloat16
+    lead = (B,) if T is None else (B, T)
+    return dict(q_nope=torch.zeros(lead + (H, d_n), dtype=bf),
+                q_rope=torch.zeros(lead + (H, d_R), dtype=bf),
+                W_UK=torch.zeros(H, d_n, d_c, dtype=bf), W_UV=torch.zeros(H, d_c, d_v, dtype=bf),
+                kv_pages=torch.zeros(P, 64, d_c + d_R, dtype=bf),
+                page_table=torch.zeros(B, mp, dtype=torch.int32),
+                seq_lens=torch.ones(B, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("W_UK", (16, 120, 64)), ("W_UK", (32, 128, 64)), ("W_UV", (32, 32, 128)),
+    ("kv_pages", (4, 64, 64)), ("page_table", (1, 2)), ("seq_lens", (3,)),
+    ("q_rope", (2, 16, 8)), ("out", (2, 32, 64)), ("lse", (1, 32))])
+def test_binding_rejects_inconsistent_sizes(name, bad):
+    # the C ABI sees only pointers, so the binding is the one place where sizes are checked
+    # against each other: every mismatch raises before anything reaches the library (the
+    # tensors live on the CPU, so a call that got past the checks would fail differently)
+    import torch
+    a = _small_decode_args()
+    kw = {}
+    if name in ("out", "lse"):
+        kw[name] = torch.zeros(bad, dtype=torch.bfloat16 if name == "out" else torch.float32)
+    else:
+        a[name] = torch.zeros(bad, dtype=a[name].dtype)
+    with pytest.raises(ValueError, match="shape"):
+        M.decode(*a.values(), **kw)
+
+
+def test_binding_rejects_inconsistent_sizes_other_calls():
+    import torch
+    bf = torch.bfloat16
+    a = _small_decode_args()
+    W_UVO = torch.zeros(256, 32 * 64, dtype=bf)
+    args = [a["q_nope"], a["q_rope"], a["W_UK"], W_UVO, a["kv_pages"], a["page_table"]]
+    with pytest.raises(ValueError, match="shape"):   # out of the wrong width
+        M.decode_out(*args, a["seq_lens"], out=torch.zeros(2, 128, dtype=bf))
+    with pytest.raises(ValueError, match="shape"):   # one length too few
+        M.decode_out(*args, a["seq_lens"][:1])
+    with pytest.raises(ValueError):                  # W_UVO not [hidden, H*d_c]
+        M.decode_out(a["q_nope"], a["q_rope"], a["W_UK"], torch.zeros(256, 100, dtype=bf),
+                     a["kv_pages"], a["page_table"], a["seq_lens"])
+    x = torch.zeros(2, 1, 1024, dtype=bf)
+    Wd, Wr = torch.zeros(64, 1024, dtype=bf), torch.zeros(8, 1024, dtype=bf)
+    with pytest.raises(ValueError, match="shape"):   # seq_lens of another batch
+        M.cache_append(x, Wd, Wr, a["kv_pages"], a["page_table"], a["seq_lens"][:1])
+    with pytest.raises(ValueError, match="shape"):   # W_KR of another hidden width
+        M.cache_append(x, Wd, torch.zeros(8, 512, dtype=bf), a["kv_pages"], a["page_table"],
+                       a["seq_lens"])
+    with pytest.raises(ValueError, match="shape"):
+        M.gather_pages(a["kv_pages"], a["page_table"], a["seq_lens"][:1], 64)

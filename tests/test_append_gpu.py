@@ -92,3 +92,64 @@ def test_decode_reads_appended_tokens(M):
     inp["kv_pages"] = kv.cpu()
     inp["seq_lens"] = before + 1
     check_against_oracle(M, inp, label="decode after append")
+
+
+def test_unallocated_page_entry_is_not_written(M):
+    # a new token whose page-table entry names no pool page (-1: not allocated yet, or past
+    # the pool) is skipped: every other slot of the pool stays bit for bit as it was, and the
+    # tokens with valid entries are written as usual
+    inp, x, Wd, Wr, before = _case("mha2mla", [62, 130, 5], 3, 45)
+    pt = inp["page_table"].clone()
+    pt[0, 1] = -1                         # page of position 64 (sequence 0's third new token)
+    pt[1, 2] = inp["kv_pages"].shape[0]   # past the pool: positions 128.. of sequence 1
+    say("append with unallocated page entries")
+    kv0 = inp["kv_pages"].clone()
+    kv = inp["kv_pages"].cuda()
+    M.cache_append(x.cuda(), Wd.cuda(), Wr.cuda(), kv, pt.cuda(), before.cuda())
+    torch.cuda.synchronize()
+    got = kv.cpu()
+    rows, where = oracle.cache_append(W.u16(x), W.u16(Wd), W.u16(Wr), pt.numpy(),
+                                      before.numpy())
+    written = np.zeros(got.shape[:2], dtype=bool)
+    skipped = 0
+    for b in range(3):
+        for i in range(3):
+            page, slot = where[b, i]
+            if page < 0 or page >= got.shape[0]:
+                skipped += 1
+                continue
+            ref = rows[b, i]
+            err = np.abs(got[page, slot].double().numpy() - ref)
+            assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5), (b, i, float(err.max()))
+            written[page, slot] = True
+    assert skipped == 4  # sequence 0: position 64; sequence 1: positions 130, 131, 132
+    same = got.view(torch.int16).numpy()[~written] == kv0.view(torch.int16).numpy()[~written]
+    assert np.all(same), "a slot outside the valid new tokens changed"
+
+
+def test_check_mode_refuses_unallocated_page_entry(M):
+    import os
+    inp, x, Wd, Wr, before = _case("mha2mla", [62, 10], 3, 46)
+    pt = inp["page_table"].clone()
+    pt[0, 1] = -1
+    kv0 = inp["kv_pages"].clone()
+    kv = inp["kv_pages"].cuda()
+    old = os.environ.get("MLA_CHECK")
+    os.environ["MLA_CHECK"] = "1"
+    try:
+        say("append check mode: -1 entry")
+        with pytest.raises(M.MlaError) as e:
+            M.cache_append(x.cuda(), Wd.cuda(), Wr.cuda(), kv, pt.cuda(), before.cuda())
+        assert e.value.code == 7  # MLA_ERR_DEVICE_CHECK
+        torch.cuda.synchronize()
+        assert torch.equal(kv.cpu().view(torch.int16), kv0.view(torch.int16))  # nothing written
+        # valid entries pass the check and are appended
+        M.cache_append(x.cuda(), Wd.cuda(), Wr.cuda(), kv, inp["page_table"].cuda(),
+                       before.cuda())
+        torch.cuda.synchronize()
+        assert not torch.equal(kv.cpu().view(torch.int16), kv0.view(torch.int16))
+    finally:
+        if old is None:
+            del os.environ["MLA_CHECK"]
+        else:
+            os.environ["MLA_CHECK"] = old

@@ -103,19 +103,40 @@ def test_fp8_equals_bf16_on_the_same_values(M):
     assert torch.equal(a, b)
 
 
-def test_fp8_scale_mantissa_is_ignored(M):
-    # a scale that is not a power of two acts as the power of two of its exponent: scaling
-    # each token's scale by a factor in [1, 2) leaves the result bit for bit the same
+def test_fp8_check_mode_flags_scales_off_contract(M):
+    # MLA_CHECK=1 inspects the scale of every slot a sequence uses: a scale that is not a
+    # positive normal power of two there is reported (MLA_ERR_DEVICE_CHECK) and nothing is
+    # decoded; the same value in a slot past the sequence's end is ignored
+    import os
     inp = _inp([300, 64, 129], 51)
     kv8, sc = W.fp8_cache(inp, seed=6)
-    g = torch.Generator().manual_seed(7)
-    sc2 = sc * (1.0 + torch.rand(sc.shape, generator=g) * 0.999)
-    assert not torch.equal(sc, sc2)
     d = to_dev(inp)
-    a, b = (M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8.cuda(),
-                     d["page_table"], d["seq_lens"], kv_scales=s.cuda()) for s in (sc, sc2))
-    torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    pt = inp["page_table"].numpy()
+    kv8 = kv8.cuda()
+
+    def run(scales):
+        o = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8, d["page_table"],
+                     d["seq_lens"], kv_scales=scales.cuda())
+        torch.cuda.synchronize()
+        return o
+
+    ref = run(sc)
+    os.environ["MLA_CHECK"] = "1"
+    try:
+        assert torch.equal(run(sc), ref)
+        for b, tt, bad in ((0, 17, 0.3), (0, 299, 1.5), (1, 0, 0.0), (2, 128, -0.25)):
+            s2 = sc.clone()
+            s2[pt[b, tt // 64], tt % 64] = bad
+            say("fp8 check: bad scale %r at sequence %d token %d" % (bad, b, tt))
+            with pytest.raises(M.MlaError) as e:
+                run(s2)
+            assert e.value.code == 7  # MLA_ERR_DEVICE_CHECK
+        # past the end of sequence 2 (129 tokens): slot 129 of its page table row
+        s2 = sc.clone()
+        s2[pt[2, 129 // 64], 129 % 64] = 0.3
+        assert torch.equal(run(s2), ref)
+    finally:
+        del os.environ["MLA_CHECK"]
 
 
 def test_fp8_workload_full_size(M):

@@ -60,18 +60,23 @@ def test_dequant_hand_rows():
     assert out.shape == (1, 64, d_c + d_R)
     assert out[0, 0].tolist() == [0x3E80, 0xBE80, 0x3A00, 0x42E0, 0x3F80, 0xC000]
     assert np.all(out[0, 1:] == 0)
-    # a scale that is not a power of two counts as the power of two of its exponent
-    scales[0, 0] = 0.3
-    assert oracle.dequant_fp8_cache(kv8, scales, d_c)[0, 0].tolist() == out[0, 0].tolist()
-    scales[0, 0] = 1.99
-    assert oracle.dequant_fp8_cache(kv8, scales, d_c)[0, 0, :2].tolist() == [0x3F80, 0xBF80]
+    # a scale outside the contract is refused, not reinterpreted
+    for bad in (0.3, 1.99, 0.0, -0.25, 3.0):
+        scales[0, 0] = bad
+        with pytest.raises(ValueError):
+            oracle.dequant_fp8_cache(kv8, scales, d_c)
 
 
-def test_scale_pow2():
-    s = np.array([1.0, 0.25, 0.3, 1.5, 3.0, 2.0 ** -20, 2.0 ** 20 * 1.7, np.nan])
-    want = [1.0, 0.25, 0.25, 1.0, 2.0, 2.0 ** -20, 2.0 ** 20]
-    got = oracle.scale_pow2(s)
-    assert got[:-1].tolist() == want and np.isnan(got[-1])
+def test_scale_contract():
+    # positive normal powers of two (2^-126 .. 2^127) and NaN (unused slots) are accepted
+    good = np.array([1.0, 0.25, 2.0 ** -126, 2.0 ** 127, 2.0 ** -20, np.nan])
+    got = oracle.check_scales(good)
+    assert got[:-1].tolist() == good[:-1].tolist() and np.isnan(got[-1])
+    # anything else is refused: mantissa bits, zero, negative, subnormal, infinity
+    for bad in (0.3, 1.5, 3.0, 2.0 ** 20 * 1.7, 0.0, -1.0, -2.0, 2.0 ** -127, 2.0 ** -140,
+                np.inf):
+        with pytest.raises(ValueError):
+            oracle.check_scales(np.array([1.0, bad]))
 
 
 def test_fp8_cache_round_trip():

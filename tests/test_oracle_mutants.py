@@ -2,7 +2,8 @@
 
 The mistakes are the plausible ones for this method: a dropped RoPE term, a transposed W_UK,
 the wrong softmax scale, the page table ignored, the last token dropped, the wrong head's
-W_UV, a missing log in the log-sum-exp and the wrong head's RoPE query.
+W_UV, a missing log in the log-sum-exp, the wrong head's RoPE query, and in the page gather
+a zero fill that starts one row late or rows copied without their RoPE part.
 """
 import os
 import tempfile
@@ -15,7 +16,8 @@ from tests import pins
 
 MUTANTS = {1: "rope dropped", 2: "W_UK transposed", 3: "scale 1/sqrt(d_n)",
            4: "page table ignored", 5: "last token dropped", 6: "W_UV of head 0",
-           7: "lse without log", 8: "q_rope of head 0"}
+           7: "lse without log", 8: "q_rope of head 0", 9: "gather zero fill one row late",
+           10: "gather drops k_R"}
 
 
 @pytest.mark.parametrize("k", sorted(MUTANTS), ids=[MUTANTS[k] for k in sorted(MUTANTS)])
