@@ -124,6 +124,27 @@ mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* 
                         float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same operation, arguments and
+ * results, without the workspace. Its scratch is an array built into the library, one per
+ * GPU, of MLA_NOALLOC_SCRATCH_BYTES; each GPU that calls it holds that memory until the
+ * process ends. The call allocates nothing and calls no allocating routine; its first call on
+ * a device looks the array's address up once (hipGetSymbolAddress).
+ *   - Uses the array of the current device; `stream` must belong to that device.
+ *   - Returns MLA_ERR_WORKSPACE when the dims need more scratch than the array holds
+ *     (mla_decode_workspace_bytes(dims) > MLA_NOALLOC_SCRATCH_BYTES), before enqueueing.
+ *   - Every call on a GPU shares that GPU's array, which keeps the last call's contents:
+ *     calls that overlap on one GPU (on different streams, or from several threads without
+ *     ordering) race and give wrong results. Order them on one stream.
+ * Everything else (dims, layouts, MLA_CHECK, errors) is as for mla_decode.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+mla_status_t mla_decode_noalloc(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                                const void* W_UK, const void* W_UV, const void* kv_pages,
+                                const int32_t* page_table, const int32_t* seq_lens, void* out,
+                                float* lse_out, void* stream);
+
+/*
  * mla_decode with kernel timing: identical work and results, and, when stage_events is not
  * NULL, binds six caller-owned events (hipEvent_t, each may be NULL) to the kernels it enqueues
  * on `stream`: stage_events[2k] to the start and stage_events[2k+1] to the end of kernel k's

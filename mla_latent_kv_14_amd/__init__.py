@@ -3,9 +3,10 @@
 The compute path is libmla_decode.so (hand-written HIP kernels behind a C ABI, see
 include/mla_decode.h); this package is its thin Python binding.
 """
-from .binding import (AppendDims, Dims, MlaError, STATUS, cache_append, decode, decode_out,
-                      gather_pages, header_symbols, lib, make_dims, workspace_bytes)
+from .binding import (NOALLOC_SCRATCH_BYTES, AppendDims, Dims, MlaError, STATUS, cache_append,
+                      decode, decode_out, gather_pages, header_symbols, lib, make_dims,
+                      workspace_bytes)
 
-__all__ = ["AppendDims", "Dims", "MlaError", "STATUS", "cache_append", "decode", "decode_out",
+__all__ = ["NOALLOC_SCRATCH_BYTES", "AppendDims", "Dims", "MlaError", "STATUS", "cache_append", "decode", "decode_out",
            "gather_pages",
            "header_symbols", "lib", "make_dims", "workspace_bytes"]

@@ -18,6 +18,9 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL_ARG", 2: "MLA_ERR_BAD_DIMS", 3: "MLA_ERR
           4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_UNSUPPORTED", 6: "MLA_ERR_HIP",
           7: "MLA_ERR_DEVICE_CHECK"}
 STATUS_CODE = {v: k for k, v in STATUS.items()}
+# size of the scratch array built into the library for mla_decode_noalloc (the header's
+# MLA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 48 << 20
 
 
 class Dims(ctypes.Structure):
@@ -63,6 +66,8 @@ def lib():
         L.mla_decode_workspace_bytes.argtypes = [dp]
         L.mla_decode.restype = c_int
         L.mla_decode.argtypes = [dp] + [vp] * 10 + [sz, vp]
+        L.mla_decode_noalloc.restype = c_int
+        L.mla_decode_noalloc.argtypes = [dp] + [vp] * 9 + [vp]
         L.mla_decode_timed.restype = c_int
         L.mla_decode_timed.argtypes = [dp] + [vp] * 10 + [sz, vp, ctypes.POINTER(vp)]
         L.mla_decode_fp8.restype = c_int
@@ -155,7 +160,7 @@ def _want(t, name, dtype, ndim, device):
 
 def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None, lse=None,
            max_seq_len=None, softmax_scale=None, num_units=0, workspace=None, stream=None,
-           return_lse=False, kernel_events=None, kv_scales=None):
+           return_lse=False, kernel_events=None, kv_scales=None, no_alloc=False):
     """Absorbed MLA decode through mla_decode(). Tensors live on one HIP device.
 
     q_nope bf16 [B,H,d_n], q_rope bf16 [B,H,d_R], W_UK bf16 [H,d_n,d_c], W_UV bf16 [H,d_c,d_v],
@@ -170,11 +175,16 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
     kv_scales: an FP8 cache (mla_decode_fp8): kv_pages is then uint8 [P,64,d_c+2*d_R], token
     = [c_KV as FP8 e4m3 bytes | k_R bf16], and kv_scales fp32 [P,64] holds each token's c_KV
     scale.
+    no_alloc: run mla_decode_noalloc, whose scratch is built into the library (no workspace;
+    pass out, and lse when return_lse, so that nothing is allocated here either).
     """
     bf, i32 = torch.bfloat16, torch.int32
     nq = q_nope.dim() if isinstance(q_nope, torch.Tensor) else 3
     if nq not in (3, 4):
         raise ValueError("q_nope must be [B,H,d_n] or [B,T,H,d_n]")
+    if no_alloc and (workspace is not None or kernel_events is not None or
+                     kv_scales is not None):
+        raise ValueError("no_alloc takes no workspace, kernel_events or kv_scales")
     dev = q_nope.device
     # dtype, rank and layout of every tensor, then the sizes they must agree on (the library
     # only sees pointers: a short tensor here would be read or written past its end on the
@@ -220,6 +230,12 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
         out = torch.empty(lead + (H, d_v), dtype=bf, device=dev)
     if return_lse and lse is None:
         lse = torch.empty(lead + (H,), dtype=torch.float32, device=dev)
+    if no_alloc:
+        _check(lib().mla_decode_noalloc(
+            ctypes.byref(dims), _ptr(q_nope), _ptr(q_rope), _ptr(W_UK), _ptr(W_UV),
+            _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
+            _stream(stream, dev)))
+        return (out, lse) if return_lse else out
     nbytes = workspace_bytes(dims)
     if nbytes == 0:
         _check(lib().mla_decode(ctypes.byref(dims), *([ctypes.c_void_p(0)] * 10), 0,

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "mla_decode.h"
@@ -205,6 +206,40 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
 
 }  // namespace
 
+namespace {
+
+// Scratch of mla_decode_noalloc: one array per GPU in the code object, sized for every
+// supported call whose mla_decode_workspace_bytes is at most kNoAllocScratchBytes (the five
+// benchmark workloads need 2.4 to 33.7 MB). Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per device, with that
+// device current.
+constexpr size_t kNoAllocScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call on that device).
+mla_status_t scratch_for_current_device(void** ptr) {
+  int dev = 0;
+  mla_status_t st = hip_status(hipGetDevice(&dev));
+  if (st != MLA_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (st != MLA_OK) return st;
+    if (!p || ((uintptr_t)p & 255) != 0) return MLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
@@ -242,6 +277,22 @@ mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* 
                         float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
   return mla_decode_timed(dims, q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out,
                           lse_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+mla_status_t mla_decode_noalloc(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                                const void* W_UK, const void* W_UV, const void* kv_pages,
+                                const int32_t* page_table, const int32_t* seq_lens, void* out,
+                                float* lse_out, void* stream) {
+  ShapeInfo s;
+  const mla_status_t st0 = check_dims(dims, &s);
+  if (st0 != MLA_OK) return st0;
+  const size_t need = mla_decode_workspace_bytes(dims);
+  if (need == 0 || need > kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const mla_status_t st = scratch_for_current_device(&ws);
+  if (st != MLA_OK) return st;
+  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, nullptr, page_table,
+                     seq_lens, out, lse_out, ws, kNoAllocScratchBytes, stream, nullptr);
 }
 
 mla_status_t mla_gather_pages(const mla_dims_t* dims, const void* kv_pages,

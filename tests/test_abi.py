@@ -8,8 +8,8 @@ import pytest
 import mla_latent_kv_14_amd as M
 from mla_latent_kv_14_amd.binding import STATUS_CODE
 
-EXPECTED = ["mla_cache_append", "mla_decode", "mla_decode_fp8", "mla_decode_out",
-            "mla_decode_timed",
+EXPECTED = ["mla_cache_append", "mla_decode", "mla_decode_fp8", "mla_decode_noalloc",
+            "mla_decode_out", "mla_decode_timed",
             "mla_decode_workspace_bytes", "mla_gather_pages", "mla_last_hip_error",
             "mla_status_str"]
 
@@ -122,6 +122,33 @@ def test_workspace_too_small_or_missing():
     assert M.lib().mla_decode_fp8(ctypes.byref(d), *p, ctypes.c_void_p(0), _al(10),
                                   M.workspace_bytes(d) - 256, ctypes.c_void_p(0), None) == \
         STATUS_CODE["MLA_ERR_WORKSPACE"]
+
+
+def test_noalloc_scratch_size_matches_header():
+    import re
+    text = open(M.binding.HEADER).read()
+    m = re.search(r"#define MLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == M.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_refuses_before_enqueueing():
+    # dims checks and the scratch limit come before any device call
+    def noalloc(d):
+        p = [_al(k + 1) for k in range(9)]
+        return M.lib().mla_decode_noalloc(ctypes.byref(d) if d is not None else None, *p,
+                                          ctypes.c_void_p(0))
+    assert noalloc(None) == STATUS_CODE["MLA_ERR_NULL_ARG"]
+    d = ds_dims()
+    d.page_size = 32
+    assert noalloc(d) == STATUS_CODE["MLA_ERR_BAD_DIMS"]
+    # the five benchmark workloads fit; 4096 DeepSeek sequences do not
+    assert M.workspace_bytes(ds_dims(B=64, max_pages=128)) <= M.NOALLOC_SCRATCH_BYTES
+    d = ds_dims(B=4096, max_pages=512, num_pages=1 << 20, max_seq_len=32768)
+    assert M.workspace_bytes(d) > M.NOALLOC_SCRATCH_BYTES
+    assert noalloc(d) == STATUS_CODE["MLA_ERR_WORKSPACE"]
+    d = m2_dims(B=8192, max_pages=512, num_pages=1 << 22)
+    assert M.workspace_bytes(d) > M.NOALLOC_SCRATCH_BYTES
+    assert noalloc(d) == STATUS_CODE["MLA_ERR_WORKSPACE"]
 
 
 def test_gather_rejects_bad_args():
