@@ -70,3 +70,30 @@ def check_against_oracle(M, inp, pairs=None, units=0, label=""):
     assert mx <= MAX_ABS, (label, mx)
     assert lerr <= LSE_ABS, (label, lerr)
     return rel, mx, lerr
+
+
+class HipEvents:
+    """hipEvent_t handles through ctypes (the library takes raw events)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = self.ct.c_void_p()
+        assert self.L.hipEventCreate(self.ct.byref(e)) == 0
+        return e.value
+
+    def ms(self, a, b):
+        t = self.ct.c_float()
+        assert self.L.hipEventElapsedTime(self.ct.byref(t), self.ct.c_void_p(a),
+                                          self.ct.c_void_p(b)) == 0
+        return t.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(self.ct.c_void_p(e))

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import REL_L2, errors, gpu_decode, need_gpu, say, to_dev
+from tests.gpu_helpers import REL_L2, HipEvents, errors, gpu_decode, need_gpu, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -120,33 +120,6 @@ def test_sequence_longer_than_table_is_clamped(M):
     assert torch.equal(_bits(a), _bits(b))
 
 
-class _HipEvents:
-    """hipEvent_t handles through ctypes (the library takes raw events)."""
-
-    def __init__(self):
-        import ctypes
-        self.ct = ctypes
-        self.L = ctypes.CDLL("libamdhip64.so")
-        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                               ctypes.c_void_p]
-        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
-
-    def create(self):
-        e = self.ct.c_void_p()
-        assert self.L.hipEventCreate(self.ct.byref(e)) == 0
-        return e.value
-
-    def ms(self, a, b):
-        t = self.ct.c_float()
-        assert self.L.hipEventElapsedTime(self.ct.byref(t), self.ct.c_void_p(a),
-                                          self.ct.c_void_p(b)) == 0
-        return t.value
-
-    def destroy(self, e):
-        self.L.hipEventDestroy(self.ct.c_void_p(e))
-
-
 @pytest.mark.parametrize("dims", [DS, M2], ids=["deepseek", "mha2mla"])
 def test_timed_entry_point(M, dims):
     # mla_decode_timed gives the same bits as mla_decode, and its six events bracket the three
@@ -155,7 +128,7 @@ def test_timed_entry_point(M, dims):
     d = to_dev(inp)
     say("timed entry point", dims["d_c"])
     ref = gpu_decode(M, d)
-    hip = _HipEvents()
+    hip = HipEvents()
     ev = [hip.create() for _ in range(6)]
     out = gpu_decode(M, d, kernel_events=ev)
     torch.cuda.synchronize()
