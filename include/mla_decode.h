@@ -18,8 +18,8 @@
  * Supported shapes: (num_heads, d_nope, d_latent, d_rope, d_v) = (128, 128, 512, 64, 128),
  * the DeepSeek-V2/V3 widths (bhfrc.com/news/60867 S3), and (32, 120, 64, 8, 128), the MHA2MLA
  * Llama-2-7B attention config (lpnh.cn/news/2494972 S3.2). page_size must be 64. The cache is
- * bf16 (mla_decode, mla_decode_timed, mla_decode_out) or, at the MHA2MLA widths, FP8 E4M3 with
- * a power-of-two scale per token (mla_decode_fp8).
+ * bf16 (mla_decode, mla_decode_timed, mla_decode_out) or FP8 E4M3 with a power-of-two scale
+ * per token (mla_decode_fp8).
  *
  * Conventions for every entry point:
  *   - tensors are dense row-major, in device memory, 16-byte aligned; bf16 is stored as its
@@ -162,8 +162,8 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
 /*
  * The decode over a quantised latent cache: c_KV stored as 8-bit floats with a scale per token
  * (bhfrc.com/news/60867 S1 and S5 quantise the latent cache that the decode gathers; this is
- * the FP8 form of that cache). Built for the MHA2MLA widths (H=32, d_nope=120, d_latent=64,
- * d_rope=8, d_v=128) only; other widths return MLA_ERR_UNSUPPORTED.
+ * the FP8 form of that cache), at both supported widths: a token takes d_latent + 2*d_rope
+ * bytes plus its 4-byte scale (644 bytes at the DeepSeek widths, against 1152 in bf16).
  *   kv_pages   uint8 [num_pages, 64, d_latent + 2*d_rope]  token row = [c_KV as d_latent
  *              FP8 E4M3 bytes (OCP format: 4 exponent bits, bias 7, 3 mantissa bits, no
  *              infinities, S.1111.111 = NaN) | k_R as d_rope bf16 values]

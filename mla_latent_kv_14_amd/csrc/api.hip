@@ -140,7 +140,6 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
   ShapeInfo s;
   mla_status_t st = check_dims(dims, &s);
   if (st != MLA_OK) return st;
-  if (kv_scales && s.shape != mla::kShapeMha2Mla) return MLA_ERR_UNSUPPORTED;
   if (kv_scales && !aligned16(kv_scales)) return MLA_ERR_MISALIGNED;
   if (hidden < 0 || hidden > (1 << 20)) return MLA_ERR_BAD_DIMS;
   if (hidden > 0 && (hidden % 16 != 0 || (s.H * s.DC) % 1024 != 0)) return MLA_ERR_UNSUPPORTED;

@@ -78,34 +78,80 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const Plan* plan, const i
 // rounds to land. P, the rescale factors and 1/l are double buffered by tile parity.
 // The reference max of a head is fixed on the segment's first tile and only moves when a tile
 // beats it by more than 64 in log2 units (a factor 2^64); the value team then rescales.
+//
+// FP8 cache (bhfrc.com/news/60867 S1 quantised latent cache, read as FP8 e4m3 with a
+// power-of-two scale per token): a token row is [c_KV as FP8 (512 bytes) | k_R bf16 (128
+// bytes)], 640 bytes, and a ring entry is a tile's 20 KiB of rows plus its 32 scales. Seven
+// entries fit where four bf16 tiles did: tiles r and r+1 in use, r+2 .. r+6 in flight. The MFMA
+// operands are formed from the FP8 bytes in registers: a score wave converts its operand (8
+// latent values of one token) with that token's scale; a value wave converts its operand (8
+// tokens of one latent column, from 8-bit transposing reads) unscaled, and the score wave
+// multiplies each token's bf16 weight by the token's scale instead. A power of two moves
+// exactly between the two factors, so the products are those over the bf16 cache that holds
+// c_KV * scale. At a segment's end a value wave stages its partial in its own 128 columns of
+// the finished tile, 64 output columns at a time.
 namespace ds {
 constexpr int H = 128, HG = 64, DC = 512, DR = 64, DK = DC + DR, ROWB = DK * 2;
-constexpr int NBUF = 4;
 constexpr int NW = 8;        // waves per work group: 4 score waves, 4 value waves
 constexpr int PPITCH = 80;   // bytes per head row of P (32 bf16 + 16 pad: conflict-free reads)
 constexpr int KST = DK / 32; // score MFMA steps (16x16x32) per token block
 using Tile = PagedTile<kSub, ROWB>;
-constexpr int IPW = Tile::INSTR / 4;  // load instructions per value wave per tile
 constexpr float kRescale = 64.f;      // log2 headroom before the running max must move
+constexpr int ROWB8 = DC + 2 * DR;    // FP8 cache: bytes per token row
+using Tile8 = PagedTile<kSub, ROWB8>;
+constexpr int SCB = 256;              // FP8 cache: bytes of a ring entry's scale block
+// Per cache format: ring depth, bytes per ring entry, and load instructions per value wave per
+// tile (the FP8 tile's 20 instructions over four waves, plus each wave's load of the scales).
+template <bool FP8> struct Ring {
+  static constexpr int NBUF = 4, BYTES = Tile::BYTES, TILE_IPW = Tile::INSTR / 4;
+  static constexpr int IPW = TILE_IPW;
+};
+template <> struct Ring<true> {
+  static constexpr int NBUF = 7, BYTES = Tile8::BYTES + SCB, TILE_IPW = Tile8::INSTR / 4;
+  static constexpr int IPW = TILE_IPW + 1;
+};
+static_assert(Ring<false>::IPW == 9 && Ring<true>::IPW == 6, "load instructions per wave");
+static_assert(Ring<true>::BYTES % 256 == 0, "ring entries start on the same LDS bank");
 }  // namespace ds
 
-// Waits until at most `after` (0..2) tiles of N instructions each are still in flight.
-template <int N>
-__device__ __forceinline__ void wait_tiles_after(int after) {
-  if (after >= 2) wait_vmcnt<2 * N>();
-  else if (after == 1) wait_vmcnt<N>();
-  else wait_vmcnt<0>();
+// Waits until at most `after` tiles of N load instructions each are still in flight, with S
+// younger stores also outstanding (a segment's partial, written after the round's tile loads:
+// vmcnt counts loads and stores alike, in issue order, so the stores are part of the budget;
+// left out, the wait would also hold until the partial is written and drain tile loads that
+// may stay in flight). `after` is clamped to MAXA, the most a caller can have in flight (the
+// ring depth minus the tiles in use), which also keeps the chain of tests short.
+template <int N, int MAXA, int S = 0>
+__device__ __forceinline__ void wait_tiles(int after) {
+  static_assert(MAXA * N + S < 64, "vmcnt range");
+  if (after >= MAXA) wait_vmcnt<MAXA * N + S>();
+  else if constexpr (MAXA > 1) wait_tiles<N, MAXA - 1, S>(after);
+  else wait_vmcnt<S>();
 }
 
+// FP8 e4m3 -> bf16, 8 values from two words (bytes 0..7 in order), times 2^(exponent of sc)
+__device__ __forceinline__ bf16x8 cvt_fp8x8(uint32_t w0, uint32_t w1, float sc) {
+  const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
+  const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
+  const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
+  const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
+  return cat4(__builtin_shufflevector(a0, a1, 0, 1, 2, 3),
+              __builtin_shufflevector(a2, a3, 0, 1, 2, 3));
+}
+
+template <bool FP8>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
                      const char* __restrict__ kv, const int32_t* __restrict__ page_table,
                      const int32_t* __restrict__ seq_lens, int B, int max_pages, int q_len,
                      int num_pages,
                      const Plan* __restrict__ plan, int G, float scale_log2,
-                     uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
+                     uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
+                     const float* __restrict__ kv_scales) {
   using namespace ds;
-  __shared__ __attribute__((aligned(1024))) char lds_tiles[NBUF * Tile::BYTES];
+  using TileL = typename std::conditional<FP8, Tile8, Tile>::type;  // the format as loaded
+  constexpr int NBUF = Ring<FP8>::NBUF, LB = Ring<FP8>::BYTES, IPW = Ring<FP8>::IPW;
+  constexpr int TIPW = Ring<FP8>::TILE_IPW;  // tile loads per value wave (without the scales)
+  __shared__ __attribute__((aligned(1024))) char lds_tiles[NBUF * LB];
   __shared__ __attribute__((aligned(16))) char lds_p[2][HG * PPITCH];
   __shared__ __attribute__((aligned(16))) float lds_alpha[2][HG];  // rescale factor per head
   __shared__ __attribute__((aligned(16))) float lds_invl[2][HG];   // 1/l at a segment's end
@@ -135,11 +181,24 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
     // score operand (16x16x32, A = tile rows): token row 16tb + hl, chunk 4s + g4 of step s;
     // with the row swizzle, step s sits at ko[tb][s & 1] + 128 * (s >> 1) (RoPE steps included)
     uint32_t ko[2][2];
+    // FP8: latent step s reads the 8 bytes at ko8[tb][s & 3] + 128 * (s >> 2) (bytes 32s + 8g4
+    // of the row), RoPE step 16 + q the 16 bytes at kr8[tb][q]
+    uint32_t ko8[2][4], kr8[2][2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int r = 16 * tb + hl, sw = Tile::swz(r);
-      ko[tb][0] = r * ROWB + 16 * (g4 ^ sw);
-      ko[tb][1] = r * ROWB + 16 * ((4 + g4) ^ sw);
+      const int r = 16 * tb + hl;
+      if constexpr (FP8) {
+        const int sw = Tile8::swz(r);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ko8[tb][q] = r * ROWB8 + 16 * ((2 * q + (g4 >> 1)) ^ sw) + 8 * (g4 & 1);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) kr8[tb][q] = r * ROWB8 + DC + 16 * ((4 * q + g4) ^ sw);
+      } else {
+        const int sw = Tile::swz(r);
+        ko[tb][0] = r * ROWB + 16 * (g4 ^ sw);
+        ko[tb][1] = r * ROWB + 16 * ((4 + g4) ^ sw);
+      }
     }
     bf16x8 qf[KST];
     auto load_queries = [&](int b) {  // this wave's 16 queries, loads completed here
@@ -163,21 +222,59 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         const bool seg_first = t == 0 || ca.j == 0;
         const bool seg_last = t == n - 1 || ca.j == ca.nj - 1;
         if (seg_first && t > 0) load_queries(ca.b);
-        const MLA_LDS char* kb = tiles + (t % NBUF) * Tile::BYTES;
+        const MLA_LDS char* kb = tiles + (t % NBUF) * LB;
         // Token block 0 first, then block 1; each block accumulates in two chains (even and odd
         // steps). Operand reads run one half-block (9 steps) ahead of the MFMAs, and on tiles
         // whose reference max is already set the weights of block 0 are formed while block 1's
         // MFMAs run (scheduling fences and groups keep that order).
-        bf16x8 kop[2][9];
-        auto read_half = [&](bf16x8* dst, int tb, int s0) {
+        // bf16: the operands as read. FP8: latent steps keep their 8 bytes in words 0 and 1
+        // (converted right before their MFMA, with the token's scale), RoPE steps are bf16.
+        using KOp = typename std::conditional<FP8, u32x4, bf16x8>::type;
+        KOp kop[2][9];
+        // FP8: the scale of this lane's operand token per block (sct), and the scales of its
+        // weight tokens 16tb + 4g4 + e (scw), read first so that their latency is spent here.
+        // They multiply bf16 values exactly: a scale is a power of two by the cache's contract.
+        float sct[2] = {1.f, 1.f};
+        f32x4 scw[2];
+        if constexpr (FP8) {
 #pragma unroll
-          for (int i = 0; i < 9; ++i)
-            dst[i] = lds_read_b128(kb, ko[tb][(s0 + i) & 1] + 128 * ((s0 + i) >> 1));
+          for (int tb = 0; tb < 2; ++tb) {
+            sct[tb] = *reinterpret_cast<const MLA_LDS float*>(kb + Tile8::BYTES +
+                                                              4 * (16 * tb + hl));
+            scw[tb] = *reinterpret_cast<const MLA_LDS f32x4*>(kb + Tile8::BYTES +
+                                                              4 * (16 * tb + 4 * g4));
+          }
+        }
+        auto read_half = [&](KOp* dst, int tb, int s0) {
+#pragma unroll
+          for (int i = 0; i < 9; ++i) {
+            const int s = s0 + i;
+            if constexpr (FP8) {
+              if (s < 16) {
+                const u32x2 w = *reinterpret_cast<const MLA_LDS u32x2*>(
+                    kb + ko8[tb][s & 3] + 128 * (s >> 2));
+                dst[i][0] = w[0];
+                dst[i][1] = w[1];
+              } else {
+                dst[i] = *reinterpret_cast<const MLA_LDS u32x4*>(kb + kr8[tb][s - 16]);
+              }
+            } else {
+              dst[i] = lds_read_b128(kb, ko[tb][s & 1] + 128 * (s >> 1));
+            }
+          }
         };
-        auto mfma_half = [&](f32x4* c, const bf16x8* src, int s0) {
+        auto mfma_half = [&](f32x4* c, const KOp* src, int s0, int tb) {
 #pragma unroll
-          for (int i = 0; i < 9; ++i)
-            c[(s0 + i) & 1] = mfma_16x16x32(src[i], qf[s0 + i], c[(s0 + i) & 1]);
+          for (int i = 0; i < 9; ++i) {
+            const int s = s0 + i;
+            if constexpr (FP8) {
+              const bf16x8 op = s < 16 ? cvt_fp8x8(src[i][0], src[i][1], sct[tb])
+                                       : __builtin_bit_cast(bf16x8, src[i]);
+              c[s & 1] = mfma_16x16x32(op, qf[s], c[s & 1]);
+            } else {
+              c[s & 1] = mfma_16x16x32(src[i], qf[s], c[s & 1]);
+            }
+          }
         };
         static_assert(KST == 18, "two half-blocks of nine steps");
         const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -186,15 +283,15 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         __builtin_amdgcn_sched_barrier(0);
         read_half(kop[1], 0, 9);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_half(c0, kop[0], 0);
+        mfma_half(c0, kop[0], 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         read_half(kop[0], 1, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_half(c0, kop[1], 9);
+        mfma_half(c0, kop[1], 9, 0);
         __builtin_amdgcn_sched_barrier(0);
         read_half(kop[1], 1, 9);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_half(c1, kop[0], 0);
+        mfma_half(c1, kop[0], 0, 1);
         __builtin_amdgcn_sched_barrier(0);
         // lane: head hl, tokens 16tb + 4g4 + e
         const int valid = min(kSub, ca.S - ca.j * kSub);
@@ -212,7 +309,9 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const __bf16 pbf = (__bf16)exp2f_fast(v[tb][e] - m_ref);
-            pv[e] = pbf;
+            // FP8: the weight that multiplies the unscaled values carries the token's scale
+            // (exact: a power of two); l sums the weights themselves
+            pv[e] = FP8 ? (__bf16)((float)pbf * scw[tb][e]) : pbf;
             lsum += (float)pbf;
           }
           *reinterpret_cast<MLA_LDS bf16x4*>(prow + 32 * tb) = pv;
@@ -220,7 +319,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         if (!seg_first) {
           scale_block(0, c0);
           weights_block(0);
-          mfma_half(c1, kop[1], 9);
+          mfma_half(c1, kop[1], 9, 1);
 #pragma unroll
           for (int i = 0; i < 9; ++i) {  // one MFMA, then a few VALU instructions of block 0
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -230,7 +329,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
           scale_block(1, c1);
           weights_block(1);
         } else {
-          mfma_half(c1, kop[1], 9);
+          mfma_half(c1, kop[1], 9, 1);
           scale_block(0, c0);
           scale_block(1, c1);
         }
@@ -277,9 +376,9 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
     const int vw = wave - 4;
     const int t32 = lane & 31, hi = lane >> 5;
     const int G16 = lane >> 4, q16 = lane & 15;
-    uint32_t dmo[IPW];
+    uint32_t dmo[TIPW];
 #pragma unroll
-    for (int k = 0; k < IPW; ++k) dmo[k] = Tile::src_off(vw + 4 * k, lane, kSub);
+    for (int k = 0; k < TIPW; ++k) dmo[k] = TileL::src_off(vw + 4 * k, lane, kSub);
     // value operand (transposing reads): rows 16ks + 8(G16/2) + 4hf + q16/4, latent columns
     // 128vw + 32nb + 16(G16%2) + 4(q16%4); column block nb >= 2 is 128 bytes further on
     uint32_t ov[2][2];
@@ -291,6 +390,18 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         const int low = 4 * nb + 2 * (G16 & 1) + ((q16 >> 1) & 1);
         ov[hf][nb] = t * ROWB + 16 * (16 * vw + (low ^ Tile::swz(t))) + 8 * (q16 & 1);
       }
+    // FP8 value operand (8-bit transposing reads): in each group of 16 lanes, lane w supplies
+    // the 8 bytes at (token 16ks + 8(G16/2) + w/2, latent columns 128vw + 32nb + 16(G16%2) +
+    // 8(w%2) ..+8), and lane l receives byte l%8 of the segments of lanes 2b + ((l >> 3) & 1),
+    // b = 0..7: latent column 128vw + 32nb + (l & 31) of tokens 16ks + 8(l/32) + b
+    uint32_t ov8[4];
+    if constexpr (FP8) {
+      const int t = 8 * (G16 >> 1) + (q16 >> 1);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        ov8[nb] = t * ROWB8 + 128 * vw + 16 * ((2 * nb + (G16 & 1)) ^ Tile8::swz(t)) +
+                  8 * (q16 & 1);
+    }
     const uint32_t pr = t32 * PPITCH + 16 * hi;  // P read: + 32*PPITCH*mb + 32*ks
 
     // tile loads. A loading wave keeps 64 page-table entries of the current sequence in one
@@ -299,11 +410,21 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
     Cursor lc = c0;
     int issued = 0;
     int pw_v = 0, pw_b = -1, pw_base = 0;
-    // The next tile to load: its global base, valid rows and LDS buffer (lookup), then its 9
-    // instructions per wave, possibly in parts, then the cursor moves on (advance).
+    // The next tile to load: its global base, valid rows and LDS buffer (lookup), then its
+    // instructions (and, FP8, its scales), possibly in parts, then the cursor moves on
+    // (advance).
     const char* nbase = kv;
+    const float* nsc = kv_scales;  // FP8: the tile's 32 scales
     int nvalid = 0;
     MLA_LDS char* ndst = tiles;
+    // FP8: lane l loads the scale of token min(l % 32, valid - 1) into byte 4l of the block
+    auto sc_off = [&](int valid) { return 4u * (uint32_t)min(lane & 31, valid - 1); };
+    auto set_scales = [&](int page, int j) {
+      if constexpr (FP8) {
+        page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+        nsc = kv_scales + (size_t)page * kPage + (j % Tile8::TPP) * kSub;
+      }
+    };
     auto lookup = [&]() {
       const int p = lc.j / Tile::TPP;
       if (lc.b != pw_b || p < pw_base || p >= pw_base + 64) {
@@ -318,17 +439,23 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)"
                      : "=v"(pw_v) : "v"(src) : "memory");
       }
-      nbase = Tile::base_of(kv, __builtin_amdgcn_readlane(pw_v, p - pw_base), lc.j, num_pages);
+      const int page = __builtin_amdgcn_readlane(pw_v, p - pw_base);
+      nbase = TileL::base_of(kv, page, lc.j, num_pages);
+      set_scales(page, lc.j);
       nvalid = min(kSub, lc.S - lc.j * kSub);
-      ndst = tiles + (issued % NBUF) * Tile::BYTES;
+      ndst = tiles + (issued % NBUF) * LB;
     };
     auto advance = [&]() {
       ++issued;
       cursor_next(lc, plan, seq_lens, B, max_pages, q_len);
     };
+    auto issue_scales = [&]() {
+      if constexpr (FP8) load_lds_4(nsc, sc_off(nvalid), ndst + Tile8::BYTES);
+    };
     auto issue_next = [&]() {
       lookup();
-      Tile::issue<4>(nbase, nvalid, dmo, ndst, vw, lane);
+      TileL::template issue<4>(nbase, nvalid, dmo, ndst, vw, lane);
+      issue_scales();
       advance();
     };
     {
@@ -338,19 +465,44 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
       // statement, so the window register is complete when the compiler first sees it and no
       // instruction can read it while the load is in flight (it is early-clobber: no input
       // shares its register). M0, the LDS destination, steps by 4 KiB per instruction.
-      static_assert(IPW == 9, "nine loads per wave per tile");
       pw_b = lc.b;
       pw_base = lc.j / Tile::TPP;
       const int idx = pw_base + lane < max_pages ? pw_base + lane : max_pages - 1;
       const int32_t* src = page_table + (size_t)virt_row(lc.b, q_len) * max_pages + idx;
-      nbase = Tile::base_of(kv, us.page, lc.j, num_pages);
+      nbase = TileL::base_of(kv, us.page, lc.j, num_pages);
+      set_scales(us.page, lc.j);
       nvalid = min(kSub, lc.S - lc.j * kSub);
       ndst = tiles;
-      uint32_t o[IPW];
+      uint32_t o[TIPW];
 #pragma unroll
-      for (int k = 0; k < IPW; ++k)
-        o[k] = nvalid >= kSub ? dmo[k] : Tile::src_off(vw + 4 * k, lane, nvalid);
+      for (int k = 0; k < TIPW; ++k)
+        o[k] = nvalid >= kSub ? dmo[k] : TileL::src_off(vw + 4 * k, lane, nvalid);
       uint32_t m0 = (uint32_t)(uintptr_t)(ndst + vw * 1024);
+      if constexpr (FP8) {
+        // five tile loads, then the scales (M0 moved to the entry's scale block); the wait
+        // leaves those six in flight
+        static_assert(TIPW == 5 && IPW == 6, "five tile loads and one scale load per wave");
+        const uint32_t m0_sc = (uint32_t)(uintptr_t)(ndst + Tile8::BYTES);
+        asm volatile(
+            "global_load_dword %0, %2, off\n\t"
+            "global_load_lds_dwordx4 %4, %3\n\t"
+            "s_add_u32 m0, m0, 0x1000\n\t"
+            "global_load_lds_dwordx4 %5, %3\n\t"
+            "s_add_u32 m0, m0, 0x1000\n\t"
+            "global_load_lds_dwordx4 %6, %3\n\t"
+            "s_add_u32 m0, m0, 0x1000\n\t"
+            "global_load_lds_dwordx4 %7, %3\n\t"
+            "s_add_u32 m0, m0, 0x1000\n\t"
+            "global_load_lds_dwordx4 %8, %3\n\t"
+            "s_mov_b32 m0, %11\n\t"
+            "global_load_lds_dword %9, %10\n\t"
+            "s_waitcnt vmcnt(6)"
+            : "=&v"(pw_v), "+{m0}"(m0)
+            : "v"(src), "s"(nbase), "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]),
+              "v"(sc_off(nvalid)), "s"(nsc), "s"(m0_sc)
+            : "memory", "scc");
+      } else {
+      static_assert(IPW == 9, "nine loads per wave per tile");
       asm volatile(
           "global_load_dword %0, %2, off\n\t"
           "global_load_lds_dwordx4 %4, %3\n\t"
@@ -375,14 +527,16 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
           : "v"(src), "s"(nbase), "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]),
             "v"(o[5]), "v"(o[6]), "v"(o[7]), "v"(o[8])
           : "memory", "scc");
+      }
       advance();
     }
-    while (issued < 3 && issued < n) issue_next();
-    wait_tiles_after<IPW>(issued - 1);  // tile 0 landed
+    constexpr int MAXA = NBUF - 2;  // tiles in flight beyond the two in use
+    while (issued < NBUF - 1 && issued < n) issue_next();
+    wait_tiles<IPW, MAXA>(issued - 1);  // tile 0 landed
     block_sync_tagged<1>();
 
     // round -1: the score team works on tile 0
-    if (1 < n) wait_tiles_after<IPW>(issued - 2);  // tile 1 landed
+    if (1 < n) wait_tiles<IPW, MAXA>(issued - 2);  // tile 1 landed
     block_sync_tagged<1>();
 
     Cursor cb = c0;
@@ -396,12 +550,12 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
       for (int k = 0; k < seg; ++k, ++r) {
-        // tile r+3 goes into the buffer tile r-1 left (read before the last barrier); its
+        // tile r+NBUF-1 goes into the buffer tile r-1 left (read before the last barrier); its
         // loads are issued in three parts between the value MFMAs
         const bool load = issued < n;
         if (load) lookup();
         const int pb = r & 1;
-        const MLA_LDS char* kb = tiles + (r % NBUF) * Tile::BYTES;
+        const MLA_LDS char* kb = tiles + (r % NBUF) * LB;
         const MLA_LDS char* pbuf = (const MLA_LDS char*)lds_p[pb];
         if (k > 0) {
           const u32x4 fl =
@@ -427,12 +581,25 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
           for (int mb = 0; mb < 2; ++mb)
             pa[mb] = lds_read_b128(pbuf, pr + 32 * PPITCH * mb + 32 * ks);
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            vb[nb] = cat4(lds_read_tr16(kb, ov[0][nb & 1] + 128 * (nb >> 1) + ks * 16 * ROWB),
-                          lds_read_tr16(kb, ov[1][nb & 1] + 128 * (nb >> 1) + ks * 16 * ROWB));
+          for (int nb = 0; nb < 4; ++nb) {
+            if constexpr (FP8) {
+              typedef int v2i __attribute__((ext_vector_type(2)));
+              const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                  (MLA_LDS v2i*)(kb + ov8[nb] + ks * 16 * ROWB8));
+              vb[nb] = cvt_fp8x8((uint32_t)w[0], (uint32_t)w[1], 1.0f);
+            } else {
+              vb[nb] = cat4(lds_read_tr16(kb, ov[0][nb & 1] + 128 * (nb >> 1) + ks * 16 * ROWB),
+                            lds_read_tr16(kb, ov[1][nb & 1] + 128 * (nb >> 1) + ks * 16 * ROWB));
+            }
+          }
           if (load) {
-            if (ks == 0) Tile::issue_part<4, 0, 3>(nbase, nvalid, dmo, ndst, vw, lane);
-            else Tile::issue_part<4, 3, 6>(nbase, nvalid, dmo, ndst, vw, lane);
+            if constexpr (FP8) {
+              if (ks == 0) Tile8::issue_part<4, 0, 2>(nbase, nvalid, dmo, ndst, vw, lane);
+              else Tile8::issue_part<4, 2, 4>(nbase, nvalid, dmo, ndst, vw, lane);
+            } else {
+              if (ks == 0) Tile::issue_part<4, 0, 3>(nbase, nvalid, dmo, ndst, vw, lane);
+              else Tile::issue_part<4, 3, 6>(nbase, nvalid, dmo, ndst, vw, lane);
+            }
           }
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb)
@@ -441,14 +608,55 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
               acc[mb][nb] = mfma_32x32x16(vb[nb], pa[mb], acc[mb][nb]);
         }
         if (load) {
-          Tile::issue_part<4, 6, 9>(nbase, nvalid, dmo, ndst, vw, lane);
+          if constexpr (FP8) Tile8::issue_part<4, 4, 5>(nbase, nvalid, dmo, ndst, vw, lane);
+          else Tile::issue_part<4, 6, 9>(nbase, nvalid, dmo, ndst, vw, lane);
+          issue_scales();
           advance();
         }
-        if (k == seg - 1) {
+        if (FP8 && k == seg - 1) {
+          // Normalise and write this wave's block of the segment's partial, staged in the
+          // bytes of tile r that only this wave read (its 128 FP8 columns of each 640-byte row,
+          // 4 KiB): 32 heads x 64 columns per pass, head 32mb + t of the pass in row t, then
+          // written as whole 128-byte rows. Within a row the 8-byte unit u (four columns) sits
+          // at u ^ 2((t >> 1) & 7): the 64 lanes of a write hit every bank twice, and 16-byte
+          // pieces stay whole for the read-back.
+          MLA_LDS char* stg = tiles + (r % NBUF) * LB + 128 * vw;
+          int slot_e = slot, lane_e = lane;
+          asm volatile("" : "+s"(slot_e), "+v"(lane_e));
+          uint16_t* po = part_o + ((size_t)slot_e * H + HG * hh) * DC + 128 * vw;
+          const int t32e = lane_e & 31;
+          const int wsw = 2 * ((t32e >> 1) & 7);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const float il = lds_invl[pb][32 * mb + t32e];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+#pragma unroll
+              for (int nbl = 0; nbl < 2; ++nbl)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                  const f32x16& o = acc[mb][2 * half + nbl];
+                  const int u = 8 * nbl + 2 * r4 + (lane_e >> 5);
+                  const u32x2 w = {pack_bf16x2(o[4 * r4] * il, o[4 * r4 + 1] * il),
+                                   pack_bf16x2(o[4 * r4 + 2] * il, o[4 * r4 + 3] * il)};
+                  *reinterpret_cast<MLA_LDS u32x2*>(stg + t32e * ROWB8 + 8 * (u ^ wsw)) = w;
+                }
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {  // 32 rows x 8 pieces of 16 bytes
+                const int q = q4 * 64 + lane_e, row = q >> 3, piece = q & 7;
+                const int rsw = 2 * ((row >> 1) & 7);
+                *reinterpret_cast<u32x4*>(po + (size_t)(32 * mb + row) * DC + 64 * half +
+                                          piece * 8) =
+                    *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * ROWB8 +
+                                                            8 * ((2 * piece) ^ rsw));
+              }
+            }
+          }
+        } else if (k == seg - 1) {
           // Normalise and write this wave's block of the segment's partial. It is staged, 32
           // heads at a time, in the bytes of tile r that only this wave read (256 bytes at
           // 256vw of each 1152-byte row), then written as whole 256-byte rows.
-          MLA_LDS char* stg = tiles + (r % NBUF) * Tile::BYTES + 256 * vw;
+          MLA_LDS char* stg = tiles + (r % NBUF) * LB + 256 * vw;
           // (the slot and lane pass through empty asm so that the store addresses are formed
           // here, not kept in registers through the whole segment)
           int slot_e = slot, lane_e = lane;
@@ -483,7 +691,12 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
             }
           }
         }
-        if (r + 2 < n) wait_tiles_after<IPW>(issued - (r + 3));  // tile r+2 landed
+        // tile r+2 landed (a wave that wrote a partial above has 16 stores behind the loads)
+        constexpr int kPartStores = 16;
+        if (r + 2 < n) {
+          if (k == seg - 1) wait_tiles<IPW, MAXA, kPartStores>(issued - (r + 3));
+          else wait_tiles<IPW, MAXA>(issued - (r + 3));
+        }
         block_sync_tagged<1>();  // P of tile r+1 visible; tile r free
       }
       cb.j += seg - 1;
@@ -779,13 +992,15 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
                             float scale_log2, void* part_o, float* part_lse,
                             const float* kv_scales, const Launch& L) {
   if (shape == kShapeDeepSeek) {
-    if (kv_scales) return hipErrorInvalidValue;  // the FP8 cache is built for MHA2MLA only
     // two head halves per tile stream, paired 8 ids apart; ids padded to whole groups of 16
     const int blocks = 16 * ((G + 7) / 8);
-    return launch_kernel(attn_deepseek_kernel, dim3(blocks), dim3(64 * ds::NW), L,
-                         (const uint16_t*)q_abs, (const uint16_t*)q_rope, (const char*)kv,
-                         page_table, seq_lens, B, max_pages, q_len, num_pages, (const Plan*)plan, G,
-                         scale_log2, (uint16_t*)part_o, part_lse);
+    auto go = [&](auto kernel) {
+      return launch_kernel(kernel, dim3(blocks), dim3(64 * ds::NW), L, (const uint16_t*)q_abs,
+                           (const uint16_t*)q_rope, (const char*)kv, page_table, seq_lens, B,
+                           max_pages, q_len, num_pages, (const Plan*)plan, G, scale_log2,
+                           (uint16_t*)part_o, part_lse, kv_scales);
+    };
+    return kv_scales ? go(attn_deepseek_kernel<true>) : go(attn_deepseek_kernel<false>);
   }
   const int blocks = (G + kAttnWavesMha2Mla - 1) / kAttnWavesMha2Mla;
   auto go = [&](auto kernel) {

@@ -245,11 +245,10 @@ def test_decode_fp8_rejects_before_enqueueing():
     def call(d, scales):
         return L.mla_decode_fp8(ctypes.byref(d), *ptrs, scales, *rest, _al(10),
                                 M.workspace_bytes(d), ctypes.c_void_p(0), None)
-    assert call(m2_dims(), ctypes.c_void_p(0)) == STATUS_CODE["MLA_ERR_NULL_ARG"]
-    # the FP8 cache is built for the MHA2MLA widths only
-    assert call(ds_dims(), _al(6)) == STATUS_CODE["MLA_ERR_UNSUPPORTED"]
-    assert call(m2_dims(), ctypes.c_void_p(_al(6).value + 4)) == \
-        STATUS_CODE["MLA_ERR_MISALIGNED"]
+    for dims in (m2_dims, ds_dims):  # the FP8 cache at both widths
+        assert call(dims(), ctypes.c_void_p(0)) == STATUS_CODE["MLA_ERR_NULL_ARG"]
+        assert call(dims(), ctypes.c_void_p(_al(6).value + 4)) == \
+            STATUS_CODE["MLA_ERR_MISALIGNED"]
     bad = m2_dims()
     bad.batch = 0
     assert call(bad, _al(6)) == STATUS_CODE["MLA_ERR_BAD_DIMS"]

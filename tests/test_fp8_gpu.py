@@ -1,4 +1,4 @@
-"""GPU parity of the FP8 latent cache (MHA2MLA widths): the decode over an FP8 e4m3 cache with
+"""GPU parity of the FP8 latent cache (both widths): the decode over an FP8 e4m3 cache with
 per-token power-of-two scales, through mla_decode_fp8, against the fp64 oracle run on the bf16
 cache that the FP8 one stands for (oracle.dequant_fp8_cache; with power-of-two scales every
 dequantised value is a bf16 value, so both sides see the same numbers and the bf16 bounds
@@ -14,6 +14,7 @@ from tests.gpu_helpers import LSE_ABS, MAX_ABS, REL_L2, errors, need_gpu, say, t
 pytestmark = pytest.mark.gpu
 
 M2 = dict(H=32, d_n=120, d_c=64, d_R=8, d_v=128)
+DS = dict(H=128, d_n=128, d_c=512, d_R=64, d_v=128)
 
 
 @pytest.fixture(scope="module")
@@ -21,13 +22,13 @@ def M():
     return need_gpu()
 
 
-def _inp(lens, seed, **kw):
-    return W.make_inputs(len(lens), M2["H"], M2["d_n"], M2["d_c"], M2["d_R"], M2["d_v"], lens,
-                         seed, **kw)
+def _inp(lens, seed, dims=M2, **kw):
+    return W.make_inputs(len(lens), dims["H"], dims["d_n"], dims["d_c"], dims["d_R"],
+                         dims["d_v"], lens, seed, **kw)
 
 
-def check_fp8(M, inp, units=0, pairs=None, poison=False, label="", seed=5):
-    kv8, sc = W.fp8_cache(inp, seed=seed, poison=poison)
+def check_fp8(M, inp, units=0, pairs=None, poison=False, label="", seed=5, exps=(-6, -2)):
+    kv8, sc = W.fp8_cache(inp, seed=seed, poison=poison, exps=exps)
     say(label, "fp8 B=%d units=%d T=%d" % (inp["B"], units,
                                             inp["q_nope"].shape[1] if inp["q_nope"].dim() == 4
                                             else 1))
@@ -145,14 +146,71 @@ def test_fp8_workload_full_size(M):
     check_fp8(M, inp, label="fp8 workload 5")
 
 
-def test_fp8_rejected_for_deepseek_widths(M):
-    inp = W.make_inputs(1, 128, 128, 512, 64, 128, [64], 3)
-    kv8, sc = W.fp8_cache(inp)
+# ---- DeepSeek widths (a 640-byte FP8 row plus its scale, against 1152 bytes in bf16)
+
+@pytest.mark.parametrize("units", [0, 1, 3, 7, 40])
+def test_fp8_deepseek_ragged(M, units):
+    # lengths around the 32-token tile and 64-token page edges, NaN in every unused slot
+    inp = _inp([1, 31, 32, 33, 64, 65, 700, 130], 81, DS, poison=True)
+    check_fp8(M, inp, units=units, poison=True, label="fp8 deepseek ragged")
+
+
+@pytest.mark.parametrize("units", [1, 2])
+def test_fp8_deepseek_long_sequences_few_units(M, units):
+    # a unit walks more than 64 pages (the page window refills) and crosses into the next
+    check_fp8(M, _inp([64 * 70 + 7, 64 * 3 + 40], 82, DS), units=units,
+              label="fp8 deepseek long")
+
+
+def test_fp8_deepseek_query_tokens(M):
+    inp = _inp([70, 2, 200, 64 * 3 + 1], 83, DS)
+    g = torch.Generator().manual_seed(84)
+    inp["q_nope"] = torch.randn(4, 2, 128, 128, generator=g).to(torch.bfloat16)
+    inp["q_rope"] = torch.randn(4, 2, 128, 64, generator=g).to(torch.bfloat16)
+    check_fp8(M, inp, label="fp8 deepseek 2 query tokens")
+
+
+def test_fp8_deepseek_equals_bf16_on_the_same_values(M):
+    # the score operand is converted with the token's scale and the value operand unscaled with
+    # the scale moved into the weight: every product equals the bf16 path's, bit for bit
+    inp = _inp([300, 64, 1000, 33], 85, DS)
+    kv8, sc = W.fp8_cache(inp, seed=3)
+    deq = oracle.dequant_fp8_cache(kv8.numpy(), sc.numpy(), inp["d_c"])
+    inp["kv_pages"] = torch.from_numpy(deq.view(np.int16)).view(torch.bfloat16)
     d = to_dev(inp)
-    with pytest.raises(M.MlaError) as e:
-        M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8.cuda(), d["page_table"],
-                 d["seq_lens"], kv_scales=sc.cuda())
-    assert e.value.code == 5  # MLA_ERR_UNSUPPORTED
+    for units in (0, 3):
+        a, la = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8.cuda(),
+                         d["page_table"], d["seq_lens"], kv_scales=sc.cuda(), num_units=units,
+                         return_lse=True)
+        b, lb = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], d["kv_pages"],
+                         d["page_table"], d["seq_lens"], num_units=units, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b) and torch.equal(la, lb), units
+
+
+def test_fp8_deepseek_empty_sequence_gives_zero_and_neg_inf(M):
+    inp = _inp([100, 5, 64], 86, DS)
+    kv8, sc = W.fp8_cache(inp, seed=1)
+    d = to_dev(inp)
+    d["seq_lens"][1] = 0
+    out, lse = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8.cuda(),
+                        d["page_table"], d["seq_lens"], return_lse=True, kv_scales=sc.cuda())
+    torch.cuda.synchronize()
+    assert torch.all(out[1].float() == 0)
+    assert torch.all(torch.isneginf(lse[1]))
+    assert torch.isfinite(out[0].float()).all() and torch.isfinite(out[2].float()).all()
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_fp8_deepseek_workload_full_size(M, cfg):
+    # B=16 at S=4096 (every (b, h)) and at S=65536 (a seeded sample of (b, h) pairs, every
+    # sequence) over an FP8 copy of the workload's cache
+    inp = W.config_inputs(cfg)
+    pairs = None
+    if cfg == 4:
+        rng = np.random.default_rng(44)
+        pairs = [(b, int(h)) for b in range(inp["B"]) for h in rng.choice(inp["H"], 4, False)]
+    check_fp8(M, inp, pairs=pairs, label="fp8 workload %d" % cfg, exps=(-5, -1))
 
 
 @pytest.mark.parametrize("units", [1, 5, 33])
