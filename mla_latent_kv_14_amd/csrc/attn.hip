@@ -539,6 +539,9 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
     if (1 < n) wait_tiles<IPW, MAXA>(issued - 2);  // tile 1 landed
     block_sync_tagged<1>();
 
+    // global stores of one segment's partial per wave (both formats), counted in the tile wait
+    // that follows them
+    constexpr int kPartStores = 16;
     Cursor cb = c0;
     f32x16 acc[2][4];
     int r = 0;
@@ -641,6 +644,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
                                    pack_bf16x2(o[4 * r4 + 2] * il, o[4 * r4 + 3] * il)};
                   *reinterpret_cast<MLA_LDS u32x2*>(stg + t32e * ROWB8 + 8 * (u ^ wsw)) = w;
                 }
+              static_assert(2 * 2 * 4 == kPartStores, "stores per partial (mb, half, q4)");
 #pragma unroll
               for (int q4 = 0; q4 < 4; ++q4) {  // 32 rows x 8 pieces of 16 bytes
                 const int q = q4 * 64 + lane_e, row = q >> 3, piece = q & 7;
@@ -681,6 +685,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
                 *reinterpret_cast<MLA_LDS uint64_t*>(stg + wrow + 8 * ((8 * nb + 2 * r4) ^ wsw)) =
                     (uint64_t)lo | ((uint64_t)hi2 << 32);
               }
+            static_assert(2 * 8 == kPartStores, "stores per partial (mb, q8)");
 #pragma unroll
             for (int q8 = 0; q8 < 8; ++q8) {  // 32 rows x 16 pieces of 16 bytes
               const int q = q8 * 64 + lane_e, row = q >> 4, piece = q & 15;
@@ -691,8 +696,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
             }
           }
         }
-        // tile r+2 landed (a wave that wrote a partial above has 16 stores behind the loads)
-        constexpr int kPartStores = 16;
+        // tile r+2 landed (a wave that wrote a partial above has its stores behind the loads)
         if (r + 2 < n) {
           if (k == seg - 1) wait_tiles<IPW, MAXA, kPartStores>(issued - (r + 3));
           else wait_tiles<IPW, MAXA>(issued - (r + 3));
