@@ -23,8 +23,9 @@ decompression it avoids excluded):
   F = 2 B H d_n d_c + 2 H (d_c + d_R) sumS + 2 H d_c sumS + 2 B H d_c d_v
   Bytes = sumS (d_c + d_R) 2 + 2 H d_c (d_n + d_v) + 2 B H (d_n + d_R) + 2 B H d_v
           + 4 (B max_pages + B)
-Attention kernel alone: sumS (d_c + d_R) 2 bytes of cache (1152 B per token) plus
-2 B H (d_c + d_R) bytes of queries and 4 (B max_pages + B) bytes of page table and lengths.
+Attention kernel alone (the roofline object): the cache bytes, sumS (d_c + d_R) 2 (1152 B per
+token; 644 B over the FP8 cache), the per-token figure times the tokens. The absorbed queries
+it reads (an intermediate the method makes, not an input) are not counted.
 """
 import argparse
 import ctypes
@@ -62,7 +63,7 @@ def algorithmic(inp, T=1, row_bytes=None):
     flops = 2 * Q * H * d_n * d_c + 2 * H * (d_c + d_R) * A + 2 * H * d_c * A + 2 * Q * H * d_c * d_v
     nbytes = (S * rb + 2 * H * d_c * (d_n + d_v) + 2 * Q * H * (d_n + d_R)
               + 2 * Q * H * d_v + 4 * (B * mp + B))
-    attn_bytes = S * rb + 2 * Q * H * (d_c + d_R) + 4 * (B * mp + B)
+    attn_bytes = S * rb
     attn_flops = 2 * H * (d_c + d_R) * A + 2 * H * d_c * A
     return dict(sumS=A, flops=flops, bytes=nbytes, attn_bytes=attn_bytes, attn_flops=attn_flops)
 
@@ -104,6 +105,20 @@ def source_digest():
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def measured_mfma_util(workload_name):
+    """Share of the attention kernel's time its matrix cores were busy (rocprofv3 SQ counters,
+    from the same committed record), or None as for the traffic."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(workload_name)
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("mfma_busy_share")
 
 
 def measured_traffic(workload_name):
@@ -247,8 +262,11 @@ def run(args):
     for e in ev:
         for x in e:
             hip.destroy(x)
+    util = measured_mfma_util(cfg["name"] + ("_fp8" if args.kv_fp8 else ""))
+    if util is not None:
+        res["roofline"]["mfma_util"] = util
     if not args.no_cpu and T == 1 and not args.kv_fp8:
-        res["cpu_baseline"] = cpu_baseline(base, alg)
+        res["cpu_baseline"] = cpu_baseline(base, alg, gpu_out=outs[0].float().cpu().numpy())
     else:
         res["cpu_baseline"] = None
     return res
@@ -375,9 +393,12 @@ def run_append(args):
                          "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}}
 
 
-def cpu_baseline(inp, alg, runs=3):
+def cpu_baseline(inp, alg, runs=3, gpu_out=None):
     """The fp64 oracle, as it stands, on the host cores: every (b, h) of one input set, the
-    median of `runs` runs (each run well under a minute at every workload but the longest)."""
+    median of `runs` runs (each run well under a minute at every workload but the longest).
+    With gpu_out (the timed GPU output of that same input set) the leg also reports how far it
+    is from the oracle's output: rel-L2 over the whole tensor and the largest absolute error."""
+    import numpy as np
     import oracle
     import workloads as W
     cores = len(os.sched_getaffinity(0))
@@ -385,14 +406,21 @@ def cpu_baseline(inp, alg, runs=3):
     times = []
     for _ in range(runs):
         t0 = time.perf_counter()
-        oracle.decode(*args, threads=cores)
+        ref, _ = oracle.decode(*args, threads=cores)
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[len(times) // 2]
-    return {"value": round(alg["sumS"] / dt, 1), "unit": "KV-tokens/s", "cores": cores,
-            "kind": "oracle",
-            "sample": "all %d (b,h) pairs of one input set of this workload (%d KV tokens), "
-                      "fp64, OpenMP over (b,h); median of %d runs, %.2f s wall each"
-                      % (inp["B"] * inp["H"], alg["sumS"], runs, dt)}
+    res = {"value": round(alg["sumS"] / dt, 1), "unit": "KV-tokens/s", "cores": cores,
+           "kind": "oracle",
+           "sample": "all %d (b,h) pairs of one input set of this workload (%d KV tokens), "
+                     "fp64, OpenMP over (b,h); median of %d runs, %.2f s wall each"
+                     % (inp["B"] * inp["H"], alg["sumS"], runs, dt)}
+    if gpu_out is not None:
+        g = np.asarray(gpu_out, dtype=np.float64)
+        r = np.asarray(ref, dtype=np.float64)
+        res["parity"] = {"rel_l2": float("%.3e" % (np.linalg.norm(g - r) / np.linalg.norm(r))),
+                         "max_abs": float("%.3e" % np.max(np.abs(g - r))),
+                         "of": "the GPU output of that input set, every (b, h)"}
+    return res
 
 
 def main():
@@ -418,6 +446,8 @@ def main():
     ap.add_argument("--kv-fp8", action="store_true", help="decode over an FP8 copy of the "
                     "cache with per-token scales")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--all-workloads", action="store_true", help="one JSON line for each of "
+                    "the five workloads instead of one for --workload")
     ap.add_argument("--cold-only", action="store_true", help="skip the single-set warm run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the decode, run 5 device copies of MIB MiB (a plain copy "
@@ -441,6 +471,11 @@ def main():
         res = run_append(args)
     elif args.out_proj:
         res = run_out(args)
+    elif args.all_workloads:
+        for w in (1, 2, 3, 4, 5):  # one line per workload, the headline's among them
+            args.workload = w
+            print(json.dumps(run(args)), flush=True)
+        return
     else:
         res = run(args)
     print(json.dumps(res), flush=True)
