@@ -87,14 +87,26 @@ typedef struct {
                                   MHA2MLA, one unit = one wave; 2048 for MHA2MLA with the
                                   FP8 cache, two work groups to a CU). At most 65536.      */
     int32_t q_len;             /* T: query tokens per sequence, 0 or 1 = one (plain decode),
-                                  at most 256, B*T at most 2^20. With T > 1 the T query
+                                  at most 65536, B*T at most 2^20. With T > 1 the T query
                                   tokens of sequence b are its T newest tokens, whose
-                                  [c_KV | k_R] are already in the cache (multi-token decode:
-                                  verification of drafted tokens): query token i sits at
+                                  [c_KV | k_R] are already in the cache (multi-token decode,
+                                  or the prompt of a prefill): query token i sits at
                                   position S_b - T + i and attends to tokens
                                   0 .. S_b - T + i, itself included. A query token with no
                                   token to attend to (S_b - T + i < 0) gets out = 0,
                                   lse = -inf.                                              */
+    int32_t prefill_threshold; /* T from which the call takes the decompressed branch
+                                  (bhfrc.com/news/60867 S3 and S6: the absorb/decompress split
+                                  threshold on query rows, tuned there at 128/256/512): keys
+                                  and values are expanded per head from c_KV (K_nope =
+                                  W_UK c_KV, V = W_UV^T c_KV) and attention runs at the head
+                                  widths. 0 = 256. Below it the absorbed branch serves the
+                                  call, for T up to 1024 (larger T below the threshold:
+                                  MLA_ERR_UNSUPPORTED). The decompressed branch reads a bf16
+                                  cache and writes out [B][T][H][d_v] (mla_decode,
+                                  mla_decode_timed, mla_decode_noalloc); mla_decode_out and
+                                  mla_decode_fp8 return MLA_ERR_UNSUPPORTED for it. Both
+                                  branches compute the same result up to rounding.          */
 } mla_dims_t;
 
 /* Bytes of scratch a call with these dims needs (pure function of the dims, host only), for

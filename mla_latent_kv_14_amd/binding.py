@@ -31,7 +31,7 @@ class Dims(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("num_units", ctypes.c_int32),
-                ("q_len", ctypes.c_int32)]
+                ("q_len", ctypes.c_int32), ("prefill_threshold", ctypes.c_int32)]
 
 
 class AppendDims(ctypes.Structure):
@@ -103,9 +103,10 @@ def _check(code):
 
 
 def make_dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, max_seq_len=None,
-              softmax_scale=None, num_units=0):
+              softmax_scale=None, num_units=0, prefill_threshold=0):
     """Dims of a call; q_nope [B, H, d_n] (one query token per sequence) or [B, T, H, d_n]
-    (T query tokens per sequence)."""
+    (T query tokens per sequence; from prefill_threshold on, 0 = 256, the decompressed
+    branch)."""
     if q_nope.dim() == 4:
         B, T, H, d_n = q_nope.shape
     else:
@@ -122,6 +123,7 @@ def make_dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, max_seq_len=None
     d.max_seq_len = int(max_seq_len) if max_seq_len else 0
     d.softmax_scale = float(softmax_scale) if softmax_scale else 0.0
     d.num_units = int(num_units)
+    d.prefill_threshold = int(prefill_threshold)
     return d
 
 
@@ -160,7 +162,8 @@ def _want(t, name, dtype, ndim, device):
 
 def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None, lse=None,
            max_seq_len=None, softmax_scale=None, num_units=0, workspace=None, stream=None,
-           return_lse=False, kernel_events=None, kv_scales=None, no_alloc=False):
+           return_lse=False, kernel_events=None, kv_scales=None, no_alloc=False,
+           prefill_threshold=0):
     """Absorbed MLA decode through mla_decode(). Tensors live on one HIP device.
 
     q_nope bf16 [B,H,d_n], q_rope bf16 [B,H,d_R], W_UK bf16 [H,d_n,d_c], W_UV bf16 [H,d_c,d_v],
@@ -177,6 +180,8 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
     scale.
     no_alloc: run mla_decode_noalloc, whose scratch is built into the library (no workspace;
     pass out, and lse when return_lse, so that nothing is allocated here either).
+    prefill_threshold: query tokens per sequence from which the decompressed branch serves
+    the call (0 = 256).
     """
     bf, i32 = torch.bfloat16, torch.int32
     nq = q_nope.dim() if isinstance(q_nope, torch.Tensor) else 3
@@ -196,7 +201,7 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
                          (seq_lens, "seq_lens", i32, 1)):
         _want(t, n, dt, nd, t.device)
     dims = make_dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, max_seq_len,
-                     softmax_scale, num_units)
+                     softmax_scale, num_units, prefill_threshold)
     B, H, d_v = dims.batch, dims.num_heads, dims.d_v
     d_n, d_c, d_R = dims.d_nope, dims.d_latent, dims.d_rope
     lead = (B,) if nq == 3 else (B, dims.q_len)

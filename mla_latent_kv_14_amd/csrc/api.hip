@@ -1,5 +1,7 @@
-// C ABI of libmla_decode.so: argument checks, workspace layout, work plan size and the three
-// launches (absorb -> attention -> combine) on the caller's stream. No allocation, no sync.
+// C ABI of libmla_decode.so: argument checks, workspace layout, work plan size and the
+// launches on the caller's stream: absorb -> attention -> combine for the absorbed branch, or
+// transpose -> (decompress -> attention) per group of sequences for the decompressed one. No
+// allocation, no sync.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -14,7 +16,12 @@
 
 namespace {
 
-constexpr int kMaxQLen = 256;  // query tokens per sequence
+constexpr int kMaxQLen = 65536;         // query tokens per sequence
+constexpr int kMaxAbsorbedQLen = 1024;  // of which the absorbed branch takes at most this many
+constexpr int kPrefillThreshold = 256;  // default: the decompressed branch from this many on
+// Bytes of decompressed keys and values the decompressed branch keeps for one group of
+// sequences (at least one sequence, whatever its size).
+constexpr size_t kPrefillGroupBytes = (size_t)256 << 20;
 
 thread_local char g_hip_err[256] = "";
 
@@ -48,8 +55,19 @@ mla_status_t check_dims(const mla_dims_t* d, ShapeInfo* s) {
   if ((int64_t)d->max_seq_len > (int64_t)d->max_pages_per_seq * d->page_size)
     return MLA_ERR_BAD_DIMS;
   if (d->page_size != mla::kPage) return MLA_ERR_UNSUPPORTED;
+  if (d->prefill_threshold < 0) return MLA_ERR_BAD_DIMS;
   if (!shape_of(d, s)) return MLA_ERR_UNSUPPORTED;
+  const int T = d->q_len > 1 ? d->q_len : 1;
+  const int thr = d->prefill_threshold > 0 ? d->prefill_threshold : kPrefillThreshold;
+  if (T < thr && T > kMaxAbsorbedQLen) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
+}
+
+// The decompressed branch serves the call (query tokens per sequence at or above the threshold).
+bool decompressed(const mla_dims_t* d) {
+  const int T = d->q_len > 1 ? d->q_len : 1;
+  const int thr = d->prefill_threshold > 0 ? d->prefill_threshold : kPrefillThreshold;
+  return T >= thr;
 }
 
 // Query tokens per sequence (0 in the dims means 1).
@@ -89,6 +107,28 @@ struct Layout {
   size_t plan, q_abs, part_lse, part_o, total;
 };
 
+// Workspace of the decompressed branch: the MLA_CHECK flag, W_UV transposed, and the
+// decompressed keys and values of one group of sequences.
+struct PrefillLayout {
+  size_t flag, wuvt, kbuf, vbuf, total;
+  int group;
+};
+
+PrefillLayout prefill_layout(const mla_dims_t* d, const ShapeInfo& s) {
+  const size_t smax = (size_t)max_len(d);
+  const size_t per_seq = smax * s.H * (s.DN + s.DV) * 2;
+  size_t g = per_seq > 0 ? kPrefillGroupBytes / per_seq : 1;
+  g = g < 1 ? 1 : (g > (size_t)d->batch ? (size_t)d->batch : g);
+  PrefillLayout L;
+  L.group = (int)g;
+  L.flag = 0;
+  L.wuvt = 256;
+  L.kbuf = L.wuvt + align256((size_t)s.H * s.DV * s.DC * 2);
+  L.vbuf = L.kbuf + align256(g * smax * s.H * s.DN * 2);
+  L.total = L.vbuf + align256(g * smax * s.H * s.DV * 2);
+  return L;
+}
+
 Layout layout(const mla_dims_t* d, const ShapeInfo& s, bool fp8) {
   const size_t B = (size_t)rows(d), slots = (size_t)plan_units(d, s, fp8) + B;
   Layout L;
@@ -115,6 +155,7 @@ extern "C" {
 size_t mla_decode_workspace_bytes(const mla_dims_t* dims) {
   ShapeInfo s;
   if (check_dims(dims, &s) != MLA_OK) return 0;
+  if (decompressed(dims)) return prefill_layout(dims, s).total;
   // enough for either cache format (the FP8 one may use more plan units)
   const size_t a = layout(dims, s, false).total;
   if (s.shape != mla::kShapeMha2Mla) return a;
@@ -151,16 +192,20 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
       (workspace && ((uintptr_t)workspace & 255) != 0))
     return MLA_ERR_MISALIGNED;
   const bool fp8 = kv_scales != nullptr;
-  const Layout L = layout(dims, s, fp8);
-  if (!workspace || workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  const bool prefill = decompressed(dims);
+  // the decompressed branch reads a bf16 cache and writes the per-head output
+  if (prefill && (fp8 || hidden > 0)) return MLA_ERR_UNSUPPORTED;
+  const Layout L = prefill ? Layout{} : layout(dims, s, fp8);
+  const PrefillLayout PL = prefill ? prefill_layout(dims, s) : PrefillLayout{};
+  if (!workspace || workspace_bytes < (prefill ? PL.total : L.total)) return MLA_ERR_WORKSPACE;
 
   const hipStream_t hs = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const int B = dims->batch, mp = dims->max_pages_per_seq, T = q_len(dims), R = B * T;
   if (check_mode()) {
-    // validate the device-resident inputs first; the flag lives in the query region, which
-    // the decode overwrites afterwards
-    int* flag = (int*)(ws + L.q_abs);
+    // validate the device-resident inputs first; the flag lives in a region the decode
+    // overwrites afterwards (the queries, or the branch's own flag word)
+    int* flag = (int*)(ws + (prefill ? PL.flag : L.q_abs));
     int host_flag = 0;
     st = hip_status(mla::launch_check(seq_lens, page_table, B, mp, dims->num_pages,
                                       max_len(dims), kv_scales, flag, hs));
@@ -170,10 +215,29 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
     if ((st = hip_status(hipStreamSynchronize(hs))) != MLA_OK) return st;
     if (host_flag != 0) return MLA_ERR_DEVICE_CHECK;
   }
-  const int G = plan_units(dims, s, fp8);
   const float scale = dims->softmax_scale > 0.f ? dims->softmax_scale
                                                 : 1.0f / sqrtf((float)(s.DN + s.DR));
   const float scale_log2 = scale * mla::kLog2e;
+  if (prefill) {
+    // stage events: 0/1 and 4/5 mark one point each (no absorb or combine kernel), 2/3 bracket
+    // the branch's kernels
+    auto record = [&](int k) -> mla_status_t {
+      if (!stage_events || !stage_events[k]) return MLA_OK;
+      return hip_status(hipEventRecord((hipEvent_t)stage_events[k], hs));
+    };
+    for (int k = 0; k < 3; ++k)
+      if ((st = record(k)) != MLA_OK) return st;
+    st = hip_status(mla::launch_prefill(s.shape, q_nope, q_rope, W_UK, W_UV, kv_pages,
+                                        page_table, seq_lens, B, T, mp, dims->num_pages,
+                                        max_len(dims), PL.group, scale_log2, ws + PL.wuvt,
+                                        ws + PL.kbuf, ws + PL.vbuf, out, lse_out,
+                                        mla::Launch{hs}));
+    if (st != MLA_OK) return st;
+    for (int k = 3; k < 6; ++k)
+      if ((st = record(k)) != MLA_OK) return st;
+    return MLA_OK;
+  }
+  const int G = plan_units(dims, s, fp8);
   // stage_events: start and end of each kernel's own execution (bound to the kernels)
   auto ctx = [&](int k) {
     mla::Launch L{hs};

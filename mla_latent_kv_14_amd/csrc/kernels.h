@@ -49,6 +49,16 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
                             float scale_log2, void* part_o, float* part_lse,
                             const float* kv_scales, const Launch& L);
 
+// The decompressed branch for T query tokens per sequence at or above the prefill threshold:
+// W_UV transposed into W_UVt [H][d_v][d_c], then per group of `group` sequences the
+// decompression of their cached tokens into kbuf [group][smax][H][d_nope] and vbuf
+// [group][smax][H][d_v], and causal attention over them into out [B][T][H][d_v] and lse.
+hipError_t launch_prefill(int shape, const void* q_nope, const void* q_rope, const void* W_UK,
+                          const void* W_UV, const void* kv, const int32_t* page_table,
+                          const int32_t* seq_lens, int B, int T, int max_pages, int num_pages,
+                          int smax, int group, float scale_log2, void* W_UVt, void* kbuf,
+                          void* vbuf, void* out, float* lse_out, const Launch& L);
+
 hipError_t launch_combine(int shape, const void* part_o, const float* part_lse, const void* plan,
                           const int32_t* seq_lens, const void* W_UV, void* out, float* lse_out,
                           int B, int H, int max_pages, const Launch& L);

@@ -81,12 +81,54 @@ def test_workspace_bytes_closed_form():
     ("max_pages_per_seq", 0, "MLA_ERR_BAD_DIMS"), ("num_pages", 0, "MLA_ERR_BAD_DIMS"),
     ("max_seq_len", 64 * 64 + 1, "MLA_ERR_BAD_DIMS"), ("num_units", -1, "MLA_ERR_BAD_DIMS"),
     ("num_units", 65537, "MLA_ERR_BAD_DIMS"), ("q_len", -1, "MLA_ERR_BAD_DIMS"),
-    ("q_len", 257, "MLA_ERR_BAD_DIMS")])
+    ("q_len", 65537, "MLA_ERR_BAD_DIMS"), ("prefill_threshold", -1, "MLA_ERR_BAD_DIMS")])
 def test_bad_dims(field, value, status):
     d = ds_dims(max_seq_len=0)  # 0: bounded by the page table alone
     setattr(d, field, value)
     assert M.workspace_bytes(d) == 0
     assert call(d) == STATUS_CODE[status]
+
+
+def test_prefill_workspace_and_limits():
+    al = lambda x: (x + 255) // 256 * 256
+    # q_len at the threshold (256 by default): the decompressed branch's workspace, a flag
+    # word, W_UV transposed, and the keys and values of one group of sequences (as many as fit
+    # in 256 MiB of them, at least one)
+    d = ds_dims(B=4, max_pages=16, num_pages=64, max_seq_len=1024)
+    d.q_len = 256
+    per_seq = 1024 * 128 * (128 + 128) * 2  # 64 MiB
+    g = 4
+    assert M.workspace_bytes(d) == 256 + al(128 * 128 * 512 * 2) + al(g * 1024 * 128 * 128 * 2) \
+        + al(g * 1024 * 128 * 128 * 2)
+    d.max_seq_len = 4096
+    d.max_pages_per_seq = 64
+    g = 1  # 256 MiB per sequence
+    assert M.workspace_bytes(d) == 256 + al(128 * 128 * 512 * 2) + 2 * al(g * 4096 * 128 * 128 * 2)
+    prefill_bytes = M.workspace_bytes(d)
+    # one token below the threshold: the absorbed branch's workspace (1020 virtual rows)
+    d.q_len = 255
+    slots = 128 + 4 * 255
+    plan = (16 + 4 * 1020 + 31) // 32 * 32 + 32 * 128
+    assert M.workspace_bytes(d) == al(plan) + al(1020 * 128 * 512 * 2) + al(slots * 128 * 4) \
+        + al(slots * 128 * 512 * 2)
+    # the threshold moves: q_len 255 from threshold 128 on is decompressed
+    d.prefill_threshold = 128
+    assert M.workspace_bytes(d) == prefill_bytes
+    # below the threshold the absorbed branch takes at most 1024 query tokens
+    d.prefill_threshold = 4096
+    d.q_len = 1025
+    assert M.workspace_bytes(d) == 0 and call(d) == STATUS_CODE["MLA_ERR_UNSUPPORTED"]
+    # the decompressed branch reads a bf16 cache and writes per-head outputs
+    d = ds_dims(B=2, max_pages=16, num_pages=64, max_seq_len=1024)
+    d.q_len = 300
+    p = [_al(k + 1) for k in range(5)] + [_al(6)] + [_al(k + 7) for k in range(3)]
+    assert M.lib().mla_decode_fp8(ctypes.byref(d), *p, ctypes.c_void_p(0), _al(10),
+                                  M.workspace_bytes(d), ctypes.c_void_p(0), None) == \
+        STATUS_CODE["MLA_ERR_UNSUPPORTED"]
+    q = [_al(k + 1) for k in range(9)]
+    assert M.lib().mla_decode_out(ctypes.byref(d), 1024, *q[:8], ctypes.c_void_p(0), _al(10),
+                                  M.workspace_bytes(d), ctypes.c_void_p(0)) == \
+        STATUS_CODE["MLA_ERR_UNSUPPORTED"]
 
 
 def test_null_dims_and_pointers():
