@@ -173,7 +173,7 @@ def run(args):
         sets.append({k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()})
     d0 = sets[0]
     dims = M.make_dims(d0["q_nope"], d0["q_rope"], d0["W_UK"], d0["W_UV"], d0["kv_pages"],
-                       d0["page_table"])
+                       d0["page_table"], prefill_threshold=args.prefill_threshold)
     ws_bytes = M.workspace_bytes(dims)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     outs = [torch.empty(((d["B"],) if T == 1 else (d["B"], T)) + (d["H"], d["d_v"]),
@@ -244,6 +244,8 @@ def run(args):
                    "d_rope": cfg["d_R"], "d_v": cfg["d_v"], "page_size": 64,
                    "page_table": cfg["layout"], "input_sets_rotated": n_sets,
                    "query_tokens_per_seq": T,
+                   "branch": "decompressed" if T >= (args.prefill_threshold or 256)
+                             else "absorbed",
                    "kv_cache": ("fp8_e4m3 c_KV + bf16 k_R + fp32 scale per token, %d B"
                                 % fp8_row) if args.kv_fp8 else "bf16"},
         "tflops": round(alg["flops"] / sec / 1e12, 2),
@@ -438,6 +440,8 @@ def main():
     ap.add_argument("--q-len", type=int, default=1, help="query tokens per sequence (the "
                     "sequence's newest tokens, causal among themselves); with more than one, "
                     "value counts (query token, cached token) pairs per second")
+    ap.add_argument("--prefill-threshold", type=int, default=0, help="query tokens per "
+                    "sequence from which the decompressed branch serves the call (0 = 256)")
     ap.add_argument("--out-proj", type=int, default=0, metavar="HIDDEN",
                     help="time mla_decode_out (merged W_UV W_O to width HIDDEN) instead")
     ap.add_argument("--append", action="store_true", help="time the cache append "

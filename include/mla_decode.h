@@ -100,13 +100,15 @@ typedef struct {
                                   threshold on query rows, tuned there at 128/256/512): keys
                                   and values are expanded per head from c_KV (K_nope =
                                   W_UK c_KV, V = W_UV^T c_KV) and attention runs at the head
-                                  widths. 0 = 256. Below it the absorbed branch serves the
-                                  call, for T up to 1024 (larger T below the threshold:
-                                  MLA_ERR_UNSUPPORTED). The decompressed branch reads a bf16
-                                  cache and writes out [B][T][H][d_v] (mla_decode,
-                                  mla_decode_timed, mla_decode_noalloc); mla_decode_out and
-                                  mla_decode_fp8 return MLA_ERR_UNSUPPORTED for it. Both
-                                  branches compute the same result up to rounding.          */
+                                  widths. 0 = the default: 256 at the DeepSeek widths, never
+                                  at the MHA2MLA widths (their latent is narrower than a
+                                  head's key, so expanding never saves work). Below it the
+                                  absorbed branch serves the call. The decompressed branch
+                                  reads a bf16 cache and writes out [B][T][H][d_v]
+                                  (mla_decode, mla_decode_timed, mla_decode_noalloc);
+                                  mla_decode_out and mla_decode_fp8 return
+                                  MLA_ERR_UNSUPPORTED for it. Both branches compute the same
+                                  result up to rounding.                                    */
 } mla_dims_t;
 
 /* Bytes of scratch a call with these dims needs (pure function of the dims, host only), for

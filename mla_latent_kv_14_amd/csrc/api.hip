@@ -17,11 +17,12 @@
 namespace {
 
 constexpr int kMaxQLen = 65536;         // query tokens per sequence
-constexpr int kMaxAbsorbedQLen = 1024;  // of which the absorbed branch takes at most this many
-constexpr int kPrefillThreshold = 256;  // default: the decompressed branch from this many on
+constexpr int kPrefillThreshold = 256;  // DeepSeek widths, default: decompressed from here on
 // Bytes of decompressed keys and values the decompressed branch keeps for one group of
-// sequences (at least one sequence, whatever its size).
-constexpr size_t kPrefillGroupBytes = (size_t)256 << 20;
+// sequences (at least one sequence, whatever its size). Measured at B = 16, S = 4096, T = 256
+// (DeepSeek widths): one sequence per group (256 MiB) took 9.1 ms, four (1 GiB) 6.8 ms; the
+// attention grid of a group needs several sequences to fill the chip.
+constexpr size_t kPrefillGroupBytes = (size_t)1024 << 20;
 
 thread_local char g_hip_err[256] = "";
 
@@ -57,17 +58,17 @@ mla_status_t check_dims(const mla_dims_t* d, ShapeInfo* s) {
   if (d->page_size != mla::kPage) return MLA_ERR_UNSUPPORTED;
   if (d->prefill_threshold < 0) return MLA_ERR_BAD_DIMS;
   if (!shape_of(d, s)) return MLA_ERR_UNSUPPORTED;
-  const int T = d->q_len > 1 ? d->q_len : 1;
-  const int thr = d->prefill_threshold > 0 ? d->prefill_threshold : kPrefillThreshold;
-  if (T < thr && T > kMaxAbsorbedQLen) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
-// The decompressed branch serves the call (query tokens per sequence at or above the threshold).
+// The decompressed branch serves the call: query tokens per sequence at or above the
+// threshold. By default 256 at the DeepSeek widths; never at the MHA2MLA widths, whose latent
+// (64) is narrower than a head's key (d_nope + d_rope = 128), so that expanding the cache per
+// head costs more work at every T than scoring in the latent space.
 bool decompressed(const mla_dims_t* d) {
   const int T = d->q_len > 1 ? d->q_len : 1;
-  const int thr = d->prefill_threshold > 0 ? d->prefill_threshold : kPrefillThreshold;
-  return T >= thr;
+  if (d->prefill_threshold > 0) return T >= d->prefill_threshold;
+  return d->num_heads == 128 && T >= kPrefillThreshold;
 }
 
 // Query tokens per sequence (0 in the dims means 1).

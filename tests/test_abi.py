@@ -93,17 +93,17 @@ def test_prefill_workspace_and_limits():
     al = lambda x: (x + 255) // 256 * 256
     # q_len at the threshold (256 by default): the decompressed branch's workspace, a flag
     # word, W_UV transposed, and the keys and values of one group of sequences (as many as fit
-    # in 256 MiB of them, at least one)
+    # in 1 GiB of them, at least one)
     d = ds_dims(B=4, max_pages=16, num_pages=64, max_seq_len=1024)
     d.q_len = 256
     per_seq = 1024 * 128 * (128 + 128) * 2  # 64 MiB
     g = 4
     assert M.workspace_bytes(d) == 256 + al(128 * 128 * 512 * 2) + al(g * 1024 * 128 * 128 * 2) \
         + al(g * 1024 * 128 * 128 * 2)
-    d.max_seq_len = 4096
-    d.max_pages_per_seq = 64
-    g = 1  # 256 MiB per sequence
-    assert M.workspace_bytes(d) == 256 + al(128 * 128 * 512 * 2) + 2 * al(g * 4096 * 128 * 128 * 2)
+    d.max_seq_len = 8192
+    d.max_pages_per_seq = 128
+    g = 2  # 512 MiB per sequence
+    assert M.workspace_bytes(d) == 256 + al(128 * 128 * 512 * 2) + 2 * al(g * 8192 * 128 * 128 * 2)
     prefill_bytes = M.workspace_bytes(d)
     # one token below the threshold: the absorbed branch's workspace (1020 virtual rows)
     d.q_len = 255
@@ -114,10 +114,13 @@ def test_prefill_workspace_and_limits():
     # the threshold moves: q_len 255 from threshold 128 on is decompressed
     d.prefill_threshold = 128
     assert M.workspace_bytes(d) == prefill_bytes
-    # below the threshold the absorbed branch takes at most 1024 query tokens
-    d.prefill_threshold = 4096
-    d.q_len = 1025
-    assert M.workspace_bytes(d) == 0 and call(d) == STATUS_CODE["MLA_ERR_UNSUPPORTED"]
+    # MHA2MLA widths: absorbed at any T unless a threshold is set
+    d = m2_dims(B=2, max_pages=16, num_pages=64, max_seq_len=1024)
+    d.q_len = 300
+    absorbed = M.workspace_bytes(d)
+    d.prefill_threshold = 256
+    assert M.workspace_bytes(d) == 256 + al(32 * 128 * 64 * 2) + al(2 * 1024 * 32 * 120 * 2) \
+        + al(2 * 1024 * 32 * 128 * 2) != absorbed
     # the decompressed branch reads a bf16 cache and writes per-head outputs
     d = ds_dims(B=2, max_pages=16, num_pages=64, max_seq_len=1024)
     d.q_len = 300

@@ -88,9 +88,13 @@ def _check(M, inp, label, **kw):
 
 @pytest.mark.parametrize("T", [1, 2, 16, 255, 256, 257, 512])
 def test_mha2mla_across_the_threshold(M, T):
-    # lengths: longer than T, equal to T, and shorter than T (its first rows attend to nothing)
+    # lengths: longer than T, equal to T, and shorter than T (its first rows attend to nothing);
+    # at these widths the decompressed branch runs only with a threshold set (here 256)
     inp = _inp(M2, [T + 700, T, max(1, T // 2), T + 65], T, 10 + T)
-    _check(M, inp, "mha2mla T=%d (%s branch)" % (T, "decompressed" if T >= 256 else "absorbed"))
+    _check(M, inp, "mha2mla T=%d (%s branch)" % (T, "decompressed" if T >= 256 else "absorbed"),
+           prefill_threshold=256)
+    if T == 512:  # and without it, the absorbed branch serves any T
+        _check(M, inp, "mha2mla T=512 absorbed")
 
 
 @pytest.mark.parametrize("T", [256, 300])
@@ -101,10 +105,10 @@ def test_deepseek_decompressed(M, T):
 
 @pytest.mark.parametrize("dims", [DS, M2], ids=["deepseek", "mha2mla"])
 def test_threshold_moves_the_branch(M, dims):
-    # T = 200 decoded by both branches: absorbed at the default threshold, decompressed from a
-    # threshold of 128 on; T = 300 the other way round with a threshold of 512. All four are
-    # held to the oracle, and each pair agrees within the same bound.
-    for T, lo, hi in ((200, 128, 0), (300, 0, 512)):
+    # T = 200 and T = 300 each decoded by both branches: decompressed from a threshold at or
+    # below T, absorbed with one above it. All four are held to the oracle, and each pair
+    # agrees within the same bound.
+    for T, lo, hi in ((200, 128, 1024), (300, 256, 512)):
         inp = _inp(dims, [T + 90, T + 1], T, 30 + T)
         a = _check(M, inp, "T=%d threshold %d" % (T, lo), prefill_threshold=lo)
         b = _check(M, inp, "T=%d threshold %d" % (T, hi), prefill_threshold=hi)
@@ -121,12 +125,12 @@ def test_single_token_rows_through_the_decompressed_branch(M):
 
 
 def test_deepseek_prefill_groups(M):
-    # more sequences than one group holds (256 MiB of decompressed keys and values: at
-    # max_seq_len 4096 one sequence per group), so the branch loops over groups. Checked on
+    # more sequences than one group holds (1 GiB of decompressed keys and values: at
+    # max_seq_len 16384 one sequence per group), so the branch loops over groups. Checked on
     # sampled (sequence, row, head) triples: row i of sequence b is the single-token decode
     # over its first S_b - T + 1 + i tokens.
     T = 256
-    lens = [4096, 300, 2000]
+    lens = [16384, 300, 2000]
     inp = _inp(DS, lens, T, 51)
     say("deepseek prefill groups")
     d = to_dev(inp)
@@ -145,7 +149,7 @@ def test_deepseek_prefill_groups(M):
 
 
 def test_timed_entry_point_brackets_the_branch(M):
-    inp = _inp(M2, [800, 400], 256, 61)
+    inp = _inp(DS, [800, 400], 256, 61)
     d = to_dev(inp)
     hip = HipEvents()
     ev = [hip.create() for _ in range(6)]
