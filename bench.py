@@ -354,11 +354,16 @@ def run_append(args):
     x = torch.randn(B, T, hidden, generator=g).to(torch.bfloat16).to(dev)
     Wd = (torch.randn(d_c, hidden, generator=g) / hidden ** 0.5).to(torch.bfloat16).to(dev)
     Wr = (torch.randn(d_R, hidden, generator=g) / hidden ** 0.5).to(torch.bfloat16).to(dev)
-    kv = inp["kv_pages"].to(dev)
+    sc = None
+    if args.kv_fp8:  # append into an FP8 copy of the cache
+        kv8, sc8 = W.fp8_cache(inp, seed=cfg["seed"] + 8)
+        kv, sc = kv8.to(dev), sc8.to(dev)
+    else:
+        kv = inp["kv_pages"].to(dev)
     pt = inp["page_table"].to(dev)
     # room for the new tokens: append before each sequence's last T tokens
     before = (inp["seq_lens"] - T).clamp(min=0).to(torch.int32).to(dev)
-    M.cache_append(x, Wd, Wr, kv, pt, before)  # checks the arguments once
+    M.cache_append(x, Wd, Wr, kv, pt, before, kv_scales=sc)  # checks the arguments once
     # then the C entry point directly, with prebuilt arguments (per-call Python checks would
     # make the loop host-bound)
     lib = M.lib()
@@ -368,27 +373,33 @@ def run_append(args):
     d.rope_base = 10000.0
     stream = torch.cuda.current_stream(dev)
     vp = ctypes.c_void_p
+    wsb = M.binding.append_workspace_bytes(d)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     call = [ctypes.byref(d)] + [vp(t.data_ptr()) for t in (x, Wd, Wr, pt, before, kv)] + \
-        [vp(stream.cuda_stream)]
+        ([vp(sc.data_ptr())] if sc is not None else []) + \
+        [vp(ws.data_ptr()), ctypes.c_size_t(wsb), vp(stream.cuda_stream)]
+    entry = lib.mla_cache_append_fp8 if sc is not None else lib.mla_cache_append
     for _ in range(args.warmup):
-        lib.mla_cache_append(*call)
+        entry(*call)
     hip = Hip()
     e0, e1 = hip.event(), hip.event()
     hip.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     torch.cuda.synchronize()
     hip.L.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
     for _ in range(args.steps):
-        if lib.mla_cache_append(*call) != 0:
+        if entry(*call) != 0:
             raise RuntimeError("mla_cache_append failed")
     hip.L.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     us = hip.ms(e0, e1) * 1e3 / args.steps
-    nbytes = 2 * (d_c + d_R) * hidden + 2 * B * T * hidden + 2 * B * T * (d_c + d_R)
+    row = (d_c + 2 * d_R + 4) if sc is not None else 2 * (d_c + d_R)
+    nbytes = 2 * (d_c + d_R) * hidden + 2 * B * T * hidden + B * T * row
     return {"metric": "MLA cache append (c_KV = x W_DKV, RoPE(x W_KR)) per call",
             "value": round(us, 3), "unit": "us", "higher_is_better": False,
             "steps": args.steps, "warmup": args.warmup,
             "config": {"workload": cfg["name"], "batch": B, "new_tokens_per_seq": T,
-                       "hidden": hidden, "d_latent": d_c, "d_rope": d_R},
+                       "hidden": hidden, "d_latent": d_c, "d_rope": d_R,
+                       "kv_cache": "fp8" if sc is not None else "bf16"},
             "gbps": round(nbytes / us / 1e3, 1),
             "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",

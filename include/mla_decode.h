@@ -242,9 +242,11 @@ mla_status_t mla_decode_out(const mla_dims_t* dims, int32_t hidden, const void* 
  * the host, synchronises the stream, and returns MLA_ERR_DEVICE_CHECK (writing nothing) when
  * an S_b is outside [0, max_pages_per_seq * 64] or such an entry of a new token is outside
  * the pool. Sizes: hidden a multiple of 1024, d_latent and d_rope multiples of 4, B*T at most
- * 2^20. Same conventions as above otherwise (enqueued on `stream`, no allocation, argument
- * errors before anything is enqueued). The decode's q_rope must be rotated with the same
- * pairing and base.
+ * 2^20, d_latent at most 1024, d_rope at most 512. The workspace (256-byte aligned, at least
+ * mla_cache_append_workspace_bytes) holds fp32 partial sums; the caller owns it and may reuse
+ * it between calls. Same conventions as above otherwise (enqueued on `stream`, no allocation,
+ * argument errors before anything is enqueued). The decode's q_rope must be rotated with the
+ * same pairing and base.
  */
 typedef struct {
     int32_t batch;             /* B sequences                                               */
@@ -258,9 +260,30 @@ typedef struct {
     float rope_base;           /* RoPE base; <= 0 means 10000                               */
 } mla_append_dims_t;
 
+/* Bytes of scratch mla_cache_append and mla_cache_append_fp8 need for these dims (fp32
+ * partial rows of the contraction, split over the model width); 0 if the dims are invalid. */
+size_t mla_cache_append_workspace_bytes(const mla_append_dims_t* dims);
+
 mla_status_t mla_cache_append(const mla_append_dims_t* dims, const void* x, const void* W_DKV,
                               const void* W_KR, const int32_t* page_table,
-                              const int32_t* seq_lens, void* kv_pages, void* stream);
+                              const int32_t* seq_lens, void* kv_pages, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * The same append into an FP8 cache (the layout mla_decode_fp8 reads): kv_pages uint8
+ * [num_pages, 64, d_latent + 2*d_rope] with rows [c_KV as E4M3 bytes | k_R as bf16], and
+ * kv_scales fp32 [num_pages, 64]. For each new token the scale is the smallest power of two
+ * 2^e with max_c |c_KV[c]| <= 448 * 2^e (448 is the largest E4M3 value; e kept within
+ * -126 .. 127, 1 for an all-zero row), and byte c is c_KV[c] / 2^e rounded to the nearest E4M3
+ * value, ties to even (c_KV as fp32 sums, not rounded to bf16 first). k_R is rotated and
+ * rounded to bf16 as above. Everything else is as for mla_cache_append; kv_scales must be
+ * non-NULL and 16-byte aligned.
+ */
+mla_status_t mla_cache_append_fp8(const mla_append_dims_t* dims, const void* x,
+                                  const void* W_DKV, const void* W_KR,
+                                  const int32_t* page_table, const int32_t* seq_lens,
+                                  void* kv_pages, float* kv_scales, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Logical copy of the paged cache, through the same page addressing and LDS staging the

@@ -75,7 +75,11 @@ def lib():
         L.mla_decode_out.restype = c_int
         L.mla_decode_out.argtypes = [dp, ctypes.c_int32] + [vp] * 10 + [sz, vp]
         L.mla_cache_append.restype = c_int
-        L.mla_cache_append.argtypes = [ctypes.POINTER(AppendDims)] + [vp] * 7
+        L.mla_cache_append.argtypes = [ctypes.POINTER(AppendDims)] + [vp] * 7 + [sz, vp]
+        L.mla_cache_append_fp8.restype = c_int
+        L.mla_cache_append_fp8.argtypes = [ctypes.POINTER(AppendDims)] + [vp] * 8 + [sz, vp]
+        L.mla_cache_append_workspace_bytes.restype = sz
+        L.mla_cache_append_workspace_bytes.argtypes = [ctypes.POINTER(AppendDims)]
         L.mla_gather_pages.restype = c_int
         L.mla_gather_pages.argtypes = [dp, vp, vp, vp, vp, vp]
         L.mla_status_str.restype = ctypes.c_char_p
@@ -323,20 +327,27 @@ def decode_out(q_nope, q_rope, W_UK, W_UVO, kv_pages, page_table, seq_lens, out=
     return (out, lse) if return_lse else out
 
 
+def append_workspace_bytes(d):
+    return int(lib().mla_cache_append_workspace_bytes(ctypes.byref(d)))
+
+
 def cache_append(x, W_DKV, W_KR, kv_pages, page_table, seq_lens, rope_base=10000.0,
-                 stream=None):
+                 stream=None, kv_scales=None, workspace=None):
     """Writes [c_KV | RoPE(k_R)] of the new tokens into kv_pages in place (mla_cache_append).
 
     x bf16 [B,T,hidden] (or [B,hidden] for one token), W_DKV bf16 [d_c,hidden], W_KR bf16
     [d_R,hidden], kv_pages bf16 [P,64,d_c+d_R], page_table int32 [B,max_pages], seq_lens int32
     [B] (tokens already cached; token i of sequence b goes to position seq_lens[b] + i).
+    kv_scales: an FP8 cache (mla_cache_append_fp8): kv_pages uint8 [P,64,d_c+2*d_R] and
+    kv_scales fp32 [P,64], both written at the new tokens' slots. workspace: a uint8 tensor of
+    at least mla_cache_append_workspace_bytes (allocated here when None).
     """
     bf = torch.bfloat16
     dev = kv_pages.device
     _want(x, "x", bf, x.dim() if x.dim() in (2, 3) else 3, x.device)
     _want(W_DKV, "W_DKV", bf, 2, W_DKV.device)
     _want(W_KR, "W_KR", bf, 2, W_KR.device)
-    _want(kv_pages, "kv_pages", bf, 3, dev)
+    _want(kv_pages, "kv_pages", bf if kv_scales is None else torch.uint8, 3, dev)
     _want(page_table, "page_table", torch.int32, 2, page_table.device)
     _want(seq_lens, "seq_lens", torch.int32, 1, seq_lens.device)
     d = AppendDims()
@@ -346,22 +357,35 @@ def cache_append(x, W_DKV, W_KR, kv_pages, page_table, seq_lens, rope_base=10000
     d.d_latent, d.d_rope = W_DKV.shape[0], W_KR.shape[0]
     _shape(W_DKV, "W_DKV", (d.d_latent, d.hidden))
     _shape(W_KR, "W_KR", (d.d_rope, d.hidden))
-    _shape(kv_pages, "kv_pages", (kv_pages.shape[0], kv_pages.shape[1], d.d_latent + d.d_rope))
+    row = d.d_latent + d.d_rope if kv_scales is None else d.d_latent + 2 * d.d_rope
+    _shape(kv_pages, "kv_pages", (kv_pages.shape[0], kv_pages.shape[1], row))
     _shape(page_table, "page_table", (d.batch, page_table.shape[1]))
     _shape(seq_lens, "seq_lens", (d.batch,))
+    if kv_scales is not None:
+        _want(kv_scales, "kv_scales", torch.float32, 2, kv_scales.device)
+        _shape(kv_scales, "kv_scales", tuple(kv_pages.shape[:2]))
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or
+                                  not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor")
     if dev.type != "cuda":
         raise ValueError("the cache append runs on a HIP device; got %s" % dev)
     for t, n in ((x, "x"), (W_DKV, "W_DKV"), (W_KR, "W_KR"), (page_table, "page_table"),
-                 (seq_lens, "seq_lens")):
-        if t.device != dev:
+                 (seq_lens, "seq_lens"), (kv_scales, "kv_scales"), (workspace, "workspace")):
+        if t is not None and t.device != dev:
             raise ValueError("%s is on %s, expected %s" % (n, t.device, dev))
     d.page_size = kv_pages.shape[1]
     d.max_pages_per_seq = page_table.shape[1]
     d.num_pages = kv_pages.shape[0]
     d.rope_base = float(rope_base)
-    _check(lib().mla_cache_append(ctypes.byref(d), _ptr(x), _ptr(W_DKV), _ptr(W_KR),
-                                  _ptr(page_table), _ptr(seq_lens), _ptr(kv_pages),
-                                  _stream(stream, dev)))
+    if workspace is None:
+        workspace = torch.empty(max(append_workspace_bytes(d), 1), dtype=torch.uint8, device=dev)
+    args = (ctypes.byref(d), _ptr(x), _ptr(W_DKV), _ptr(W_KR), _ptr(page_table),
+            _ptr(seq_lens), _ptr(kv_pages))
+    tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
+    if kv_scales is None:
+        _check(lib().mla_cache_append(*args, *tail))
+    else:
+        _check(lib().mla_cache_append_fp8(*args, _ptr(kv_scales), *tail))
     return kv_pages
 
 

@@ -380,9 +380,12 @@ mla_status_t mla_gather_pages(const mla_dims_t* dims, const void* kv_pages,
                                        (hipStream_t)stream));
 }
 
-mla_status_t mla_cache_append(const mla_append_dims_t* d, const void* x, const void* W_DKV,
-                              const void* W_KR, const int32_t* page_table,
-                              const int32_t* seq_lens, void* kv_pages, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of the append's dims; fills T.
+mla_status_t check_append_dims(const mla_append_dims_t* d, int* T_out) {
   if (!d) return MLA_ERR_NULL_ARG;
   const int T = d->q_len > 1 ? d->q_len : 1;
   if (d->batch < 1 || d->q_len < 0 || (int64_t)d->batch * T > (1 << 20) || d->hidden < 1 ||
@@ -390,21 +393,34 @@ mla_status_t mla_cache_append(const mla_append_dims_t* d, const void* x, const v
       (int64_t)d->batch * d->max_pages_per_seq > (int64_t)1 << 29 || d->page_size < 1)
     return MLA_ERR_BAD_DIMS;
   if (d->page_size != mla::kPage || d->hidden % 1024 != 0 || d->hidden > (1 << 20) ||
-      d->d_latent % 4 != 0 || d->d_rope % 4 != 0)
+      d->d_latent % 4 != 0 || d->d_rope % 4 != 0 || d->d_latent > 1024 || d->d_rope > 512)
     return MLA_ERR_UNSUPPORTED;
+  *T_out = T;
+  return MLA_OK;
+}
+
+mla_status_t append_call(const mla_append_dims_t* d, const void* x, const void* W_DKV,
+                         const void* W_KR, const int32_t* page_table, const int32_t* seq_lens,
+                         void* kv_pages, float* kv_scales, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int T = 1;
+  mla_status_t st = check_append_dims(d, &T);
+  if (st != MLA_OK) return st;
   if (!x || !W_DKV || !W_KR || !page_table || !seq_lens || !kv_pages) return MLA_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(W_DKV) || !aligned16(W_KR) || !aligned16(page_table) ||
-      !aligned16(seq_lens) || !aligned16(kv_pages))
+      !aligned16(seq_lens) || !aligned16(kv_pages) || (kv_scales && !aligned16(kv_scales)) ||
+      (workspace && ((uintptr_t)workspace & 255) != 0))
     return MLA_ERR_MISALIGNED;
+  const size_t need = mla::append_workspace_bytes(d->batch * T, d->hidden, d->d_latent, d->d_rope);
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   const hipStream_t hs = (hipStream_t)stream;
   if (check_mode()) {
-    // validate on the host (the append takes no workspace for a device flag): every S_b in
-    // [0, max_pages_per_seq * 64], and the page-table entry of every new token that falls
-    // inside its row in [0, num_pages)
+    // validate on the host: every S_b in [0, max_pages_per_seq * 64], and the page-table
+    // entry of every new token that falls inside its row in [0, num_pages)
     const int B = d->batch, mp = d->max_pages_per_seq;
     std::vector<int32_t> lens(B), table((size_t)B * mp);
-    mla_status_t st = hip_status(hipMemcpyAsync(lens.data(), seq_lens, sizeof(int32_t) * B,
-                                                hipMemcpyDeviceToHost, hs));
+    st = hip_status(hipMemcpyAsync(lens.data(), seq_lens, sizeof(int32_t) * B,
+                                   hipMemcpyDeviceToHost, hs));
     if (st == MLA_OK)
       st = hip_status(hipMemcpyAsync(table.data(), page_table, sizeof(int32_t) * table.size(),
                                      hipMemcpyDeviceToHost, hs));
@@ -421,9 +437,36 @@ mla_status_t mla_cache_append(const mla_append_dims_t* d, const void* x, const v
     }
   }
   const double base = d->rope_base > 0.f ? (double)d->rope_base : 10000.0;
-  return hip_status(mla::launch_append(x, W_DKV, W_KR, page_table, seq_lens, kv_pages, d->batch,
-                                       T, d->hidden, d->d_latent, d->d_rope,
-                                       d->max_pages_per_seq, d->num_pages, base, hs));
+  return hip_status(mla::launch_append(x, W_DKV, W_KR, page_table, seq_lens, kv_pages, kv_scales,
+                                       workspace, d->batch, T, d->hidden, d->d_latent,
+                                       d->d_rope, d->max_pages_per_seq, d->num_pages, base, hs));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_cache_append_workspace_bytes(const mla_append_dims_t* d) {
+  int T = 1;
+  if (check_append_dims(d, &T) != MLA_OK) return 0;
+  return mla::append_workspace_bytes(d->batch * T, d->hidden, d->d_latent, d->d_rope);
+}
+
+mla_status_t mla_cache_append(const mla_append_dims_t* d, const void* x, const void* W_DKV,
+                              const void* W_KR, const int32_t* page_table,
+                              const int32_t* seq_lens, void* kv_pages, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return append_call(d, x, W_DKV, W_KR, page_table, seq_lens, kv_pages, nullptr, workspace,
+                     workspace_bytes, stream);
+}
+
+mla_status_t mla_cache_append_fp8(const mla_append_dims_t* d, const void* x, const void* W_DKV,
+                                  const void* W_KR, const int32_t* page_table,
+                                  const int32_t* seq_lens, void* kv_pages, float* kv_scales,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kv_scales) return MLA_ERR_NULL_ARG;
+  return append_call(d, x, W_DKV, W_KR, page_table, seq_lens, kv_pages, kv_scales, workspace,
+                     workspace_bytes, stream);
 }
 
 const char* mla_status_str(mla_status_t s) {

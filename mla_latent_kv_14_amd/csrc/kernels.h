@@ -80,11 +80,16 @@ hipError_t launch_check(const int32_t* seq_lens, const int32_t* page_table, int 
                         hipStream_t stream);
 
 // Writes [c_KV | RoPE(k_R)] of B*T new tokens (token i of sequence b at position
-// seq_lens[b] + i). Needs d_c % 4 == 0, d_R % 4 == 0 and hidden % 1024 == 0.
+// seq_lens[b] + i): bf16 rows, or with kv_scales an FP8 cache (E4M3 c_KV, bf16 k_R, a
+// power-of-two scale per token). Needs d_c even and at most 1024, d_R even and at most 512,
+// hidden % 256 == 0, and a workspace of append_workspace_bytes.
 hipError_t launch_append(const void* x, const void* W_DKV, const void* W_KR,
-                         const int32_t* page_table, const int32_t* seq_lens, void* kv, int B,
-                         int T, int hidden, int d_c, int d_R, int max_pages, int num_pages,
-                         double rope_base, hipStream_t stream);
+                         const int32_t* page_table, const int32_t* seq_lens, void* kv,
+                         float* kv_scales, void* workspace, int B, int T, int hidden, int d_c,
+                         int d_R, int max_pages, int num_pages, double rope_base,
+                         hipStream_t stream);
+// Workspace of launch_append: fp32 partial rows of the split contraction.
+size_t append_workspace_bytes(int R, int hidden, int d_c, int d_R);
 
 hipError_t launch_gather(int d_latent, int d_rope, const void* kv, const int32_t* page_table,
                          const int32_t* seq_lens, int B, int max_pages, int num_pages, int S_max,

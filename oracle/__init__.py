@@ -226,6 +226,21 @@ def cache_append(x, W_DKV, W_KR, page_table, seq_lens, base=10000.0):
     return rows, where
 
 
+def cache_append_fp8(x, W_DKV, W_KR, page_table, seq_lens, base=10000.0):
+    """Cache append into an FP8 cache: cache_append's rows with the latent part quantised per
+    token (quantise_fp8_row) and the RoPE key left in fp64 (stored as bf16). Returns
+    (codes uint8 [B, T, d_c], scales [B, T], k_R fp64 [B, T, d_R], where [B, T, 2])."""
+    rows, where = cache_append(x, W_DKV, W_KR, page_table, seq_lens, base)
+    d_c = _u16(W_DKV).shape[0]
+    B, T = rows.shape[:2]
+    codes = np.zeros((B, T, d_c), dtype=np.uint8)
+    scales = np.zeros((B, T))
+    for b in range(B):
+        for i in range(T):
+            codes[b, i], scales[b, i] = quantise_fp8_row(rows[b, i, :d_c])
+    return codes, scales, rows[:, :, d_c:], where
+
+
 def fp8_e4m3_value(code):
     """Exact value of FP8 E4M3 bytes (the OCP 8-bit float format with 4 exponent bits, bias 7,
     and 3 mantissa bits; no infinities, S.1111.111 is NaN), as fp64. This is the element format
@@ -239,6 +254,47 @@ def fp8_e4m3_value(code):
     subnormal = (m / 8.0) * 2.0 ** -6
     v = sign * np.where(e == 0, subnormal, normal)
     return np.where((e == 15) & (c & 0x7 == 7), np.nan, v)
+
+
+def fp8_e4m3_encode(v):
+    """The E4M3 byte nearest to each value v (fp64, |v| <= 448, no NaN): among the 127 finite
+    non-negative E4M3 values, the nearest to |v|, a tie going to the even code (last mantissa
+    bit 0), with the sign bit of v (0 gets code 0x00). This is round-to-nearest-even into the
+    format fp8_e4m3_value reads, written out as a search over the format's values."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(np.isnan(v)) or np.any(np.abs(v) > 448.0):
+        raise ValueError("E4M3 encodes finite values of magnitude at most 448")
+    codes = np.arange(127)
+    vals = fp8_e4m3_value(codes)                 # increasing in the code
+    a = np.abs(v)
+    hi = np.clip(np.searchsorted(vals, a), 0, 126)  # first value >= |v|
+    lo = np.clip(hi - 1, 0, 126)
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a == vals[hi], hi, pick)
+    return (pick | np.where((v < 0) & (pick != 0), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_scale_exponent(amax):
+    """The exponent e of an FP8 row's scale 2^e: the smallest integer with
+    amax <= 448 * 2^e (448 = 0.875 * 2^9, the largest E4M3 value), kept within -126 .. 127;
+    0 for amax = 0. With amax = m * 2^k, 0.5 <= m < 1, that is k - 9 when m <= 0.875, else
+    k - 8 (exact)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    m, k = np.frexp(amax)
+    e = int(k) - 9 if m <= 0.875 else int(k) - 8
+    return min(127, max(-126, e))
+
+
+def quantise_fp8_row(c):
+    """A latent row c (fp64) as an FP8 cache row: (E4M3 codes of c / 2^e, 2^e) with e from
+    fp8_scale_exponent(max |c|) (the writer of the quantised latent cache, bhfrc.com/news/60867
+    S1 and S5, read as a per-token power-of-two scaled E4M3 cache)."""
+    c = np.asarray(c, dtype=np.float64)
+    e = fp8_scale_exponent(np.max(np.abs(c)) if c.size else 0.0)
+    return fp8_e4m3_encode(c * 2.0 ** -e), 2.0 ** e
 
 
 def check_scales(scales):

@@ -8,7 +8,8 @@ import pytest
 import mla_latent_kv_14_amd as M
 from mla_latent_kv_14_amd.binding import STATUS_CODE
 
-EXPECTED = ["mla_cache_append", "mla_decode", "mla_decode_fp8", "mla_decode_noalloc",
+EXPECTED = ["mla_cache_append", "mla_cache_append_fp8", "mla_cache_append_workspace_bytes",
+            "mla_decode", "mla_decode_fp8", "mla_decode_noalloc",
             "mla_decode_out", "mla_decode_timed",
             "mla_decode_workspace_bytes", "mla_gather_pages", "mla_last_hip_error",
             "mla_status_str"]
@@ -251,22 +252,55 @@ def test_append_rejects_bad_dims(field, value, status):
     d = _append_dims()
     setattr(d, field, value)
     p = [_al(k + 1) for k in range(6)]
-    assert M.lib().mla_cache_append(ctypes.byref(d), *p, ctypes.c_void_p(0)) == \
-        STATUS_CODE[status]
+    assert M.lib().mla_cache_append(ctypes.byref(d), *p, _al(7), 1 << 30,
+                                    ctypes.c_void_p(0)) == STATUS_CODE[status]
+    assert M.lib().mla_cache_append_workspace_bytes(ctypes.byref(d)) == 0
 
 
 def test_append_rejects_null_and_misaligned():
     L = M.lib()
-    assert L.mla_cache_append(None, *[_al(k + 1) for k in range(6)], None) == \
+    assert L.mla_cache_append(None, *[_al(k + 1) for k in range(6)], _al(7), 1 << 30, None) == \
         STATUS_CODE["MLA_ERR_NULL_ARG"]
     for i in range(6):
         p = [_al(k + 1) for k in range(6)]
         p[i] = ctypes.c_void_p(0)
-        assert L.mla_cache_append(ctypes.byref(_append_dims()), *p, None) == \
+        assert L.mla_cache_append(ctypes.byref(_append_dims()), *p, _al(7), 1 << 30, None) == \
             STATUS_CODE["MLA_ERR_NULL_ARG"], i
         p[i] = ctypes.c_void_p(0x100008)
-        assert L.mla_cache_append(ctypes.byref(_append_dims()), *p, None) == \
+        assert L.mla_cache_append(ctypes.byref(_append_dims()), *p, _al(7), 1 << 30, None) == \
             STATUS_CODE["MLA_ERR_MISALIGNED"], i
+    p = [_al(k + 1) for k in range(6)]
+    assert L.mla_cache_append_fp8(ctypes.byref(_append_dims()), *p, None, _al(7), 1 << 30,
+                                  None) == STATUS_CODE["MLA_ERR_NULL_ARG"]
+    assert L.mla_cache_append_fp8(ctypes.byref(_append_dims()), *p, ctypes.c_void_p(0x100004),
+                                  _al(7), 1 << 30, None) == STATUS_CODE["MLA_ERR_MISALIGNED"]
+
+
+def test_append_workspace():
+    # fp32 partial rows, one set per slice of the model width: as many slices (a divisor of
+    # hidden / 256) as keep the partial grid within 1024 work groups and within what the
+    # finishing work group sums (min(8, 1024 / (N / 4)) threads per column quad, 8 slices each)
+    L = M.lib()
+    d = _append_dims(B=16)  # 18 column blocks x 1 token block: 28 slices of 256
+    need = L.mla_cache_append_workspace_bytes(ctypes.byref(d))
+    assert need == 28 * 16 * 576 * 4
+    d = _append_dims(B=64, T=16)  # 18 x 16 blocks of 64 token rows: 2 slices
+    assert L.mla_cache_append_workspace_bytes(ctypes.byref(d)) == 2 * 1024 * 576 * 4
+    d = _append_dims(B=96)  # 18 x 3 blocks of 32 token rows: 14 slices
+    assert L.mla_cache_append_workspace_bytes(ctypes.byref(d)) == 14 * 96 * 576 * 4
+    d = _append_dims(B=32, hidden=4096, d_c=64, d_R=8)  # 3 x 2 blocks: all 16 slices
+    assert L.mla_cache_append_workspace_bytes(ctypes.byref(d)) == 16 * 32 * 72 * 4
+    # N = 1536: 2 threads per quad, so at most 16 slices (the grid would allow 20 of 5120 / 256)
+    d = _append_dims(B=16, hidden=5120, d_c=1024, d_R=512)
+    assert L.mla_cache_append_workspace_bytes(ctypes.byref(d)) == 10 * 16 * 1536 * 4
+    d = _append_dims(B=16)
+    p = [_al(k + 1) for k in range(6)]
+    assert L.mla_cache_append(ctypes.byref(d), *p, _al(7), need - 4, None) == \
+        STATUS_CODE["MLA_ERR_WORKSPACE"]
+    assert L.mla_cache_append(ctypes.byref(d), *p, ctypes.c_void_p(0), need, None) == \
+        STATUS_CODE["MLA_ERR_WORKSPACE"]
+    assert L.mla_cache_append(ctypes.byref(d), *p, ctypes.c_void_p(0x100010), need, None) == \
+        STATUS_CODE["MLA_ERR_MISALIGNED"]
 
 
 def test_status_strings():

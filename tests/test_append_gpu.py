@@ -13,7 +13,10 @@ from tests.gpu_helpers import check_against_oracle, need_gpu, say, to_dev
 pytestmark = pytest.mark.gpu
 
 SHAPES = {"deepseek": dict(H=128, d_n=128, d_c=512, d_R=64, d_v=128, hidden=7168),
-          "mha2mla": dict(H=32, d_n=120, d_c=64, d_R=8, d_v=128, hidden=4096)}
+          "mha2mla": dict(H=32, d_n=120, d_c=64, d_R=8, d_v=128, hidden=4096),
+          # the widest row the append takes (d_latent 1024, d_rope 512): two threads per
+          # column quad in the finishing kernel, so its slice count is capped at 16
+          "wide": dict(H=16, d_n=64, d_c=1024, d_R=512, d_v=64, hidden=5120)}
 
 
 @pytest.fixture(scope="module")
@@ -61,7 +64,12 @@ def _append_and_check(M, shape, lens, T, seed):
 
 @pytest.mark.parametrize("shape,lens,T", [("deepseek", [62, 64, 500], 2),
                                           ("deepseek", [1 + 37 * i for i in range(16)], 1),
-                                          ("mha2mla", [1, 63, 64, 1000], 3)])
+                                          ("mha2mla", [1, 63, 64, 1000], 3),
+                                          ("wide", [5, 70, 130], 2),
+                                          # 160 and 100 token rows: partial work groups
+                                          # of 64 and 32 rows, each with a ragged last block
+                                          ("deepseek", [1 + 37 * i for i in range(10)], 16),
+                                          ("deepseek", [3 + 41 * i for i in range(50)], 2)])
 def test_append_matches_oracle(M, shape, lens, T):
     _append_and_check(M, shape, lens, T, 41)
 
@@ -153,3 +161,89 @@ def test_check_mode_refuses_unallocated_page_entry(M):
             del os.environ["MLA_CHECK"]
         else:
             os.environ["MLA_CHECK"] = old
+
+
+# ---- appending into an FP8 cache (mla_cache_append_fp8)
+
+def _fp8_pool(inp, seed):
+    kv8, sc = W.fp8_cache(inp, seed=seed)
+    return kv8, sc
+
+
+@pytest.mark.parametrize("shape,lens,T", [("deepseek", [62, 64, 500], 2),
+                                          ("deepseek", [1 + 37 * i for i in range(16)], 1),
+                                          ("mha2mla", [1, 63, 64, 1000], 3),
+                                          ("wide", [5, 70, 130], 2)])
+def test_fp8_append_matches_oracle(M, shape, lens, T):
+    # Each new token's scale is the smallest power of two 2^e with max |c_KV| <= 448 * 2^e and
+    # its bytes are c_KV / 2^e rounded to the nearest even E4M3 value. The kernel decides
+    # from fp32 sums and the oracle from fp64 ones, so a code may differ by one step where the
+    # exact value sits within summation noise of a rounding midpoint, and a scale where max
+    # |c_KV| sits at a power-of-two edge; everything else must agree exactly, and every other
+    # byte of the pool and its scales stays as it was.
+    inp, x, Wd, Wr, before = _case(shape, lens, T, 44)
+    c = SHAPES[shape]
+    d_c, d_R = c["d_c"], c["d_R"]
+    kv8_0, sc0 = _fp8_pool(inp, 3)
+    kv8, sc = kv8_0.clone().cuda(), sc0.clone().cuda()
+    say("fp8 append", shape, "B=%d T=%d" % (len(lens), T))
+    M.cache_append(x.cuda(), Wd.cuda(), Wr.cuda(), kv8, inp["page_table"].cuda(), before.cuda(),
+                   kv_scales=sc)
+    torch.cuda.synchronize()
+    got8, gotsc = kv8.cpu().numpy(), sc.cpu().numpy()
+    codes, scales, kr, where = oracle.cache_append_fp8(
+        W.u16(x), W.u16(Wd), W.u16(Wr), inp["page_table"].numpy(), before.numpy())
+    rows, _ = oracle.cache_append(W.u16(x), W.u16(Wd), W.u16(Wr), inp["page_table"].numpy(),
+                                  before.numpy())
+    written = np.zeros(got8.shape[:2], dtype=bool)
+    n_codes = n_diff = 0
+    for b in range(len(lens)):
+        for i in range(T):
+            page, slot = where[b, i]
+            written[page, slot] = True
+            s_gpu = float(gotsc[page, slot])
+            if s_gpu != scales[b, i]:  # only at an edge of the scale rule
+                amax = np.max(np.abs(rows[b, i, :d_c]))
+                ratio = amax / (448 * min(s_gpu, scales[b, i]))
+                assert abs(ratio - 1) < 1e-5, (b, i, s_gpu, scales[b, i])
+                continue
+            g = got8[page, slot, :d_c].astype(np.int64)
+            r = codes[b, i].astype(np.int64)
+            diff = g != r
+            n_codes += g.size
+            n_diff += int(diff.sum())
+            # a differing code is the other neighbour of a value at a rounding midpoint
+            vg = oracle.fp8_e4m3_value(g[diff]) * s_gpu
+            vr = oracle.fp8_e4m3_value(r[diff]) * s_gpu
+            exact = rows[b, i, :d_c][diff]
+            assert np.all(np.abs(np.abs(vg - exact) - np.abs(vr - exact)) <= 1e-5 * s_gpu + 1e-6 * np.abs(exact)), (b, i)
+            # k_R: bf16 within half an ulp of the fp64 rotation
+            krg = got8[page, slot, d_c:].view(np.uint16).astype(np.uint32) << 16
+            krg = krg.view(np.float32).astype(np.float64)
+            assert np.all(np.abs(krg - kr[b, i]) <= 2.0 ** -8 * np.abs(kr[b, i]) + 1e-5), (b, i)
+    assert n_diff <= max(2, n_codes // 200), (n_diff, n_codes)
+    assert np.array_equal(got8[~written], kv8_0.numpy()[~written])
+    assert np.array_equal(gotsc[~written], sc0.numpy()[~written], equal_nan=True)
+
+
+def test_fp8_append_then_decode(M):
+    # tokens appended into an FP8 cache are read back by mla_decode_fp8: the decode agrees with
+    # the oracle run on the bf16 cache that the FP8 one stands for (dequant_fp8_cache)
+    lens, T = [70, 300, 5], 2
+    inp, x, Wd, Wr, before = _case("deepseek", lens, T, 45)
+    kv8_0, sc0 = _fp8_pool(inp, 4)
+    kv8, sc = kv8_0.clone().cuda(), sc0.clone().cuda()
+    M.cache_append(x.cuda(), Wd.cuda(), Wr.cuda(), kv8, inp["page_table"].cuda(), before.cuda(),
+                   kv_scales=sc)
+    torch.cuda.synchronize()
+    d = to_dev(inp)
+    say("fp8 append then decode")
+    out = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8, d["page_table"],
+                   d["seq_lens"], kv_scales=sc)
+    torch.cuda.synchronize()
+    args = list(W.oracle_args(inp))
+    args[4] = oracle.dequant_fp8_cache(kv8.cpu().numpy(), sc.cpu().numpy(), inp["d_c"])
+    ref, _ = oracle.decode(*args)
+    g = out.float().cpu().numpy()
+    rel = float(np.linalg.norm(g - ref) / np.linalg.norm(ref))
+    assert rel <= 5e-3, rel

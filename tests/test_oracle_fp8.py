@@ -92,3 +92,78 @@ def test_fp8_cache_round_trip():
     # |error| <= half a step of the code: 2^-4 relative for normals, 2^-10 * scale absolute
     assert np.all(np.abs(a - b) <= np.maximum(np.abs(b) * 2.0 ** -4, 2.0 ** -10 * scale))
     assert np.mean(a == b) < 1.0  # quantisation really happened
+
+
+# ---- the FP8 writer (quantise_fp8_row): round to nearest even E4M3 under a power-of-two
+# scale chosen from the row's largest magnitude
+
+def test_encode_round_trips_every_finite_code():
+    v = oracle.fp8_e4m3_value(np.arange(256))
+    fin = ~np.isnan(v)
+    codes = np.arange(256)[fin]
+    enc = oracle.fp8_e4m3_encode(v[fin]).astype(np.int64)
+    # -0 (0x80) encodes as +0; every other finite code comes back as itself
+    assert np.all((enc == codes) | ((codes == 0x80) & (enc == 0)))
+
+
+def test_encode_rounds_to_nearest_ties_to_even():
+    vals = oracle.fp8_e4m3_value(np.arange(127))
+    mid = (vals[:-1] + vals[1:]) / 2
+    e = oracle.fp8_e4m3_encode(mid).astype(np.int64)
+    assert np.all(e % 2 == 0)                           # a tie takes the even code
+    assert np.all((e == np.arange(126)) | (e == np.arange(1, 127)))
+    gap = vals[1:] - vals[:-1]
+    below = oracle.fp8_e4m3_encode(mid - gap / 8).astype(np.int64)
+    above = oracle.fp8_e4m3_encode(mid + gap / 8).astype(np.int64)
+    assert np.array_equal(below, np.arange(126)) and np.array_equal(above, np.arange(1, 127))
+    neg = oracle.fp8_e4m3_encode(-vals[1:]).astype(np.int64)
+    assert np.array_equal(neg, np.arange(1, 127) | 0x80)
+    with pytest.raises(ValueError):
+        oracle.fp8_e4m3_encode(np.array([448.5]))
+
+
+def test_scale_exponent_is_the_smallest_that_fits():
+    for e in (-20, -8, 0, 3, 40):
+        edge = 448.0 * 2.0 ** e
+        assert oracle.fp8_scale_exponent(edge) == e
+        assert oracle.fp8_scale_exponent(edge * (1 + 2.0 ** -40)) == e + 1
+        assert oracle.fp8_scale_exponent(edge / 2 * (1 + 2.0 ** -40)) == e
+        assert oracle.fp8_scale_exponent(edge / 2) == e - 1
+    assert oracle.fp8_scale_exponent(0.0) == 0
+    assert oracle.fp8_scale_exponent(1e-300) == -126 and oracle.fp8_scale_exponent(1e300) == 127
+
+
+def test_quantised_row_error_bound():
+    rng = np.random.default_rng(7)
+    for scale in (1e-3, 1.0, 50.0):
+        c = rng.standard_normal(512) * scale
+        codes, s = oracle.quantise_fp8_row(c)
+        assert s == 2.0 ** np.round(np.log2(s))          # a power of two
+        amax = np.max(np.abs(c))
+        assert 224 * s < amax <= 448 * s                  # the smallest that fits
+        back = oracle.fp8_e4m3_value(codes) * s
+        normal = np.abs(c) >= 2.0 ** -6 * s
+        # half an E4M3 ulp: 2^-4 relative for normals, 2^-10 * s for subnormals
+        assert np.all(np.abs(back - c)[normal] <= 2.0 ** -4 * np.abs(c)[normal])
+        assert np.all(np.abs(back - c)[~normal] <= 2.0 ** -10 * s)
+    codes, s = oracle.quantise_fp8_row(np.zeros(64))
+    assert s == 1.0 and np.all(codes == 0)
+
+
+
+def test_encode_agrees_with_torch_float8_cast():
+    # torch's float32 -> float8_e4m3fn cast rounds to nearest even as well; on fp32 values
+    # within the format's range (normals, subnormals, ties) both give the same byte
+    import torch
+    rng = np.random.default_rng(11)
+    mags = np.concatenate([rng.uniform(0, 448, 4000), rng.uniform(0, 2.0 ** -6, 2000),
+                           oracle.fp8_e4m3_value(np.arange(127))])
+    v = (mags * rng.choice([-1.0, 1.0], mags.size)).astype(np.float32)
+    vals = oracle.fp8_e4m3_value(np.arange(127))
+    ties = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)     # exact in fp32
+    v = np.concatenate([v, ties, -ties])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.fp8_e4m3_encode(v.astype(np.float64))
+    # torch keeps the sign of a value that rounds to zero (0x80); the encoder writes 0x00
+    same = (got == ref) | ((got == 0) & (ref == 0x80))
+    assert np.all(same), v[~same][:5]
