@@ -13,10 +13,11 @@
 // Kernels:
 //   transpose: W_UVt[h][e][c] = W_UV[h][c][e], so that both weights are read along the latent
 //     (contraction) dimension.
-//   decompress: per (sequence, 128 tokens, head, K or V): out^T[128 columns x 128 tokens] =
-//     W[h] (columns x d_c) . c_KV^T, 32x32x16 bf16 MFMA over d_c in chunks of 32 staged in LDS
-//     (double-buffered through registers), rows of the page-table-addressed cache gathered
-//     directly; bf16 out into the workspace ([token][head][width] per sequence).
+//   decompress: per (sequence, 256 tokens, head, K or V): out^T[128 columns x 256 tokens] =
+//     W (columns x d_c) . c_KV^T with W = W_UK[h] or W_UVt[h], 32x32x16 bf16 MFMA over d_c in
+//     chunks of 32 staged in LDS (two chunks in flight in registers; two work groups per CU),
+//     rows of the page-table-addressed cache gathered directly; bf16 out into the workspace,
+//     [sequence][head][token][width], so that a work group's block is contiguous.
 //   attention: per (sequence, head, 128 query rows): four waves of 32 rows share each 32-token
 //     tile of [K_nope | k_R] and V in LDS (k_R straight from the paged cache), S^T = K Q^T and
 //     O^T += V^T P^T on 32x32x16 MFMA (the contraction index of P numbered in the order the
@@ -30,9 +31,10 @@ namespace mla {
 
 namespace pf {
 constexpr int NT = 256;       // threads per work group (four waves)
-constexpr int TOK = 128;      // decompress: tokens per work group
-constexpr int COLS = 128;     // decompress: output columns per work group (one K or V block)
-constexpr int KC = 32;        // decompress: contraction chunk
+constexpr int DTOK = 256;     // decompress: tokens per work group
+constexpr int DCOL = 128;     // decompress: output columns per work group (one head's K or V)
+constexpr int DKC = 32;       // decompress: contraction chunk
+constexpr int DNT = 512;      // decompress: threads per work group (eight waves)
 constexpr int QB = 128;       // attention: query rows per work group (32 per wave)
 constexpr int TT = 32;        // attention: tokens per tile
 }  // namespace pf
@@ -63,92 +65,111 @@ __global__ void __launch_bounds__(256) transpose_wuv_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------- decompression
-// Grid: x = 128-token block of the sequence, y = 2*h + part (part 0: K_nope of head h from
-// W_UK[h], rows d < DN; part 1: V of head h from W_UVt[h]), z = sequence of the group.
+// 16-byte chunk c of LDS row r of the decompression's 64-byte rows, XOR-swizzled by r / 4: 16
+// consecutive rows read at one chunk column then cover all 16 chunk slots of a 256-byte span
+// of the banks.
+__device__ __forceinline__ int dc_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// Per group of sequences: out[t][n] = sum_c c_KV[t][c] * W[n][c] for the keys (W = W_UK[h],
+// n < DN) and the values (W = W_UVt[h], n < DV) of every head. A work group computes one
+// half (K or V) of one head for 256 tokens; the grid puts the halves of all heads first, so
+// that the work groups in flight share their token tile (the gathered cache rows come from
+// L2). Eight waves, each a 64 x 64 block of the output (columns 64 (wave & 1), tokens
+// 64 (wave >> 1)) as 2 x 2 MFMA 32x32x16 blocks. The contraction runs in chunks of 32 staged in
+// LDS (two buffers) with the next two chunks' global loads in flight in registers. At 64
+// accumulator registers the kernel fits in 128 per lane, so two work groups share a CU and
+// one's output stores overlap the other's MFMAs.
+// Grid: x = 2 * head + half, y = 256-token block of the sequence, z = sequence of the group.
 template <int H, int DN, int DC, int DR, int DV>
-__global__ void __launch_bounds__(pf::NT)
+__global__ void __launch_bounds__(pf::DNT, 2)
 decompress_kernel(const char* __restrict__ kv, const int32_t* __restrict__ page_table,
                   const int32_t* __restrict__ seq_lens, int b0, int max_pages, int num_pages,
                   const uint16_t* __restrict__ W_UK, const uint16_t* __restrict__ W_UVt,
                   uint16_t* __restrict__ kbuf, uint16_t* __restrict__ vbuf, int smax) {
   using namespace pf;
-  constexpr int ROWB = (DC + DR) * 2;  // bytes per cache token row
-  constexpr int NCH = KC * 2 / 16;     // 16-byte chunks per LDS row (4)
-  static_assert(DC % KC == 0 && DN <= COLS && DV == COLS, "shape");
-  __shared__ __attribute__((aligned(16))) char lds_w[2][COLS * KC * 2];
-  __shared__ __attribute__((aligned(16))) char lds_a[2][TOK * KC * 2];
+  constexpr int ROWB = (DC + DR) * 2;   // bytes per cache token row
+  constexpr int NCH = DKC * 2 / 16;     // 16-byte chunks per LDS row (4)
+  constexpr int PA = DTOK * NCH / DNT;  // 16-byte cache-row pieces per thread per chunk (2)
+  constexpr int NCHUNK = DC / DKC;
+  constexpr int DEPTH = NCHUNK > 2 ? 2 : 1;  // chunks in flight in registers
+  static_assert(DC % DKC == 0 && DN <= DCOL && DV == DCOL, "shape");
+  static_assert(DTOK == 256 && DCOL == 128 && DKC == 32 && PA == 2 && DNT == 512,
+                "piece mapping");
+  // LDS: the two chunk buffers [W rows | cache rows], then (after the contraction) each wave's
+  // 64 x 64 output block, staged so that it leaves as whole 128-byte rows
+  constexpr int WB = DCOL * DKC * 2, AB = DTOK * DKC * 2;  // bytes of one buffer's parts
+  constexpr int STG = 64 * 128;                             // bytes of one wave's block
+  constexpr int LDS_BYTES = 2 * (WB + AB) > 8 * STG ? 2 * (WB + AB) : 8 * STG;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  auto lds_w = [&](int buf) { return (MLA_LDS char*)lds + buf * WB; };
+  auto lds_a = [&](int buf) { return (MLA_LDS char*)lds + 2 * WB + buf * AB; };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int sl = blockIdx.z, b = b0 + sl;
-  const int h = blockIdx.y >> 1, part = blockIdx.y & 1;
-  const int t0 = blockIdx.x * TOK;
+  const int h = blockIdx.x >> 1, part = blockIdx.x & 1, sl = blockIdx.z, b = b0 + sl;
+  const int t0 = blockIdx.y * DTOK;
   // S_b within the page table and within the rows the workspace keeps per sequence (smax,
   // the dims' max_seq_len: S_b <= max_seq_len is the caller's contract, enforced here)
   const int S = min(clamp_len(seq_lens[b], max_pages), smax);
   if (t0 >= S) return;
-  const int rows_w = part == 0 ? DN : DV;
-  const uint16_t* W = part == 0 ? W_UK + (size_t)h * DN * DC : W_UVt + (size_t)h * DV * DC;
+  const int width = part == 0 ? DN : DV;
 
-  // this thread's two W pieces and two A pieces per chunk: 512 pieces of 16 bytes each
-  const uint16_t* wsrc[2];
-  const uint16_t* asrc[2];
-  uint32_t wdst[2], adst[2];
-  bool wok[2];
+  // thread tid moves 16-byte chunk c = tid % 4 of weight row tid / 4 and of cache rows
+  // tid / 4 + 128k (k < 2)
+  const int c = tid & 3, rb = tid >> 2;
+  const bool wok = rb < width;  // K rows past DN are zero
+  const uint16_t* wsrc = (part == 0 ? W_UK + ((size_t)h * DN + (wok ? rb : 0)) * DC
+                                    : W_UVt + ((size_t)h * DV + rb) * DC) + 8 * c;
+  const uint32_t wlo = (uint32_t)(rb * DKC * 2 + 16 * dc_chunk(rb, c));
+  const char* asrc[PA];
+  uint32_t alo[PA];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int p = tid + NT * k, r = p >> 2, c = p & 3;
-    wok[k] = r < rows_w;
-    wsrc[k] = W + (size_t)(wok[k] ? r : 0) * DC + 8 * c;
-    wdst[k] = (uint32_t)(r * KC * 2 + 16 * pf_chunk<NCH>(r, c));
-    int t = t0 + r;
-    t = t < S ? t : S - 1;  // rows past the end repeat the last token (their outputs are unused)
+  for (int k = 0; k < PA; ++k) {
+    const int r = rb + 128 * k;
+    const int t = min(t0 + r, S - 1);  // rows past the end repeat the last token (unused)
     int page = page_table[(size_t)b * max_pages + t / kPage];
     page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
-    asrc[k] = reinterpret_cast<const uint16_t*>(kv + ((size_t)page * kPage + t % kPage) * ROWB) +
-              8 * c;
-    adst[k] = (uint32_t)(r * KC * 2 + 16 * pf_chunk<NCH>(r, c));
+    asrc[k] = kv + ((size_t)page * kPage + t % kPage) * ROWB + 16 * c;
+    alo[k] = (uint32_t)(r * DKC * 2 + 16 * dc_chunk(r, c));
   }
-  u32x4 wreg[2], areg[2];
-  auto load_chunk = [&](int kc) {
+  u32x4 wreg[DEPTH], areg[DEPTH][PA];
+  auto load_chunk = [&](int kc, int slot) {
+    wreg[slot] = wok ? *reinterpret_cast<const u32x4*>(wsrc + kc * DKC) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      wreg[k] = wok[k] ? *reinterpret_cast<const u32x4*>(wsrc[k] + kc * KC) : u32x4{0, 0, 0, 0};
-      areg[k] = *reinterpret_cast<const u32x4*>(asrc[k] + kc * KC);
-    }
+    for (int k = 0; k < PA; ++k)
+      areg[slot][k] = *reinterpret_cast<const u32x4*>(asrc[k] + kc * DKC * 2);
   };
-  auto store_chunk = [&](int buf) {
+  auto store_chunk = [&](int slot, int buf) {
+    *reinterpret_cast<MLA_LDS u32x4*>(lds_w(buf) + wlo) = wreg[slot];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      *reinterpret_cast<MLA_LDS u32x4*>((MLA_LDS char*)lds_w[buf] + wdst[k]) = wreg[k];
-      *reinterpret_cast<MLA_LDS u32x4*>((MLA_LDS char*)lds_a[buf] + adst[k]) = areg[k];
-    }
+    for (int k = 0; k < PA; ++k)
+      *reinterpret_cast<MLA_LDS u32x4*>(lds_a(buf) + alo[k]) = areg[slot][k];
   };
 
-  // wave: columns 64 (wave & 1) .. +64, tokens 64 (wave >> 1) .. +64, as 2 x 2 blocks of 32
   const int mw = 64 * (wave & 1), nw = 64 * (wave >> 1);
   const int r32 = lane & 31, hi = lane >> 5;
   f32x16 acc[2][2] = {};
-  load_chunk(0);
-  store_chunk(0);
+#pragma unroll
+  for (int kc = 0; kc < DEPTH; ++kc) load_chunk(kc, kc);
+  store_chunk(0, 0);
+  if (DEPTH < NCHUNK) load_chunk(DEPTH, 0);
   __syncthreads();
-  constexpr int NCHUNK = DC / KC;
+#pragma unroll
   for (int kc = 0; kc < NCHUNK; ++kc) {
     const int buf = kc & 1;
-    if (kc + 1 < NCHUNK) load_chunk(kc + 1);
-    const MLA_LDS char* wl = (const MLA_LDS char*)lds_w[buf];
-    const MLA_LDS char* al = (const MLA_LDS char*)lds_a[buf];
+    const MLA_LDS char* wl = lds_w(buf);
+    const MLA_LDS char* al = lds_a(buf);
 #pragma unroll
-    for (int ks = 0; ks < KC / 16; ++ks) {
+    for (int ks = 0; ks < DKC / 16; ++ks) {
       bf16x8 wa[2], ab[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int r = mw + 32 * m + r32;
-        wa[m] = lds_read_b128(wl, r * KC * 2 + 16 * pf_chunk<NCH>(r, 2 * ks + hi));
+        wa[m] = lds_read_b128(wl, r * DKC * 2 + 16 * dc_chunk(r, 2 * ks + hi));
       }
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int r = nw + 32 * n + r32;
-        ab[n] = lds_read_b128(al, r * KC * 2 + 16 * pf_chunk<NCH>(r, 2 * ks + hi));
+        ab[n] = lds_read_b128(al, r * DKC * 2 + 16 * dc_chunk(r, 2 * ks + hi));
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m)
@@ -156,29 +177,44 @@ decompress_kernel(const char* __restrict__ kv, const int32_t* __restrict__ page_
         for (int n = 0; n < 2; ++n) acc[m][n] = mfma_32x32x16(wa[m], ab[n], acc[m][n]);
     }
     if (kc + 1 < NCHUNK) {
-      store_chunk(buf ^ 1);  // the other buffer: its last reads were before the last barrier
+      // chunk kc+1 (loaded DEPTH - 1 chunks ago) into the other buffer, whose last reads were
+      // before the last barrier; then its register slot takes chunk kc+1+DEPTH
+      store_chunk((kc + 1) % DEPTH, buf ^ 1);
+      if (kc + 1 + DEPTH < NCHUNK) load_chunk(kc + 1 + DEPTH, (kc + 1) % DEPTH);
       __syncthreads();
     }
   }
-  // out^T block (m, n): lane holds token nw + 32n + r32 and columns mw + 32m + 8(i/4) + 4hi
-  // + i%4; four consecutive columns go out as one 8-byte store
-  const int width = part == 0 ? DN : DV;
-  uint16_t* dst = part == 0 ? kbuf : vbuf;
+  // out^T block (m, n): lane holds token nw + 32n + r32 and columns mw + 32m + 8(i/4) + 4hi +
+  // i%4 (i < 16). The wave's 64 x 64 block is staged in LDS (row = token, 16-byte chunk
+  // 4m + g of the row XOR-swizzled by row % 8) and read back as whole 128-byte rows, eight
+  // lanes per row: a store then covers whole lines instead of 16 bytes of 32 lines. Output
+  // layout [sequence][head][token][width]; K columns at or past DN (the zero rows) and tokens
+  // past S are not stored.
+  __syncthreads();  // every wave is done with the chunk buffers
+  MLA_LDS char* const stg = (MLA_LDS char*)lds + wave * STG;
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
-    const int t = t0 + nw + 32 * n + r32;
-    if (t >= S) continue;
-    uint16_t* row = dst + (((size_t)sl * smax + t) * H + h) * width;
+    const int row = 32 * n + r32;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = mw + 32 * m + 8 * g + 4 * hi;
-        if (col + 4 > width) continue;
         const f32x16& o = acc[m][n];
-        const u32x2 w = {pack_bf16x2(o[4 * g], o[4 * g + 1]), pack_bf16x2(o[4 * g + 2], o[4 * g + 3])};
-        *reinterpret_cast<u32x2*>(row + col) = w;
+        const u32x2 w = {pack_bf16x2(o[4 * g], o[4 * g + 1]),
+                         pack_bf16x2(o[4 * g + 2], o[4 * g + 3])};
+        *reinterpret_cast<MLA_LDS u32x2*>(stg + row * 128 + 16 * ((4 * m + g) ^ (row & 7)) +
+                                          8 * hi) = w;
       }
+  }
+  uint16_t* const dst = (part == 0 ? kbuf : vbuf) + ((size_t)sl * H + h) * smax * width;
+  const int cl = lane & 7;  // 16-byte chunk of the row: columns mw + 8cl .. +8
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 8 * i + (lane >> 3);
+    const int t = t0 + nw + row;
+    const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * 128 + 16 * (cl ^ (row & 7)));
+    if (t < S && mw + 8 * cl + 8 <= width)
+      *reinterpret_cast<u32x4*>(dst + (size_t)t * width + mw + 8 * cl) = v;
   }
 }
 
@@ -249,9 +285,9 @@ prefill_attn_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restr
       t = t < S ? t : (S > 0 ? S - 1 : 0);  // past the end: a valid row, masked
       const uint16_t* src;
       if (isv) {
-        src = vbuf + (((size_t)sl * smax + t) * H + h) * DV + 8 * c;
+        src = vbuf + (((size_t)sl * H + h) * smax + t) * DV + 8 * c;
       } else if (c < NCH_N) {
-        src = kbuf + (((size_t)sl * smax + t) * H + h) * DN + 8 * c;
+        src = kbuf + (((size_t)sl * H + h) * smax + t) * DN + 8 * c;
       } else {
         int page = page_table[(size_t)b * max_pages + t / kPage];
         page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
@@ -382,7 +418,7 @@ hipError_t launch_prefill(int shape, const void* q_nope, const void* q_rope, con
     for (int b0 = 0; b0 < B; b0 += group) {
       const int g = min(group, B - b0);
       e = launch_kernel(decompress_kernel<H, DN, DC, DR, DV>,
-                        dim3((smax + pf::TOK - 1) / pf::TOK, 2 * H, g), dim3(pf::NT), Ls,
+                        dim3(2 * H, (smax + pf::DTOK - 1) / pf::DTOK, g), dim3(pf::DNT), Ls,
                         (const char*)kv, page_table, seq_lens, b0, max_pages, num_pages,
                         (const uint16_t*)W_UK, (const uint16_t*)W_UVt, (uint16_t*)kbuf,
                         (uint16_t*)vbuf, smax);
