@@ -402,6 +402,200 @@ prefill_attn_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------- attention, DeepSeek widths
+// The same computation as prefill_attn_kernel for d_nope = d_v = 128, d_rope = 64, with a
+// work group per (sequence, head, 256 query rows): eight waves of 32 rows, so that at T <= 256
+// a head's keys and values are read once. The 32-token tiles stream straight into a six-entry
+// LDS ring (direct global->LDS loads, five tiles in flight) issued by waves 0..3, five load
+// instructions each per tile: an entry is [K_nope 32 x 256 B | k_R 32 x 128 B | V 32 x 256 B],
+// each row's 16-byte chunks XOR-swizzled by the row (K_nope and V by r % 16, k_R by (r / 2) %
+// 8) so that the MFMA operand reads of 16 consecutive rows hit distinct banks. A tile's 32
+// tokens lie in one 64-token page, whose k_R rows come straight from the paged cache.
+// Grid: x = 256-row query block, y = head, z = sequence of the group.
+namespace pfa {
+constexpr int QB = 256, NT = 512, TT = 32, NBUF = 6;
+constexpr int KNB = TT * 256, KRB = TT * 128, VB = TT * 256;  // bytes of an entry's parts
+constexpr int ENT = KNB + KRB + VB;                           // 20 KiB
+constexpr int IPW = 5;  // load instructions per loading wave per tile (20 KiB / 4 waves)
+}  // namespace pfa
+
+// Waits until at most `after` tiles of IPW load instructions each are still in flight
+// (after <= NBUF - 2).
+template <int A>
+__device__ __forceinline__ void pfa_wait_tiles(int after) {
+  if (after >= A) wait_vmcnt<A * pfa::IPW>();
+  else if constexpr (A > 0) pfa_wait_tiles<A - 1>(after);
+}
+
+__global__ void __launch_bounds__(pfa::NT)
+prefill_attn_ds_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+                       const char* __restrict__ kv, const int32_t* __restrict__ page_table,
+                       const int32_t* __restrict__ seq_lens, int b0, int max_pages,
+                       int num_pages, int T, const uint16_t* __restrict__ kbuf,
+                       const uint16_t* __restrict__ vbuf, int smax, float scale_log2,
+                       uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+  using namespace pfa;
+  constexpr int H = 128, DN = 128, DR = 64, DV = 128, DC = 512;
+  constexpr int KS = (DN + DR) / 16;  // 32x32x16 steps over the score contraction (12)
+  constexpr int ROWB = (DC + DR) * 2;
+  static_assert(ENT % 1024 == 0 && 4 * IPW * 1024 == ENT, "entry of whole KiB, 4 loaders");
+  __shared__ __attribute__((aligned(1024))) char lds_ring[NBUF * ENT];
+  MLA_LDS char* const ring = (MLA_LDS char*)lds_ring;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sl = blockIdx.z, b = b0 + sl, h = blockIdx.y;
+  const int S = min(clamp_len(ld_uniform(seq_lens + b), max_pages), smax);
+  const int i0 = blockIdx.x * QB;  // first query row of the block
+  // the block's last row sits at position S - T + min(T - 1, i0 + QB - 1): tokens past it are
+  // masked for every row of the block (so ntok <= S)
+  const int last = S - T + min(T - 1, i0 + QB - 1);
+  const int ntok = last + 1 > 0 ? last + 1 : 0;
+  const int ntiles = (ntok + TT - 1) / TT;
+
+  // ---- tile loads (waves 0..3): instruction u of wave w is number w + 4u of the tile's 20:
+  // u = 0, 1 -> K_nope rows 4i .. 4i+3 (i = w + 4u), u = 2 -> k_R rows 8w .. 8w+7,
+  // u = 3, 4 -> V rows 4i .. 4i+3 (i = w + 4u - 12). Lane l fills LDS slot l of the KiB; it
+  // loads the chunk that the row's swizzle puts there. Rows past the sequence's end repeat
+  // its last token (masked).
+  const bool loader = wave < 4;
+  const char* const kb = reinterpret_cast<const char*>(kbuf + ((size_t)sl * H + h) * smax * DN);
+  const char* const vb = reinterpret_cast<const char*>(vbuf + ((size_t)sl * H + h) * smax * DV);
+  const int32_t* const prow = page_table + (size_t)b * max_pages;
+  auto issue_tile = [&](int j) {
+    MLA_LDS char* const ent = ring + (j % NBUF) * ENT;
+    int page = ld_uniform(prow + min(TT * j / kPage, max_pages - 1));
+    page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+    const char* const rbase = kv + (size_t)page * kPage * ROWB;
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      if (u < 2 || u > 2) {  // K_nope (u < 2) or V (u > 2): four 256-byte rows per KiB
+        const int i = u < 2 ? wave + 4 * u : wave + 4 * u - 12;
+        const int r = 4 * i + (lane >> 4), t = min(TT * j + r, S - 1);
+        const int c = (lane & 15) ^ (r & 15);
+        if (u < 2) load_lds_16(kb, (uint32_t)(t * 256 + 16 * c), ent + 1024 * i);
+        else load_lds_16(vb, (uint32_t)(t * 256 + 16 * c), ent + KNB + KRB + 1024 * i);
+      } else {  // k_R: eight 128-byte rows per KiB, from the page's cache rows
+        const int r = 8 * wave + (lane >> 3), t = min(TT * j + r, S - 1);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        load_lds_16(rbase, (uint32_t)((t % kPage) * ROWB + DC * 2 + 16 * c),
+                    ent + KNB + 1024 * wave);
+      }
+    }
+  };
+  int issued = 0;
+  if (loader)
+    for (; issued < NBUF - 1 && issued < ntiles; ++issued) issue_tile(issued);
+
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int G16 = lane >> 4, q16 = lane & 15;
+  const int qi = i0 + 32 * wave + r32;        // this lane's query row
+  const int qc = qi < T ? qi : T - 1;         // (rows past T load a valid row, write nothing)
+  const int pos = S - T + qi;                 // its position: attends to tokens 0 .. pos
+  // query operand: B of S^T = K Q^T, lane = row r32, dims 16s + 8hi .. +8. Waiting for it
+  // (the loads complete in order) also lands the tiles issued above.
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qn = q_nope + (((size_t)b * T + qc) * H + h) * DN;
+    const uint16_t* qr = q_rope + (((size_t)b * T + qc) * H + h) * DR;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const int d = 16 * st + 8 * hi;
+      qf[st] = d < DN ? *reinterpret_cast<const bf16x8*>(qn + d)
+                      : *reinterpret_cast<const bf16x8*>(qr + (d - DN));
+    }
+#pragma unroll
+    for (int st = 0; st < KS; ++st) settle(qf[st]);
+  }
+  wait_vmcnt<0>();
+  block_sync();  // tile 0 (and those after it) landed
+
+  f32x16 acc[DV / 32] = {};
+  float m_run = -INFINITY, l_lane = 0.f;
+  for (int j = 0; j < ntiles; ++j) {
+    // tile j + NBUF - 1 into the entry of tile j - 1, free since the barrier that ended it
+    if (loader && issued < ntiles) issue_tile(issued++);
+    const MLA_LDS char* const ent = ring + (j % NBUF) * ENT;
+    // ---- S^T[32 tokens x 32 rows]: lane holds row r32, tokens 8(i/4) + 4hi + i%4
+    f32x16 s = {};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const int c = 2 * st + hi;
+      const bf16x8 a = st < DN / 16
+          ? lds_read_b128(ent, r32 * 256 + 16 * (c ^ (r32 & 15)))
+          : lds_read_b128(ent, KNB + r32 * 128 + 16 * ((c - DN / 8) ^ ((r32 >> 1) & 7)));
+      s = mfma_32x32x16(a, qf[st], s);
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = TT * j + 8 * (i >> 2) + 4 * hi + (i & 3);
+      const float v = t <= pos ? s[i] * scale_log2 : -INFINITY;
+      s[i] = v;
+      mt = fmaxf(mt, v);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    // a row with no token so far keeps m = -inf: its weights are 0 and nothing is rescaled
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f_fast(m_run - m_new);
+    m_run = m_new;
+#pragma unroll
+    for (int nb = 0; nb < DV / 32; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
+    float lsum = 0.f;
+    bf16x8 pa[2];  // contraction block kk: tokens 16kk + 8(j/4) + 4hi + j%4
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float x = s[8 * kk + jj];
+        const __bf16 p = (__bf16)(x == -INFINITY ? 0.f : exp2f_fast(x - m_new));
+        pa[kk][jj] = p;
+        lsum += (float)p;
+      }
+    l_lane = l_lane * alpha + lsum;
+    // ---- O^T[DV x 32 rows] += V^T P^T (transposing reads of four consecutive tokens)
+#pragma unroll
+    for (int nb = 0; nb < DV / 32; ++nb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x4 v2[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int t = 16 * kk + 8 * p + 4 * (G16 >> 1) + (q16 >> 2);
+          const int c0 = 32 * nb + 16 * (G16 & 1) + 4 * (q16 & 3);  // first of 4 columns
+          v2[p] = lds_read_tr16(ent, KNB + KRB + t * 256 + 16 * ((c0 >> 3) ^ (t & 15)) +
+                                         (c0 & 7) * 2);
+        }
+        acc[nb] = mfma_32x32x16(cat4(v2[0], v2[1]), pa[kk], acc[nb]);
+      }
+    if (j + 1 < ntiles) {
+      // tile j+1 landed: the loading waves wait until only the tiles after it are in flight
+      if (loader) pfa_wait_tiles<NBUF - 2>(issued - (j + 2));
+      block_sync();
+    }
+  }
+  // ---- normalise and write: lane holds row qi, columns 32nb + 8(i/4) + 4hi + i%4
+  const float lt = l_lane + __shfl_xor(l_lane, 32, 64);
+  if (qi < T) {
+    const float il = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* o = out + (((size_t)b * T + qi) * H + h) * DV;
+#pragma unroll
+    for (int nb = 0; nb < DV / 32; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = acc[nb];
+        const u32x2 w = {pack_bf16x2(a[4 * g] * il, a[4 * g + 1] * il),
+                         pack_bf16x2(a[4 * g + 2] * il, a[4 * g + 3] * il)};
+        *reinterpret_cast<u32x2*>(o + 32 * nb + 8 * g + 4 * hi) = w;
+      }
+    if (lse_out && hi == 0)
+      lse_out[((size_t)b * T + qi) * H + h] =
+          lt > 0.f ? (m_run + log2f_fast(lt)) * kLn2 : -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------- launch
 hipError_t launch_prefill(int shape, const void* q_nope, const void* q_rope, const void* W_UK,
                           const void* W_UV, const void* kv, const int32_t* page_table,
@@ -423,12 +617,19 @@ hipError_t launch_prefill(int shape, const void* q_nope, const void* q_rope, con
                         (const uint16_t*)W_UK, (const uint16_t*)W_UVt, (uint16_t*)kbuf,
                         (uint16_t*)vbuf, smax);
       if (e != hipSuccess) return e;
-      e = launch_kernel(prefill_attn_kernel<H, DN, DC, DR, DV>,
-                        dim3((T + pf::QB - 1) / pf::QB, H, g), dim3(pf::NT), Ls,
-                        (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const char*)kv,
-                        page_table, seq_lens, b0, max_pages, num_pages, T,
-                        (const uint16_t*)kbuf, (const uint16_t*)vbuf, smax, scale_log2,
-                        (uint16_t*)out, lse_out);
+      if constexpr (H == 128 && DN == 128 && DR == 64 && DV == 128)
+        e = launch_kernel(prefill_attn_ds_kernel, dim3((T + pfa::QB - 1) / pfa::QB, H, g),
+                          dim3(pfa::NT), Ls, (const uint16_t*)q_nope, (const uint16_t*)q_rope,
+                          (const char*)kv, page_table, seq_lens, b0, max_pages, num_pages, T,
+                          (const uint16_t*)kbuf, (const uint16_t*)vbuf, smax, scale_log2,
+                          (uint16_t*)out, lse_out);
+      else
+        e = launch_kernel(prefill_attn_kernel<H, DN, DC, DR, DV>,
+                          dim3((T + pf::QB - 1) / pf::QB, H, g), dim3(pf::NT), Ls,
+                          (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const char*)kv,
+                          page_table, seq_lens, b0, max_pages, num_pages, T,
+                          (const uint16_t*)kbuf, (const uint16_t*)vbuf, smax, scale_log2,
+                          (uint16_t*)out, lse_out);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
