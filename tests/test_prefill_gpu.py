@@ -37,6 +37,17 @@ def _inp(dims, lens, T, seed):
     return inp
 
 
+def _inp_pages(dims, lens, T, seed, max_pages):
+    """_inp with the page-table rows (and so the per-sequence workspace rows) max_pages long."""
+    inp = W.make_inputs(len(lens), dims["H"], dims["d_n"], dims["d_c"], dims["d_R"],
+                        dims["d_v"], lens, seed, max_pages=max_pages)
+    g = torch.Generator().manual_seed(seed + 1)
+    B = len(lens)
+    inp["q_nope"] = torch.randn(B, T, dims["H"], dims["d_n"], generator=g).to(torch.bfloat16)
+    inp["q_rope"] = torch.randn(B, T, dims["H"], dims["d_R"], generator=g).to(torch.bfloat16)
+    return inp
+
+
 def _run(M, d, **kw):
     out, lse = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], d["kv_pages"],
                         d["page_table"], d["seq_lens"], return_lse=True, **kw)
@@ -163,3 +174,56 @@ def test_timed_entry_point_brackets_the_branch(M):
     assert hip.ms(ev[0], ev[1]) >= 0 and hip.ms(ev[4], ev[5]) >= 0
     for e in ev:
         hip.destroy(e)
+
+
+def test_decompressed_branch_graph_replays_match_eager(M):
+    # the decompressed branch captured in a HIP graph: transpose, then per group of sequences
+    # the decompression and the attention (here two groups: at 16384 rows per sequence one
+    # sequence fills a group), replayed with the inputs swapped between replays and eager work
+    # in between; every replay bit for bit equal to the eager call on its inputs
+    T = 256
+    lens = [700, 300]
+    a = to_dev(_inp_pages(DS, lens, T, 71, 256))
+    b = to_dev(_inp_pages(DS, lens, T, 72, 256))
+
+    def call(d, **kw):
+        return M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], d["kv_pages"],
+                        d["page_table"], d["seq_lens"], return_lse=True, **kw)
+
+    def eager(d):
+        o, l = call(d)
+        torch.cuda.synchronize()
+        return o, l
+
+    ref = {"a": eager(a), "b": eager(b)}
+    assert not torch.equal(ref["a"][0], ref["b"][0])
+    st = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in a.items()}
+    out = torch.empty_like(ref["a"][0])
+    lse = torch.empty_like(ref["a"][1])
+    dm = M.make_dims(st["q_nope"], st["q_rope"], st["W_UK"], st["W_UV"], st["kv_pages"],
+                     st["page_table"])
+    ws = torch.empty(M.workspace_bytes(dm), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(st, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say("prefill graph capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(st, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    sets = {"a": a, "b": b}
+    for rep, name in enumerate(["b", "a", "b"]):
+        for k in ("q_nope", "q_rope", "W_UK", "W_UV", "kv_pages", "page_table", "seq_lens"):
+            st[k].copy_(sets[name][k])
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("prefill graph replay", rep, name)
+        assert torch.equal(out.view(torch.int16), ref[name][0].view(torch.int16)), (rep, name)
+        assert torch.equal(lse.view(torch.int32), ref[name][1].view(torch.int32)), (rep, name)
+        eager(sets["a" if name == "b" else "b"])
