@@ -45,6 +45,13 @@ def errors(gpu, ref):
     return rel, mx
 
 
+def to_bf16_bits(a):
+    """fp64 array -> uint16 bf16 bit patterns, rounded to nearest (for building the oracle's
+    own copy of a cache from its fp64 rows)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
 def check_against_oracle(M, inp, pairs=None, units=0, label=""):
     """Runs the GPU decode (with lse) and the oracle; asserts the tolerances; returns errors."""
     say(label, "B=%d H=%d d_c=%d units=%d" % (inp["B"], inp["H"], inp["d_c"], units))

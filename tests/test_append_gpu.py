@@ -8,7 +8,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import check_against_oracle, need_gpu, say, to_dev
+from tests.gpu_helpers import (LSE_ABS, MAX_ABS, REL_L2, errors, need_gpu, say, to_dev,
+                               to_bf16_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,13 +94,40 @@ def test_tokens_past_the_page_table_row_are_not_written(M):
     assert changed[p0, 63] and int(changed.sum()) == 1
 
 
+def _decode_vs_oracle(M, inp, kv_gpu, seq_lens, kv_ref, label, kv_scales=None):
+    """GPU decode over the cache the GPU append wrote, against the oracle's decode over its own
+    cache (the same initial pool with the oracle's append written in)."""
+    d = to_dev(inp)
+    out, lse = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv_gpu,
+                        d["page_table"], seq_lens.cuda(), return_lse=True, kv_scales=kv_scales)
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    args = list(W.oracle_args(inp))
+    args[4], args[6] = kv_ref, seq_lens.numpy()
+    ref, ref_lse = oracle.decode(*args)
+    rel, mx = errors(out, ref)
+    lerr = float(np.max(np.abs(lse - ref_lse)))
+    say(label, "rel_l2=%.3e max_abs=%.3e lse_err=%.3e" % (rel, mx, lerr))
+    assert np.all(np.isfinite(out))
+    assert rel <= REL_L2 and mx <= MAX_ABS and lerr <= LSE_ABS, (label, rel, mx, lerr)
+
+
 def test_decode_reads_appended_tokens(M):
     # append one token to each of 3 sequences on the GPU, then decode over the longer
-    # sequences; the oracle decodes the same cache bytes
-    inp, kv, before = _append_and_check(M, "deepseek", [100, 64, 300], 1, 44)
-    inp["kv_pages"] = kv.cpu()
-    inp["seq_lens"] = before + 1
-    check_against_oracle(M, inp, label="decode after append")
+    # sequences; the oracle decodes its own cache: the initial pool with its fp64 append
+    # rounded to bf16 at the new slots (the two caches may differ in a last bit)
+    inp, x, Wd, Wr, before = _case("deepseek", [100, 64, 300], 1, 44)
+    kv_ref = W.u16(inp["kv_pages"]).copy()
+    kv = inp["kv_pages"].cuda()
+    say("decode after append")
+    M.cache_append(x.cuda(), Wd.cuda(), Wr.cuda(), kv, inp["page_table"].cuda(), before.cuda())
+    rows, where = oracle.cache_append(W.u16(x), W.u16(Wd), W.u16(Wr), inp["page_table"].numpy(),
+                                      before.numpy())
+    bits = to_bf16_bits(rows)
+    for b in range(rows.shape[0]):
+        page, slot = where[b, 0]
+        kv_ref[page, slot] = bits[b, 0]
+    _decode_vs_oracle(M, inp, kv, before + 1, kv_ref, "decode after append")
 
 
 def test_unallocated_page_entry_is_not_written(M):
@@ -235,15 +263,20 @@ def test_fp8_append_then_decode(M):
     kv8, sc = kv8_0.clone().cuda(), sc0.clone().cuda()
     M.cache_append(x.cuda(), Wd.cuda(), Wr.cuda(), kv8, inp["page_table"].cuda(), before.cuda(),
                    kv_scales=sc)
-    torch.cuda.synchronize()
-    d = to_dev(inp)
     say("fp8 append then decode")
-    out = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], kv8, d["page_table"],
-                   d["seq_lens"], kv_scales=sc)
-    torch.cuda.synchronize()
-    args = list(W.oracle_args(inp))
-    args[4] = oracle.dequant_fp8_cache(kv8.cpu().numpy(), sc.cpu().numpy(), inp["d_c"])
-    ref, _ = oracle.decode(*args)
-    g = out.float().cpu().numpy()
-    rel = float(np.linalg.norm(g - ref) / np.linalg.norm(ref))
-    assert rel <= 5e-3, rel
+    # the oracle's own FP8 cache: the initial pool with its append (codes, scales, and k_R
+    # rounded to bf16) written in, read through the format's dequantisation
+    codes, scales, kr, where = oracle.cache_append_fp8(
+        W.u16(x), W.u16(Wd), W.u16(Wr), inp["page_table"].numpy(), before.numpy())
+    d_c = inp["d_c"]
+    kv8_ref, sc_ref = kv8_0.numpy().copy(), sc0.numpy().copy()
+    krb = to_bf16_bits(kr)
+    for b in range(len(lens)):
+        for i in range(T):
+            page, slot = where[b, i]
+            kv8_ref[page, slot, :d_c] = codes[b, i]
+            kv8_ref[page, slot, d_c:] = krb[b, i].view(np.uint8)
+            sc_ref[page, slot] = scales[b, i]
+    kv_ref = oracle.dequant_fp8_cache(kv8_ref, sc_ref, d_c)
+    _decode_vs_oracle(M, inp, kv8, inp["seq_lens"], kv_ref, "fp8 append then decode",
+                      kv_scales=sc)

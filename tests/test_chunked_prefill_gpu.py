@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import LSE_ABS, MAX_ABS, REL_L2, errors, need_gpu, say
+from tests.gpu_helpers import LSE_ABS, MAX_ABS, REL_L2, errors, need_gpu, say, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -26,12 +26,6 @@ HIDDEN = 1024
 @pytest.fixture(scope="module")
 def M():
     return need_gpu()
-
-
-def _bf16_bits(a):
-    """fp64 array -> uint16 bf16 bit patterns, rounded to nearest."""
-    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).view(torch.int16) \
-        .numpy().view(np.uint16)
 
 
 @pytest.mark.parametrize("chunk", [256, 512])
@@ -72,7 +66,7 @@ def test_chunked_prefill_matches_oracle(M, chunk):
         out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
         # the oracle: its own append into its own cache, then the causal multi-token decode
         rows, where = oracle.cache_append(W.u16(x), W.u16(Wd), W.u16(Wr), pt.numpy(), lens)
-        bits = _bf16_bits(rows)
+        bits = to_bf16_bits(rows)
         for b in range(B):
             for i in range(C):
                 page, slot = where[b, i]
