@@ -336,6 +336,139 @@ def dequant_fp8_cache(kv8, scales, d_c):
     return out
 
 
+# ---- MXFP4 latent cache (the pages' 4-bit quantised gather of the latent cache,
+# bhfrc.com/news/60867 S1 and S5, in the OCP Microscaling (MX) v1.0 format: blocks of 32
+# elements, each an FP4 E2M1 value, sharing one E8M0 power-of-two scale)
+
+MX_BLOCK = 32
+FP4_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)  # E2M1 codes 0..7, see below
+
+
+def fp4_e2m1_value(code):
+    """Exact value of FP4 E2M1 codes (4 bits: sign, 2 exponent bits with bias 1, 1 mantissa
+    bit; exponent 0 is subnormal: 0 or 0.5; no infinities or NaN), as fp64. Only the low four
+    bits of each code are read."""
+    c = np.asarray(code, dtype=np.int64) & 0xF
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(e.astype(np.float64) - 1.0))
+    return np.where(c & 0x8, -mag, mag)
+
+
+def fp4_e2m1_encode(v):
+    """The E2M1 code nearest to each value v (fp64, finite): among the 8 non-negative E2M1
+    values, the nearest to min(|v|, 6) (magnitudes above the largest, 6, saturate to it, as the
+    MX conversion does), a tie going to the even code (mantissa bit 0), with the sign of v in
+    bit 3 unless the magnitude code is 0 (zero is stored as +0)."""
+    v = np.asarray(v, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("E2M1 encodes finite values")
+    vals = fp4_e2m1_value(np.arange(8))          # increasing in the code
+    a = np.minimum(np.abs(v), vals[7])
+    hi = np.clip(np.searchsorted(vals, a), 0, 7)  # first value >= |v|
+    lo = np.clip(hi - 1, 0, 7)
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a == vals[hi], hi, pick)
+    return (pick | np.where((v < 0) & (pick != 0), 0x8, 0)).astype(np.uint8)
+
+
+def e8m0_value(code):
+    """Exact value of E8M0 scale bytes: 2^(code - 127), code 255 is NaN."""
+    c = np.asarray(code, dtype=np.int64)
+    return np.where(c == 255, np.nan, np.exp2(c.astype(np.float64) - 127.0))
+
+
+def mx_scale_exponent(amax):
+    """The shared exponent X of an MXFP4 block (its scale 2^X): floor(log2(amax)) minus 2, the
+    exponent of E2M1's largest value (6 = 1.5 * 2^2), kept within E8M0's -127 .. 127; 0 for an
+    all-zero block. With amax = m * 2^k, 0.5 <= m < 1, floor(log2(amax)) = k - 1 (exact)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    _, k = np.frexp(amax)
+    return min(127, max(-127, int(k) - 1 - 2))
+
+
+def quantise_mxfp4_row(c):
+    """A latent row c (fp64, length a multiple of 32) as MXFP4: per block of 32 elements the
+    shared exponent X = mx_scale_exponent(max |c_block|) and the E2M1 codes of c_block / 2^X.
+    Returns (codes uint8 [len(c)], one code per element, and scale bytes uint8 [len(c)/32],
+    X + 127)."""
+    c = np.asarray(c, dtype=np.float64)
+    if c.size % MX_BLOCK:
+        raise ValueError("an MXFP4 row holds whole blocks of 32 elements")
+    blocks = c.reshape(-1, MX_BLOCK)
+    codes = np.zeros(blocks.shape, dtype=np.uint8)
+    scales = np.zeros(blocks.shape[0], dtype=np.uint8)
+    for k, blk in enumerate(blocks):
+        X = mx_scale_exponent(np.max(np.abs(blk)))
+        codes[k] = fp4_e2m1_encode(blk * 2.0 ** -X)
+        scales[k] = X + 127
+    return codes.reshape(-1), scales
+
+
+def pack_fp4(codes):
+    """E2M1 codes [..., n] (n even) as bytes [..., n/2]: element 2k in the low nibble of byte
+    k, element 2k + 1 in its high nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
+
+
+def unpack_fp4(packed):
+    """The inverse of pack_fp4: bytes [..., m] -> codes [..., 2m]."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def dequant_mxfp4_cache(kv4, scales, d_c):
+    """The bf16 cache that an MXFP4 cache stands for: token row [c_KV as packed E2M1
+    (d_c/2 bytes) | k_R bf16 (2*d_R bytes)] and per token d_c/32 E8M0 scale bytes;
+    c_KV[c] = value(code c) * 2^(scale[c/32] - 127), k_R copied. Returns uint16 bf16 bits
+    [P, 64, d_c + d_R]; a NaN scale (255) gives NaN values. Every finite product is a bf16
+    value (at most 2 significant bits, exponent in range); the function checks that rather
+    than assume it."""
+    kv4 = np.ascontiguousarray(kv4, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales, dtype=np.uint8)
+    P, ps, w4 = kv4.shape
+    d_R = (w4 - d_c // 2) // 2
+    nb = d_c // MX_BLOCK
+    if sc.shape != (P, ps, nb):
+        raise ValueError("scales must be [P, 64, d_c/32]")
+    v = fp4_e2m1_value(unpack_fp4(kv4[:, :, :d_c // 2])) * \
+        np.repeat(e8m0_value(sc), MX_BLOCK, axis=2)
+    f = v.astype(np.float32)
+    nan = np.isnan(v)
+    with np.errstate(invalid="ignore"):
+        ok = nan | (f.astype(np.float64) == v)
+    bits = f.view(np.uint32)
+    if not np.all(ok) or np.any((bits[~nan] & 0xFFFF) != 0):
+        raise ValueError("dequantised c_KV is not exactly a bf16 value")
+    out = np.empty((P, ps, d_c + d_R), dtype=np.uint16)
+    out[:, :, :d_c] = np.where(nan, 0x7FC0, bits >> 16).astype(np.uint16)
+    out[:, :, d_c:] = kv4[:, :, d_c // 2:].copy().view(np.uint16).reshape(P, ps, d_R)
+    return out
+
+
+def cache_append_mxfp4(x, W_DKV, W_KR, page_table, seq_lens, base=10000.0):
+    """Cache append into an MXFP4 cache: cache_append's rows with the latent part quantised per
+    token and block (quantise_mxfp4_row) and the RoPE key left in fp64 (stored as bf16).
+    Returns (codes uint8 [B, T, d_c] one per element, scale bytes uint8 [B, T, d_c/32],
+    k_R fp64 [B, T, d_R], where [B, T, 2])."""
+    rows, where = cache_append(x, W_DKV, W_KR, page_table, seq_lens, base)
+    d_c = _u16(W_DKV).shape[0]
+    B, T = rows.shape[:2]
+    codes = np.zeros((B, T, d_c), dtype=np.uint8)
+    scales = np.zeros((B, T, d_c // MX_BLOCK), dtype=np.uint8)
+    for b in range(B):
+        for i in range(T):
+            codes[b, i], scales[b, i] = quantise_mxfp4_row(rows[b, i, :d_c])
+    return codes, scales, rows[:, :, d_c:], where
+
+
 def _f64(u16):
     """Exact fp64 value of bf16 bit patterns."""
     return (np.asarray(u16, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -132,6 +132,39 @@ def oracle_args(inp):
 FP8_NAN = 0x7F  # an e4m3 NaN byte
 
 
+def _used_slots(inp, P, ps):
+    used = torch.zeros(P, ps, dtype=torch.bool)
+    for b in range(inp["B"]):
+        S = int(inp["seq_lens"][b])
+        for t in range(S):
+            used[int(inp["page_table"][b, t // ps]), t % ps] = True
+    return used
+
+
+def mxfp4_cache(inp, seed=0, scale_codes=(122, 127), poison=False):
+    """A synthetic MXFP4 cache with the page geometry and k_R of ``inp``: every c_KV element a
+    uniformly drawn 4-bit E2M1 code, every block of 32 elements a scale byte (E8M0, 2^(code-127))
+    drawn uniformly from [scale_codes[0], scale_codes[1]] (seeded). Returns (kv4 uint8
+    [P, 64, d_c/2 + 2*d_R] with rows [c_KV codes, two per byte, element 2k in the low nibble |
+    k_R bf16 bytes], scales uint8 [P, 64, d_c/32]). With poison=True every slot that is not
+    part of a sequence holds 0xFF bytes and NaN scales (255)."""
+    kv = inp["kv_pages"]
+    P, ps, w = kv.shape
+    d_c = inp["d_c"]
+    g = torch.Generator().manual_seed(int(seed))
+    nib = torch.randint(0, 16, (P, ps, d_c), generator=g, dtype=torch.int32)
+    packed = (nib[:, :, 0::2] | (nib[:, :, 1::2] << 4)).to(torch.uint8)
+    scales = torch.randint(int(scale_codes[0]), int(scale_codes[1]) + 1, (P, ps, d_c // 32),
+                           generator=g, dtype=torch.int32).to(torch.uint8)
+    kr = kv[:, :, d_c:].contiguous().view(torch.uint8).reshape(P, ps, 2 * (w - d_c))
+    kv4 = torch.cat([packed, kr], dim=2).contiguous()
+    if poison:
+        used = _used_slots(inp, P, ps)
+        kv4[~used] = 0xFF
+        scales[~used] = 255
+    return kv4, scales
+
+
 def fp8_cache(inp, seed=0, exps=(-6, -2), poison=False):
     """An FP8 copy of the cache of ``inp``: each token's c_KV is divided by a power of two
     2^k, k drawn uniformly from [exps[0], exps[1]] per token slot (seeded), and cast to FP8
@@ -151,11 +184,7 @@ def fp8_cache(inp, seed=0, exps=(-6, -2), poison=False):
     if bool((((codes & 0x7F) == 0x7F) & ~torch.isnan(c)).any()):  # NaN past 464
         raise ValueError("c_KV out of the FP8 range for these scales")
     if poison:
-        used = torch.zeros(P, ps, dtype=torch.bool)
-        for b in range(inp["B"]):
-            S = int(inp["seq_lens"][b])
-            for t in range(S):
-                used[int(inp["page_table"][b, t // ps]), t % ps] = True
+        used = _used_slots(inp, P, ps)
         kv8[~used] = FP8_NAN
         scales[~used] = float("nan")
     return kv8, scales
