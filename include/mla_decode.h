@@ -18,8 +18,9 @@
  * Supported shapes: (num_heads, d_nope, d_latent, d_rope, d_v) = (128, 128, 512, 64, 128),
  * the DeepSeek-V2/V3 widths (bhfrc.com/news/60867 S3), and (32, 120, 64, 8, 128), the MHA2MLA
  * Llama-2-7B attention config (lpnh.cn/news/2494972 S3.2). page_size must be 64. The cache is
- * bf16 (mla_decode, mla_decode_timed, mla_decode_out) or FP8 E4M3 with a power-of-two scale
- * per token (mla_decode_fp8).
+ * bf16 (mla_decode, mla_decode_timed, mla_decode_out), FP8 E4M3 with a power-of-two scale
+ * per token (mla_decode_fp8), or MXFP4 with an E8M0 scale per token and block of 32 latent
+ * elements (mla_decode_mxfp4, MHA2MLA widths).
  *
  * Conventions for every entry point:
  *   - tensors are dense row-major, in device memory, 16-byte aligned; bf16 is stored as its
@@ -35,8 +36,8 @@
  *     [0, max_pages_per_seq * 64] and page ids to [0, num_pages - 1], so a bad table gives
  *     wrong numbers, not a memory fault. A sequence with S_b <= 0 gets out = 0, lse = -inf.
  *   - with MLA_CHECK=1 in the environment, every decode entry point first validates
- *     seq_lens, the page-table entries the sequences use and (FP8 cache) the scales of the
- *     slots they use on the device, synchronises the stream, and returns
+ *     seq_lens, the page-table entries the sequences use and (FP8 or MXFP4 cache) the scales
+ *     of the slots they use on the device, synchronises the stream, and returns
  *     MLA_ERR_DEVICE_CHECK (with nothing else enqueued) when one is out of range. This
  *     debugging mode is the only case in which the library synchronises.
  *   - page-table entries at or past ceil(S_b / 64) and cache slots at or past S_b are never
@@ -106,14 +107,14 @@ typedef struct {
                                   absorbed branch serves the call. The decompressed branch
                                   reads a bf16 cache and writes out [B][T][H][d_v]
                                   (mla_decode, mla_decode_timed, mla_decode_noalloc);
-                                  mla_decode_out and mla_decode_fp8 return
-                                  MLA_ERR_UNSUPPORTED for it. Both branches compute the same
-                                  result up to rounding.                                    */
+                                  mla_decode_out, mla_decode_fp8 and mla_decode_mxfp4
+                                  return MLA_ERR_UNSUPPORTED for it. Both branches compute
+                                  the same result up to rounding.                           */
 } mla_dims_t;
 
 /* Bytes of scratch a call with these dims needs (pure function of the dims, host only), for
- * either cache format (mla_decode and mla_decode_fp8). Returns 0 when the dims are invalid or
- * unsupported. */
+ * every cache format (mla_decode, mla_decode_fp8 and mla_decode_mxfp4). Returns 0 when the
+ * dims are invalid or unsupported. */
 size_t mla_decode_workspace_bytes(const mla_dims_t* dims);
 
 /*
@@ -201,6 +202,35 @@ mla_status_t mla_decode_fp8(const mla_dims_t* dims, const void* q_nope, const vo
                             size_t workspace_bytes, void* stream, void* const* stage_events);
 
 /*
+ * The decode over a 4-bit quantised latent cache (bhfrc.com/news/60867 S1 and S5 quantise the
+ * latent cache the decode gathers; this is its microscaled 4-bit form, the OCP Microscaling
+ * (MX) v1.0 MXFP4 format): c_KV in blocks of 32 elements, each element a 4-bit float, each
+ * block sharing one power-of-two scale. MHA2MLA widths only (MLA_ERR_UNSUPPORTED at the
+ * DeepSeek widths): a token takes d_latent/2 + 2*d_rope bytes plus d_latent/32 scale bytes
+ * (48 + 2 = 50 bytes, against 144 in bf16 and 84 in FP8).
+ *   kv_pages   uint8 [num_pages, 64, d_latent/2 + 2*d_rope]  token row = [c_KV as d_latent
+ *              E2M1 codes, two per byte, element 2k in the low nibble of byte k (E2M1: sign,
+ *              2 exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3,
+ *              4, 6) | k_R as d_rope bf16 values]
+ *   kv_scales  uint8 [num_pages, 64, d_latent/32]  E8M0 scale bytes of each slot's blocks:
+ *              c_KV[c] = value(code c) * 2^(kv_scales[page][slot][c/32] - 127).
+ *              Precondition: no slot a sequence uses holds 255 (E8M0's NaN); the MLA_CHECK
+ *              mode reports one (MLA_ERR_DEVICE_CHECK). Slots no sequence uses may hold
+ *              anything.
+ * Each dequantised c_KV element is a bf16 value, formed exactly, and the decode then runs as in
+ * mla_decode: the result is that of mla_decode on the bf16 cache holding those values. Slots at
+ * or past S_b are never read into the result. kv_scales must be 16-byte aligned and non-NULL;
+ * everything else, including q_len, the workspace size and stage_events, is as for
+ * mla_decode_timed.
+ */
+mla_status_t mla_decode_mxfp4(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                              const void* W_UK, const void* W_UV, const void* kv_pages,
+                              const uint8_t* kv_scales, const int32_t* page_table,
+                              const int32_t* seq_lens, void* out, float* lse_out,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              void* const* stage_events);
+
+/*
  * The decode with the output projection merged into the up-projection (lpnh.cn/news/2494972
  * S2.2: W_uv and W_o are merged into one matrix offline): instead of out[b,h,:] = o_lat W_UV[h]
  * it returns
@@ -260,8 +290,9 @@ typedef struct {
     float rope_base;           /* RoPE base; <= 0 means 10000                               */
 } mla_append_dims_t;
 
-/* Bytes of scratch mla_cache_append and mla_cache_append_fp8 need for these dims (fp32
- * partial rows of the contraction, split over the model width); 0 if the dims are invalid. */
+/* Bytes of scratch mla_cache_append, mla_cache_append_fp8 and mla_cache_append_mxfp4 need for
+ * these dims (fp32 partial rows of the contraction, split over the model width); 0 if the dims
+ * are invalid. */
 size_t mla_cache_append_workspace_bytes(const mla_append_dims_t* dims);
 
 mla_status_t mla_cache_append(const mla_append_dims_t* dims, const void* x, const void* W_DKV,
@@ -284,6 +315,25 @@ mla_status_t mla_cache_append_fp8(const mla_append_dims_t* dims, const void* x,
                                   const int32_t* page_table, const int32_t* seq_lens,
                                   void* kv_pages, float* kv_scales, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/*
+ * The same append into an MXFP4 cache (the layout mla_decode_mxfp4 reads): kv_pages uint8
+ * [num_pages, 64, d_latent/2 + 2*d_rope] with rows [c_KV as E2M1 codes, two per byte |
+ * k_R as bf16], and kv_scales uint8 [num_pages, 64, d_latent/32]. For each new token and
+ * block of 32 latent elements (the OCP MX conversion): the shared exponent is
+ * X = floor(log2(max |c_KV[c]|)) - 2 over the block (2 is the exponent of E2M1's largest
+ * value, 6), kept within -127 .. 127, and 0 for an all-zero block; the scale byte is X + 127;
+ * element c is c_KV[c] / 2^X rounded to the nearest E2M1 value, ties to the even code,
+ * magnitudes above 6 saturating to 6, zero stored as +0 (c_KV as fp32 sums, not rounded to
+ * bf16 first). k_R is rotated and rounded to bf16 as above. d_latent must be a multiple of
+ * 32. Everything else is as for mla_cache_append; kv_scales must be non-NULL and 16-byte
+ * aligned.
+ */
+mla_status_t mla_cache_append_mxfp4(const mla_append_dims_t* dims, const void* x,
+                                    const void* W_DKV, const void* W_KR,
+                                    const int32_t* page_table, const int32_t* seq_lens,
+                                    void* kv_pages, uint8_t* kv_scales, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * Logical copy of the paged cache, through the same page addressing and LDS staging the

@@ -72,12 +72,16 @@ def lib():
         L.mla_decode_timed.argtypes = [dp] + [vp] * 10 + [sz, vp, ctypes.POINTER(vp)]
         L.mla_decode_fp8.restype = c_int
         L.mla_decode_fp8.argtypes = [dp] + [vp] * 11 + [sz, vp, ctypes.POINTER(vp)]
+        L.mla_decode_mxfp4.restype = c_int
+        L.mla_decode_mxfp4.argtypes = [dp] + [vp] * 11 + [sz, vp, ctypes.POINTER(vp)]
         L.mla_decode_out.restype = c_int
         L.mla_decode_out.argtypes = [dp, ctypes.c_int32] + [vp] * 10 + [sz, vp]
         L.mla_cache_append.restype = c_int
         L.mla_cache_append.argtypes = [ctypes.POINTER(AppendDims)] + [vp] * 7 + [sz, vp]
         L.mla_cache_append_fp8.restype = c_int
         L.mla_cache_append_fp8.argtypes = [ctypes.POINTER(AppendDims)] + [vp] * 8 + [sz, vp]
+        L.mla_cache_append_mxfp4.restype = c_int
+        L.mla_cache_append_mxfp4.argtypes = [ctypes.POINTER(AppendDims)] + [vp] * 8 + [sz, vp]
         L.mla_cache_append_workspace_bytes.restype = sz
         L.mla_cache_append_workspace_bytes.argtypes = [ctypes.POINTER(AppendDims)]
         L.mla_gather_pages.restype = c_int
@@ -179,9 +183,11 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
     kernel_events: optional six raw hipEvent_t handles (int or None), passed to
     mla_decode_timed, which binds them to the start and end of the absorb, attention and
     combine kernels.
-    kv_scales: an FP8 cache (mla_decode_fp8): kv_pages is then uint8 [P,64,d_c+2*d_R], token
-    = [c_KV as FP8 e4m3 bytes | k_R bf16], and kv_scales fp32 [P,64] holds each token's c_KV
-    scale.
+    kv_scales: a quantised cache. fp32 [P,64]: an FP8 cache (mla_decode_fp8), kv_pages uint8
+    [P,64,d_c+2*d_R], token = [c_KV as FP8 e4m3 bytes | k_R bf16], one scale per token.
+    uint8 [P,64,d_c/32]: an MXFP4 cache (mla_decode_mxfp4, MHA2MLA widths), kv_pages uint8
+    [P,64,d_c/2+2*d_R], token = [c_KV as E2M1 codes, two per byte | k_R bf16], an E8M0 scale
+    byte per block of 32 latent elements.
     no_alloc: run mla_decode_noalloc, whose scratch is built into the library (no workspace;
     pass out, and lse when return_lse, so that nothing is allocated here either).
     prefill_threshold: query tokens per sequence from which the decompressed branch serves
@@ -206,13 +212,14 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
         _want(t, n, dt, nd, t.device)
     dims = make_dims(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, max_seq_len,
                      softmax_scale, num_units, prefill_threshold)
+    mx = kv_scales is not None and kv_scales.dtype == torch.uint8
     B, H, d_v = dims.batch, dims.num_heads, dims.d_v
     d_n, d_c, d_R = dims.d_nope, dims.d_latent, dims.d_rope
     lead = (B,) if nq == 3 else (B, dims.q_len)
     _shape(q_rope, "q_rope", lead + (H, d_R))
     _shape(W_UK, "W_UK", (H, d_n, d_c))
     _shape(W_UV, "W_UV", (H, d_c, d_v))
-    row = d_c + d_R if kv_scales is None else d_c + 2 * d_R
+    row = d_c + d_R if kv_scales is None else (d_c // 2 + 2 * d_R if mx else d_c + 2 * d_R)
     _shape(kv_pages, "kv_pages", (kv_pages.shape[0], kv_pages.shape[1], row))
     _shape(page_table, "page_table", (B, page_table.shape[1]))
     _shape(seq_lens, "seq_lens", (B,))
@@ -222,7 +229,10 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
     if lse is not None:
         _want(lse, "lse", torch.float32, nq - 1, lse.device)
         _shape(lse, "lse", lead + (H,))
-    if kv_scales is not None:
+    if mx:
+        _want(kv_scales, "kv_scales", torch.uint8, 3, kv_scales.device)
+        _shape(kv_scales, "kv_scales", tuple(kv_pages.shape[:2]) + (d_c // 32,))
+    elif kv_scales is not None:
         _want(kv_scales, "kv_scales", torch.float32, 2, kv_scales.device)
         _shape(kv_scales, "kv_scales", tuple(kv_pages.shape[:2]))
     if workspace is not None and (not isinstance(workspace, torch.Tensor) or
@@ -259,7 +269,9 @@ def decode(q_nope, q_rope, W_UK, W_UV, kv_pages, page_table, seq_lens, out=None,
         if len(kernel_events) != 6:
             raise ValueError("kernel_events needs six entries (start, end of three kernels)")
         ev = (ctypes.c_void_p * 6)(*[e or None for e in kernel_events])
-    if kv_scales is not None:
+    if mx:
+        code = lib().mla_decode_mxfp4(*args[:6], _ptr(kv_scales), *args[6:], ev)
+    elif kv_scales is not None:
         code = lib().mla_decode_fp8(*args[:6], _ptr(kv_scales), *args[6:], ev)
     elif ev is None:
         code = lib().mla_decode(*args)
@@ -338,9 +350,11 @@ def cache_append(x, W_DKV, W_KR, kv_pages, page_table, seq_lens, rope_base=10000
     x bf16 [B,T,hidden] (or [B,hidden] for one token), W_DKV bf16 [d_c,hidden], W_KR bf16
     [d_R,hidden], kv_pages bf16 [P,64,d_c+d_R], page_table int32 [B,max_pages], seq_lens int32
     [B] (tokens already cached; token i of sequence b goes to position seq_lens[b] + i).
-    kv_scales: an FP8 cache (mla_cache_append_fp8): kv_pages uint8 [P,64,d_c+2*d_R] and
-    kv_scales fp32 [P,64], both written at the new tokens' slots. workspace: a uint8 tensor of
-    at least mla_cache_append_workspace_bytes (allocated here when None).
+    kv_scales: a quantised cache, written at the new tokens' slots with kv_pages. fp32 [P,64]:
+    an FP8 cache (mla_cache_append_fp8), kv_pages uint8 [P,64,d_c+2*d_R]. uint8
+    [P,64,d_c/32]: an MXFP4 cache (mla_cache_append_mxfp4), kv_pages uint8 [P,64,d_c/2+2*d_R].
+    workspace: a uint8 tensor of at least mla_cache_append_workspace_bytes (allocated here
+    when None).
     """
     bf = torch.bfloat16
     dev = kv_pages.device
@@ -357,11 +371,16 @@ def cache_append(x, W_DKV, W_KR, kv_pages, page_table, seq_lens, rope_base=10000
     d.d_latent, d.d_rope = W_DKV.shape[0], W_KR.shape[0]
     _shape(W_DKV, "W_DKV", (d.d_latent, d.hidden))
     _shape(W_KR, "W_KR", (d.d_rope, d.hidden))
-    row = d.d_latent + d.d_rope if kv_scales is None else d.d_latent + 2 * d.d_rope
+    mx = kv_scales is not None and kv_scales.dtype == torch.uint8
+    row = (d.d_latent + d.d_rope if kv_scales is None else
+           d.d_latent // 2 + 2 * d.d_rope if mx else d.d_latent + 2 * d.d_rope)
     _shape(kv_pages, "kv_pages", (kv_pages.shape[0], kv_pages.shape[1], row))
     _shape(page_table, "page_table", (d.batch, page_table.shape[1]))
     _shape(seq_lens, "seq_lens", (d.batch,))
-    if kv_scales is not None:
+    if mx:
+        _want(kv_scales, "kv_scales", torch.uint8, 3, kv_scales.device)
+        _shape(kv_scales, "kv_scales", tuple(kv_pages.shape[:2]) + (d.d_latent // 32,))
+    elif kv_scales is not None:
         _want(kv_scales, "kv_scales", torch.float32, 2, kv_scales.device)
         _shape(kv_scales, "kv_scales", tuple(kv_pages.shape[:2]))
     if workspace is not None and (not isinstance(workspace, torch.Tensor) or
@@ -384,6 +403,8 @@ def cache_append(x, W_DKV, W_KR, kv_pages, page_table, seq_lens, rope_base=10000
     tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
     if kv_scales is None:
         _check(lib().mla_cache_append(*args, *tail))
+    elif mx:
+        _check(lib().mla_cache_append_mxfp4(*args, _ptr(kv_scales), *tail))
     else:
         _check(lib().mla_cache_append_fp8(*args, _ptr(kv_scales), *tail))
     return kv_pages

@@ -172,10 +172,11 @@ namespace {
 // merged W_UVO [hidden][H * d_latent] and out is [rows][hidden] (the combine writes the merged
 // latent rows into the query region of the workspace, dead by then, and a product with W_UVO
 // follows).
-// kv_scales: NULL for the bf16 cache; the per-token scales of an FP8 cache otherwise.
+// kv_format (mla::KvFormat) and kv_scales: NULL for the bf16 cache, the fp32 per-token
+// scales of an FP8 cache, or the E8M0 block scale bytes of an MXFP4 cache.
 mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
                          const void* q_rope, const void* W_UK, const void* W_UV,
-                         const void* kv_pages, const float* kv_scales,
+                         const void* kv_pages, int kv_format, const void* kv_scales,
                          const int32_t* page_table, const int32_t* seq_lens, void* out,
                          float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
                          void* const* stage_events) {
@@ -192,7 +193,10 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
       !aligned16(out) || (lse_out && !aligned16(lse_out)) ||
       (workspace && ((uintptr_t)workspace & 255) != 0))
     return MLA_ERR_MISALIGNED;
-  const bool fp8 = kv_scales != nullptr;
+  if ((kv_format != mla::kKvBf16) != (kv_scales != nullptr)) return MLA_ERR_NULL_ARG;
+  const bool fp8 = kv_format != mla::kKvBf16;  // a quantised cache: FP8 or MXFP4
+  // the MXFP4 cache is read at the MHA2MLA widths only
+  if (kv_format == mla::kKvMxfp4 && s.shape != mla::kShapeMha2Mla) return MLA_ERR_UNSUPPORTED;
   const bool prefill = decompressed(dims);
   // the decompressed branch reads a bf16 cache and writes the per-head output
   if (prefill && (fp8 || hidden > 0)) return MLA_ERR_UNSUPPORTED;
@@ -209,7 +213,8 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
     int* flag = (int*)(ws + (prefill ? PL.flag : L.q_abs));
     int host_flag = 0;
     st = hip_status(mla::launch_check(seq_lens, page_table, B, mp, dims->num_pages,
-                                      max_len(dims), kv_scales, flag, hs));
+                                      max_len(dims), kv_scales, kv_format, s.DC / 32, flag,
+                                      hs));
     if (st != MLA_OK) return st;
     st = hip_status(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, hs));
     if (st != MLA_OK) return st;
@@ -254,7 +259,7 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
   st = hip_status(mla::launch_attention(s.shape, ws + L.q_abs, q_rope, kv_pages, page_table,
                                         seq_lens, R, mp, T, dims->num_pages, ws + L.plan, G,
                                         scale_log2, ws + L.part_o, (float*)(ws + L.part_lse),
-                                        kv_scales, ctx(1)));
+                                        kv_scales, kv_format, ctx(1)));
   if (st != MLA_OK) return st;
   if (hidden == 0)
     return hip_status(mla::launch_combine(s.shape, ws + L.part_o,
@@ -311,8 +316,9 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
                               const int32_t* page_table, const int32_t* seq_lens, void* out,
                               float* lse_out, void* workspace, size_t workspace_bytes,
                               void* stream, void* const* stage_events) {
-  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, nullptr, page_table,
-                     seq_lens, out, lse_out, workspace, workspace_bytes, stream, stage_events);
+  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, mla::kKvBf16, nullptr,
+                     page_table, seq_lens, out, lse_out, workspace, workspace_bytes, stream,
+                     stage_events);
 }
 
 mla_status_t mla_decode_fp8(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
@@ -321,8 +327,21 @@ mla_status_t mla_decode_fp8(const mla_dims_t* dims, const void* q_nope, const vo
                             const int32_t* seq_lens, void* out, float* lse_out, void* workspace,
                             size_t workspace_bytes, void* stream, void* const* stage_events) {
   if (!kv_scales) return MLA_ERR_NULL_ARG;
-  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, kv_scales, page_table,
-                     seq_lens, out, lse_out, workspace, workspace_bytes, stream, stage_events);
+  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, mla::kKvFp8, kv_scales,
+                     page_table, seq_lens, out, lse_out, workspace, workspace_bytes, stream,
+                     stage_events);
+}
+
+mla_status_t mla_decode_mxfp4(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                              const void* W_UK, const void* W_UV, const void* kv_pages,
+                              const uint8_t* kv_scales, const int32_t* page_table,
+                              const int32_t* seq_lens, void* out, float* lse_out,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              void* const* stage_events) {
+  if (!kv_scales) return MLA_ERR_NULL_ARG;
+  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, mla::kKvMxfp4, kv_scales,
+                     page_table, seq_lens, out, lse_out, workspace, workspace_bytes, stream,
+                     stage_events);
 }
 
 mla_status_t mla_decode_out(const mla_dims_t* dims, int32_t hidden, const void* q_nope,
@@ -331,8 +350,9 @@ mla_status_t mla_decode_out(const mla_dims_t* dims, int32_t hidden, const void* 
                             const int32_t* seq_lens, void* out_hidden, float* lse_out,
                             void* workspace, size_t workspace_bytes, void* stream) {
   if (hidden < 1) return MLA_ERR_BAD_DIMS;
-  return decode_call(dims, hidden, q_nope, q_rope, W_UK, W_UVO, kv_pages, nullptr, page_table,
-                     seq_lens, out_hidden, lse_out, workspace, workspace_bytes, stream, nullptr);
+  return decode_call(dims, hidden, q_nope, q_rope, W_UK, W_UVO, kv_pages, mla::kKvBf16, nullptr,
+                     page_table, seq_lens, out_hidden, lse_out, workspace, workspace_bytes,
+                     stream, nullptr);
 }
 
 mla_status_t mla_decode(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
@@ -355,8 +375,9 @@ mla_status_t mla_decode_noalloc(const mla_dims_t* dims, const void* q_nope, cons
   void* ws = nullptr;
   const mla_status_t st = scratch_for_current_device(&ws);
   if (st != MLA_OK) return st;
-  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, nullptr, page_table,
-                     seq_lens, out, lse_out, ws, kNoAllocScratchBytes, stream, nullptr);
+  return decode_call(dims, 0, q_nope, q_rope, W_UK, W_UV, kv_pages, mla::kKvBf16, nullptr,
+                     page_table, seq_lens, out, lse_out, ws, kNoAllocScratchBytes, stream,
+                     nullptr);
 }
 
 mla_status_t mla_gather_pages(const mla_dims_t* dims, const void* kv_pages,
@@ -401,11 +422,12 @@ mla_status_t check_append_dims(const mla_append_dims_t* d, int* T_out) {
 
 mla_status_t append_call(const mla_append_dims_t* d, const void* x, const void* W_DKV,
                          const void* W_KR, const int32_t* page_table, const int32_t* seq_lens,
-                         void* kv_pages, float* kv_scales, void* workspace,
+                         void* kv_pages, int kv_format, void* kv_scales, void* workspace,
                          size_t workspace_bytes, void* stream) {
   int T = 1;
   mla_status_t st = check_append_dims(d, &T);
   if (st != MLA_OK) return st;
+  if (kv_format == mla::kKvMxfp4 && d->d_latent % 32 != 0) return MLA_ERR_UNSUPPORTED;
   if (!x || !W_DKV || !W_KR || !page_table || !seq_lens || !kv_pages) return MLA_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(W_DKV) || !aligned16(W_KR) || !aligned16(page_table) ||
       !aligned16(seq_lens) || !aligned16(kv_pages) || (kv_scales && !aligned16(kv_scales)) ||
@@ -438,7 +460,7 @@ mla_status_t append_call(const mla_append_dims_t* d, const void* x, const void* 
   }
   const double base = d->rope_base > 0.f ? (double)d->rope_base : 10000.0;
   return hip_status(mla::launch_append(x, W_DKV, W_KR, page_table, seq_lens, kv_pages, kv_scales,
-                                       workspace, d->batch, T, d->hidden, d->d_latent,
+                                       kv_format, workspace, d->batch, T, d->hidden, d->d_latent,
                                        d->d_rope, d->max_pages_per_seq, d->num_pages, base, hs));
 }
 
@@ -456,8 +478,8 @@ mla_status_t mla_cache_append(const mla_append_dims_t* d, const void* x, const v
                               const void* W_KR, const int32_t* page_table,
                               const int32_t* seq_lens, void* kv_pages, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  return append_call(d, x, W_DKV, W_KR, page_table, seq_lens, kv_pages, nullptr, workspace,
-                     workspace_bytes, stream);
+  return append_call(d, x, W_DKV, W_KR, page_table, seq_lens, kv_pages, mla::kKvBf16, nullptr,
+                     workspace, workspace_bytes, stream);
 }
 
 mla_status_t mla_cache_append_fp8(const mla_append_dims_t* d, const void* x, const void* W_DKV,
@@ -465,8 +487,18 @@ mla_status_t mla_cache_append_fp8(const mla_append_dims_t* d, const void* x, con
                                   const int32_t* seq_lens, void* kv_pages, float* kv_scales,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   if (!kv_scales) return MLA_ERR_NULL_ARG;
-  return append_call(d, x, W_DKV, W_KR, page_table, seq_lens, kv_pages, kv_scales, workspace,
-                     workspace_bytes, stream);
+  return append_call(d, x, W_DKV, W_KR, page_table, seq_lens, kv_pages, mla::kKvFp8, kv_scales,
+                     workspace, workspace_bytes, stream);
+}
+
+mla_status_t mla_cache_append_mxfp4(const mla_append_dims_t* d, const void* x,
+                                    const void* W_DKV, const void* W_KR,
+                                    const int32_t* page_table, const int32_t* seq_lens,
+                                    void* kv_pages, uint8_t* kv_scales, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!kv_scales) return MLA_ERR_NULL_ARG;
+  return append_call(d, x, W_DKV, W_KR, page_table, seq_lens, kv_pages, mla::kKvMxfp4,
+                     kv_scales, workspace, workspace_bytes, stream);
 }
 
 const char* mla_status_str(mla_status_t s) {

@@ -7,7 +7,9 @@
 //   k[j]    = sum_k x[k] W_KR[j][k]                         (W_KR  [d_rope, hidden])
 //   (k[j], k[j + d_rope/2]) rotated by p * base^(-2j/d_rope) (pairs of the two halves)
 // stored at slot p % 64 of page page_table[b][p / 64]: as bf16, or (FP8 cache) c_KV as E4M3
-// codes with a power-of-two scale per token and k_R as bf16.
+// codes with a power-of-two scale per token and k_R as bf16, or (MXFP4 cache, the OCP
+// Microscaling format) c_KV as E2M1 codes with an E8M0 scale per block of 32 elements and k_R
+// as bf16.
 //
 // The product is a skinny GEMM (B*T token rows against d_latent + d_rope weight rows over the
 // model width) bound by reading the weights once. It runs split over the contraction:
@@ -22,7 +24,9 @@
 //     product p * inv_freq would carry an error of up to 2^-8 rad at p near 65536; rotation in
 //     fp32), and the row written. For the FP8 cache the
 //     token's scale is the smallest power of two 2^e with max|c_KV| <= 448 * 2^e (448: the
-//     largest E4M3 value), and each element is c_KV / 2^e rounded to nearest even E4M3.
+//     largest E4M3 value), and each element is c_KV / 2^e rounded to nearest even E4M3. For
+//     the MXFP4 cache each block's scale is 2^X, X = floor(log2 max|c_KV|) - 2 over the block,
+//     and each element is c_KV / 2^X rounded to nearest even E2M1, saturating at 6.
 #include <math.h>
 
 #include <algorithm>
@@ -133,14 +137,15 @@ append_partial_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict
 }
 
 // One work group per token row r (sequence r / T, new token r % T).
-template <bool FP8>
+template <int FMT>
 __global__ void __launch_bounds__(app::FT)
 append_finish_kernel(const float* __restrict__ part, int nslice,
                      const int32_t* __restrict__ page_table,
                      const int32_t* __restrict__ seq_lens, char* __restrict__ kv,
-                     float* __restrict__ kv_scales, int R, int T, int d_c, int d_R,
+                     void* __restrict__ kv_scales, int R, int T, int d_c, int d_R,
                      int max_pages, int num_pages, double log2_base) {
   using namespace app;
+  constexpr bool FP8 = FMT == kKvFp8, MX = FMT == kKvMxfp4;
   __shared__ __attribute__((aligned(16))) float red[4 * FT];  // [group][column]
   __shared__ float wmax[FT / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -219,8 +224,9 @@ append_finish_kernel(const float* __restrict__ part, int nslice,
     const float k1 = colsum(d_c + tid), k2 = colsum(d_c + tid + h);
     const float o1 = k1 * cs - k2 * sn, o2 = k1 * sn + k2 * cs;
     if (write) {
-      uint16_t* kr = FP8 ? reinterpret_cast<uint16_t*>(kv + slot * (d_c + 2 * d_R) + d_c)
-                         : reinterpret_cast<uint16_t*>(kv) + slot * N + d_c;
+      uint16_t* kr = FP8  ? reinterpret_cast<uint16_t*>(kv + slot * (d_c + 2 * d_R) + d_c)
+                     : MX ? reinterpret_cast<uint16_t*>(kv + slot * (d_c / 2 + 2 * d_R) + d_c / 2)
+                          : reinterpret_cast<uint16_t*>(kv) + slot * N + d_c;
       kr[tid] = bf16_bits((__bf16)o1);
       kr[tid + h] = bf16_bits((__bf16)o2);
     }
@@ -230,7 +236,39 @@ append_finish_kernel(const float* __restrict__ part, int nslice,
   const bool mine = c < d_c;
   const float2 vv = colsum2(mine ? c : 0);
   const float v0 = mine ? vv.x : 0.f, v1 = mine ? vv.y : 0.f;
-  if constexpr (!FP8) {
+  if constexpr (MX) {
+    // OCP MX, per block of 32 latent elements (16 consecutive lanes): the shared exponent
+    // X = floor(log2 amax) - 2 (2: the exponent of E2M1's largest value, 6), within -127 .. 127,
+    // 0 for an all-zero block; with amax = m * 2^k (0.5 <= m < 1), floor(log2 amax) = k - 1
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+    int X = 0;
+    if (amax > 0.f) {
+      int k;
+      frexpf(amax, &k);
+      X = k - 3;
+      X = X < -127 ? -127 : (X > 127 ? 127 : X);
+    }
+    const float inv = ldexpf(1.f, -X);  // exact: c_KV / 2^X (X <= 125 for a finite fp32 amax)
+    // E2M1 code of c_KV / 2^X: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even
+    // code (a midpoint goes up exactly when the upper neighbour's mantissa bit is 0), above 6
+    // saturating; the sign in bit 3 unless the magnitude rounds to 0
+    auto code = [inv](float v) -> uint32_t {
+      const float a = fabsf(v) * inv;
+      const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                         (uint32_t)(a > 5.f);
+      return m | (v < 0.f && m != 0u ? 8u : 0u);
+    };
+    if (write && mine) {
+      unsigned char* row = reinterpret_cast<unsigned char*>(kv + slot * (d_c / 2 + 2 * d_R));
+      row[tid] = (unsigned char)(code(v0) | (code(v1) << 4));  // columns 2 tid, 2 tid + 1
+      if ((c & 31) == 0)
+        reinterpret_cast<unsigned char*>(kv_scales)[slot * (d_c / 32) + c / 32] =
+            (unsigned char)(X + 127);
+    }
+  } else if constexpr (!FP8) {
     if (write && mine)
       *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(kv) + slot * N + c) =
           pack_bf16x2(v0, v1);
@@ -261,7 +299,7 @@ append_finish_kernel(const float* __restrict__ part, int nslice,
         const int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0 * inv, v1 * inv, 0, false);
         *reinterpret_cast<uint16_t*>(row + c) = (uint16_t)(w & 0xFFFF);
       }
-      if (tid == 0) kv_scales[slot] = ldexpf(1.f, e);
+      if (tid == 0) reinterpret_cast<float*>(kv_scales)[slot] = ldexpf(1.f, e);
     }
   }
 }
@@ -292,9 +330,9 @@ size_t append_workspace_bytes(int R, int hidden, int d_c, int d_R) {
 
 hipError_t launch_append(const void* x, const void* W_DKV, const void* W_KR,
                          const int32_t* page_table, const int32_t* seq_lens, void* kv,
-                         float* kv_scales, void* workspace, int B, int T, int hidden, int d_c,
-                         int d_R, int max_pages, int num_pages, double rope_base,
-                         hipStream_t stream) {
+                         void* kv_scales, int kv_format, void* workspace, int B, int T,
+                         int hidden, int d_c, int d_R, int max_pages, int num_pages,
+                         double rope_base, hipStream_t stream) {
   const int R = B * T;
   const int S = append_slices(R, hidden, d_c, d_R);
   const int N = d_c + d_R;
@@ -316,7 +354,9 @@ hipError_t launch_append(const void* x, const void* W_DKV, const void* W_KR,
                          page_table, seq_lens, (char*)kv, kv_scales, R, T, d_c, d_R, max_pages,
                          num_pages, log2(rope_base));
   };
-  return kv_scales ? fin(append_finish_kernel<true>) : fin(append_finish_kernel<false>);
+  if (kv_format == kKvFp8) return fin(append_finish_kernel<kKvFp8>);
+  if (kv_format == kKvMxfp4) return fin(append_finish_kernel<kKvMxfp4>);
+  return fin(append_finish_kernel<kKvBf16>);
 }
 
 }  // namespace mla

@@ -737,7 +737,37 @@ constexpr float kRescale = 64.f;  // log2 headroom before the running max must m
 constexpr int ROWB8 = DC + 2 * DR;
 using Tile8 = PagedTile<TT, ROWB8>;
 constexpr int SB8 = Tile8::BYTES + 4 * TT;  // bytes of one loaded FP8 tile with its scales
+// MXFP4 cache: a token row is [c_KV as E2M1 codes, two per byte, element 2k in the low nibble
+// (32 bytes) | k_R bf16 (16 bytes)], 48 bytes, and each token has DC/32 = 2 E8M0 scale bytes
+// (one per block of 32 latent elements) in a separate array of the same page geometry. A loaded
+// tile is its 3 KiB of rows followed by its 128 scale bytes (in a 256-byte slot: the load moves
+// 4 bytes a lane). The score operand (8 elements of one block of a token row) is converted with
+// that block's scale. The value operand cannot carry the scale in the weight, as FP8 does: the
+// scale changes along the latent dimension. So each tile's latent part is converted once, one
+// token row per lane, into a bf16 copy in the wave's own LDS buffer, laid out as the bf16 tile,
+// and the values are read from it as in the bf16 path.
+constexpr int MXB = DC / 32;
+constexpr int ROWB4 = DC / 2 + 2 * DR;
+using Tile4 = PagedTile<TT, ROWB4>;
+constexpr int SB4 = Tile4::BYTES + 256;  // bytes of one loaded MXFP4 tile with its scales
 }  // namespace m2
+
+// E8M0 scale byte -> the fp32 scale operand of the gfx950 scaled conversions: the byte as the
+// exponent field (code 0 gives fp32 bits 0, which the conversions take as 2^-127, as E8M0 does;
+// checked on the device)
+__device__ __forceinline__ float e8m0_scale(uint32_t code) {
+  return __builtin_bit_cast(float, code << 23);
+}
+
+// 8 E2M1 elements (the 4 bytes of w, element 2k in the low nibble of byte k) -> bf16, times sc
+__device__ __forceinline__ bf16x8 cvt_fp4x8(uint32_t w, float sc) {
+  const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+  const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+  const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+  const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+  return cat4(__builtin_shufflevector(a0, a1, 0, 1, 2, 3),
+              __builtin_shufflevector(a2, a3, 0, 1, 2, 3));
+}
 
 // Waits until at most `after` (0..4) tiles of N load instructions each are still in flight.
 template <int N>
@@ -749,7 +779,7 @@ __device__ __forceinline__ void wait_tiles_upto4(int after) {
   else wait_vmcnt<0>();
 }
 
-template <bool FP8, int NB>
+template <int FMT, int NB>
 __global__ void __launch_bounds__(256)
 attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
                     const char* __restrict__ kv, const int32_t* __restrict__ page_table,
@@ -757,13 +787,18 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
                     int num_pages,
                     const Plan* __restrict__ plan, int G, float scale_log2,
                     uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-                    const float* __restrict__ kv_scales) {
+                    const void* __restrict__ kv_scales) {
   using namespace m2;
-  using TileL = typename std::conditional<FP8, Tile8, Tile>::type;  // the format as loaded
-  constexpr int LB = FP8 ? SB8 : Tile::BYTES;             // bytes of one ring entry
-  constexpr int IPW = TileL::INSTR + (FP8 ? 1 : 0);       // load instructions per tile
-  constexpr int WAVE_LDS = NB * LB;
+  constexpr bool FP8 = FMT == kKvFp8, MX = FMT == kKvMxfp4;
+  using TileL = typename std::conditional<FP8, Tile8,
+                typename std::conditional<MX, Tile4, Tile>::type>::type;  // the format as loaded
+  constexpr int LB = FP8 ? SB8 : (MX ? SB4 : Tile::BYTES);  // bytes of one ring entry
+  constexpr int IPW = TileL::INSTR + (FP8 || MX ? 1 : 0);   // load instructions per tile
+  // MXFP4: the ring, then the bf16 copy of the current tile's latent part
+  constexpr int WAVE_LDS = NB * LB + (MX ? Tile::BYTES : 0);
   __shared__ __attribute__((aligned(1024))) char lds_tiles[kAttnWavesMha2Mla][WAVE_LDS];
+  const float* sc8 = reinterpret_cast<const float*>(kv_scales);
+  const unsigned char* sc4 = reinterpret_cast<const unsigned char*>(kv_scales);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -799,8 +834,11 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
     MLA_LDS char* dst = tiles + buf * LB;
     TileL::template issue<1>(TileL::base_of(kv, page, c.j, num_pages), valid, dmo, dst, 0, lane);
     if constexpr (FP8)  // the tile's scales (slots past the end repeat the last valid one)
-      load_lds_4(kv_scales + (size_t)page * kPage + (c.j % Tile8::TPP) * TT,
+      load_lds_4(sc8 + (size_t)page * kPage + (c.j % Tile8::TPP) * TT,
                  4u * (uint32_t)min(lane, valid - 1), dst + Tile8::BYTES);
+    if constexpr (MX)  // the page's 128 scale bytes, 4 a lane (lanes 32.. repeat the last 4)
+      load_lds_4(sc4 + (size_t)page * kPage * MXB, 4u * (uint32_t)min(lane, TT * MXB / 4 - 1),
+                 dst + Tile4::BYTES);
   };
   // FP8 -> bf16, 8 values from two words (bytes 0..7 in order), times 2^(exponent of sc)
   auto cvt8 = [](uint32_t w0, uint32_t w1, float sc) {
@@ -852,6 +890,9 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
     }
     const MLA_LDS char* kb = tiles + (it % NB) * LB;
     const MLA_LDS float* ksc = reinterpret_cast<const MLA_LDS float*>(kb + Tile8::BYTES);
+    const MLA_LDS unsigned char* ksc4 =
+        reinterpret_cast<const MLA_LDS unsigned char*>(kb + Tile4::BYTES);
+    const int valid = min(TT, cc.S - cc.j * TT);
 
     // ---- scores for tokens [32*mb2, 32*mb2 + 32)
     f32x16 s[2];
@@ -869,6 +910,16 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
           a = mfma_32x32x16(cvt8(w[0], w[1], sc), qf[st], a);
         }
         kr = *reinterpret_cast<const MLA_LDS i16x4*>(rp + DC + 8 * hi);
+      } else if constexpr (MX) {  // elements 16st + 8hi .. +8 of token row `row`: block st / 2
+        const MLA_LDS char* rp = kb + row * ROWB4;
+        const float s0 = e8m0_scale(ksc4[MXB * row]), s1 = e8m0_scale(ksc4[MXB * row + 1]);
+        static_assert(MXB == 2, "two latent blocks per token row");
+#pragma unroll
+        for (int st = 0; st < DC / 16; ++st) {
+          const uint32_t w = *reinterpret_cast<const MLA_LDS uint32_t*>(rp + 8 * st + 4 * hi);
+          a = mfma_32x32x16(cvt_fp4x8(w, st < 2 ? s0 : s1), qf[st], a);
+        }
+        kr = *reinterpret_cast<const MLA_LDS i16x4*>(rp + DC / 2 + 8 * hi);
       } else {
 #pragma unroll
         for (int st = 0; st < DC / 16; ++st)
@@ -880,7 +931,6 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
     // ---- online softmax, lane = head t32 x 32 tokens
     // raw logits stay unscaled: the scale enters once in the tile maximum and as one FMA in
     // each exponent
-    const int valid = min(TT, cc.S - cc.j * TT);
     float mt = -INFINITY;
     if (valid == TT) {  // a full tile (all but a sequence's last): no tail mask
 #pragma unroll
@@ -939,6 +989,21 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
                       // rounding noise of relative size 2^-9 / sqrt(tokens)
         }
     l_lane = l_lane * alpha + lsum;
+    // MXFP4: this tile's latent part as bf16, token row `lane` per lane, into the wave's
+    // buffer (rows past the end were loaded as copies of the last valid row; their scales
+    // are taken from that row too, so that no slot outside the sequence is read)
+    MLA_LDS char* vbuf = tiles + NB * LB;
+    if constexpr (MX) {
+      const int t = lane, ts = t < valid ? t : valid - 1;
+      const float s0 = e8m0_scale(ksc4[MXB * ts]), s1 = e8m0_scale(ksc4[MXB * ts + 1]);
+      const u32x4 w0 = *reinterpret_cast<const MLA_LDS u32x4*>(kb + t * ROWB4);
+      const u32x4 w1 = *reinterpret_cast<const MLA_LDS u32x4*>(kb + t * ROWB4 + 16);
+#pragma unroll
+      for (int ch = 0; ch < DC / 8; ++ch)  // chunk ch: elements 8ch .. 8ch + 7, block ch / 4
+        *reinterpret_cast<MLA_LDS bf16x8*>(vbuf + Tile::lds_off(t, ch)) =
+            cvt_fp4x8(ch < 4 ? w0[ch] : w1[ch - 4], ch < 4 ? s0 : s1);
+    }
+    const MLA_LDS char* vb = MX ? vbuf : kb;  // where the bf16 values are read
     // ---- values: block kk holds, for lane half hi, the tokens
     //      32*mb2 + 16*half + 8*(j/4) + 4*hi + j%4  (j < 8), the order of the score layout
 #pragma unroll
@@ -964,7 +1029,7 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
         for (int p = 0; p < 2; ++p) {
           const int t = 32 * mb2 + 16 * half + 8 * p + 4 * (G16 >> 1) + (q16 >> 2);
           const int c0 = 32 * nb + 16 * (G16 & 1) + 4 * (q16 & 3);
-          v2[p] = lds_read_tr16(kb, Tile::lds_off(t, c0 >> 3) + (c0 & 7) * 2);
+          v2[p] = lds_read_tr16(vb, Tile::lds_off(t, c0 >> 3) + (c0 & 7) * 2);
         }
         acc[nb] = mfma_32x32x16(pa[kk], cat4(v2[0], v2[1]), acc[nb]);
       }
@@ -994,7 +1059,7 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
                             const int32_t* page_table, const int32_t* seq_lens, int B,
                             int max_pages, int q_len, int num_pages, const void* plan, int G,
                             float scale_log2, void* part_o, float* part_lse,
-                            const float* kv_scales, const Launch& L) {
+                            const void* kv_scales, int kv_format, const Launch& L) {
   if (shape == kShapeDeepSeek) {
     // two head halves per tile stream, paired 8 ids apart; ids padded to whole groups of 16
     const int blocks = 16 * ((G + 7) / 8);
@@ -1002,9 +1067,10 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
       return launch_kernel(kernel, dim3(blocks), dim3(64 * ds::NW), L, (const uint16_t*)q_abs,
                            (const uint16_t*)q_rope, (const char*)kv, page_table, seq_lens, B,
                            max_pages, q_len, num_pages, (const Plan*)plan, G, scale_log2,
-                           (uint16_t*)part_o, part_lse, kv_scales);
+                           (uint16_t*)part_o, part_lse, (const float*)kv_scales);
     };
-    return kv_scales ? go(attn_deepseek_kernel<true>) : go(attn_deepseek_kernel<false>);
+    if (kv_format == kKvMxfp4) return hipErrorInvalidValue;  // not built at these widths
+    return kv_format == kKvFp8 ? go(attn_deepseek_kernel<true>) : go(attn_deepseek_kernel<false>);
   }
   const int blocks = (G + kAttnWavesMha2Mla - 1) / kAttnWavesMha2Mla;
   auto go = [&](auto kernel) {
@@ -1015,9 +1081,11 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
                          kv_scales);
   };
   // FP8: a three-deep ring of 5.25 KiB tiles (16 KiB a wave) lets two work groups share a
-  // CU, two waves a SIMD
-  if (kv_scales) return go(attn_mha2mla_kernel<true, kRingFp8>);
-  return go(attn_mha2mla_kernel<false, m2::NBUF>);
+  // CU, two waves a SIMD; MXFP4: a three-deep ring of 3.25 KiB tiles and the 9 KiB bf16 copy
+  // (18.75 KiB a wave), also two work groups a CU
+  if (kv_format == kKvFp8) return go(attn_mha2mla_kernel<kKvFp8, kRingFp8>);
+  if (kv_format == kKvMxfp4) return go(attn_mha2mla_kernel<kKvMxfp4, kRingFp8>);
+  return go(attn_mha2mla_kernel<kKvBf16, m2::NBUF>);
 }
 
 }  // namespace mla

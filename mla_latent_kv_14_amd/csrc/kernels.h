@@ -34,8 +34,13 @@ enum Shape : int {
 // plan unit is served by two work groups, one per half of the heads.)
 constexpr int kAttnWavesMha2Mla = 4;
 // FP8 cache (MHA2MLA widths): ring depth of the attention kernel, and its work groups per CU
+// (the same for the MXFP4 cache)
 constexpr int kRingFp8 = 3;
 constexpr int kGroupsPerCuFp8 = 2;
+
+// Latent-cache formats: bf16 rows; FP8 E4M3 c_KV with an fp32 power-of-two scale per token;
+// MXFP4 c_KV (E2M1 codes, two per byte) with an E8M0 scale byte per token and 32-element block.
+enum KvFormat : int { kKvBf16 = 0, kKvFp8 = 1, kKvMxfp4 = 2 };
 
 // B counts virtual sequences (sequences x query tokens, q_len per sequence) in the three
 // decode launches; seq_lens and page_table stay per sequence.
@@ -47,7 +52,7 @@ hipError_t launch_attention(int shape, const void* q_abs, const void* q_rope, co
                             const int32_t* page_table, const int32_t* seq_lens, int B,
                             int max_pages, int q_len, int num_pages, const void* plan, int G,
                             float scale_log2, void* part_o, float* part_lse,
-                            const float* kv_scales, const Launch& L);
+                            const void* kv_scales, int kv_format, const Launch& L);
 
 // The decompressed branch for T query tokens per sequence at or above the prefill threshold:
 // W_UV transposed into W_UVt [H][d_v][d_c], then per group of `group` sequences the
@@ -73,21 +78,25 @@ hipError_t launch_combine_latent(int shape, const void* part_o, const float* par
 hipError_t launch_linear(const void* x, const void* W, void* out, int R, int K, int N,
                          const Launch& L);
 
-// Sets bits of *flag (cleared first) for out-of-range lengths (1), used page ids (2) or, with
-// an FP8 cache (kv_scales not NULL), used scales that are not positive normal powers of two (4).
+// Sets bits of *flag (cleared first) for out-of-range lengths (1), used page ids (2) or used
+// scales outside the format's contract (4): with an FP8 cache a scale that is not a positive
+// normal power of two, with an MXFP4 cache a scale byte of 255 (E8M0's NaN); mx_blocks is
+// d_latent / 32.
 hipError_t launch_check(const int32_t* seq_lens, const int32_t* page_table, int B, int max_pages,
-                        int num_pages, int max_len, const float* kv_scales, int* flag,
-                        hipStream_t stream);
+                        int num_pages, int max_len, const void* kv_scales, int kv_format,
+                        int mx_blocks, int* flag, hipStream_t stream);
 
 // Writes [c_KV | RoPE(k_R)] of B*T new tokens (token i of sequence b at position
-// seq_lens[b] + i): bf16 rows, or with kv_scales an FP8 cache (E4M3 c_KV, bf16 k_R, a
-// power-of-two scale per token). Needs d_c even and at most 1024, d_R even and at most 512,
-// hidden % 256 == 0, and a workspace of append_workspace_bytes.
+// seq_lens[b] + i) in the cache format kv_format: bf16 rows; an FP8 cache (E4M3 c_KV, bf16
+// k_R, an fp32 power-of-two scale per token); or an MXFP4 cache (E2M1 c_KV two per byte, bf16
+// k_R, an E8M0 scale byte per token and block of 32, d_c a multiple of 32). Needs d_c even and
+// at most 1024, d_R even and at most 512, hidden % 256 == 0, and a workspace of
+// append_workspace_bytes.
 hipError_t launch_append(const void* x, const void* W_DKV, const void* W_KR,
                          const int32_t* page_table, const int32_t* seq_lens, void* kv,
-                         float* kv_scales, void* workspace, int B, int T, int hidden, int d_c,
-                         int d_R, int max_pages, int num_pages, double rope_base,
-                         hipStream_t stream);
+                         void* kv_scales, int kv_format, void* workspace, int B, int T,
+                         int hidden, int d_c, int d_R, int max_pages, int num_pages,
+                         double rope_base, hipStream_t stream);
 // Workspace of launch_append: fp32 partial rows of the split contraction.
 size_t append_workspace_bytes(int R, int hidden, int d_c, int d_R);
 

@@ -8,8 +8,9 @@ import pytest
 import mla_latent_kv_14_amd as M
 from mla_latent_kv_14_amd.binding import STATUS_CODE
 
-EXPECTED = ["mla_cache_append", "mla_cache_append_fp8", "mla_cache_append_workspace_bytes",
-            "mla_decode", "mla_decode_fp8", "mla_decode_noalloc",
+EXPECTED = ["mla_cache_append", "mla_cache_append_fp8", "mla_cache_append_mxfp4",
+            "mla_cache_append_workspace_bytes",
+            "mla_decode", "mla_decode_fp8", "mla_decode_mxfp4", "mla_decode_noalloc",
             "mla_decode_out", "mla_decode_timed",
             "mla_decode_workspace_bytes", "mla_gather_pages", "mla_last_hip_error",
             "mla_status_str"]
@@ -331,6 +332,43 @@ def test_decode_fp8_rejects_before_enqueueing():
     bad = m2_dims()
     bad.batch = 0
     assert call(bad, _al(6)) == STATUS_CODE["MLA_ERR_BAD_DIMS"]
+
+
+def test_decode_mxfp4_rejects_before_enqueueing():
+    L = M.lib()
+    ptrs = [_al(k + 1) for k in range(5)]           # q_nope, q_rope, W_UK, W_UV, kv_pages
+    rest = [_al(7), _al(8), _al(9), ctypes.c_void_p(0)]  # page_table, seq_lens, out, lse
+    def call(d, scales):
+        return L.mla_decode_mxfp4(ctypes.byref(d), *ptrs, scales, *rest, _al(10),
+                                  M.workspace_bytes(d), ctypes.c_void_p(0), None)
+    assert call(m2_dims(), ctypes.c_void_p(0)) == STATUS_CODE["MLA_ERR_NULL_ARG"]
+    assert call(m2_dims(), ctypes.c_void_p(_al(6).value + 4)) == STATUS_CODE["MLA_ERR_MISALIGNED"]
+    # the MXFP4 cache is read at the MHA2MLA widths only
+    assert call(ds_dims(), _al(6)) == STATUS_CODE["MLA_ERR_UNSUPPORTED"]
+    # the decompressed branch reads a bf16 cache
+    d = m2_dims(B=2, max_pages=16, num_pages=64, max_seq_len=1024)
+    d.q_len, d.prefill_threshold = 300, 256
+    assert call(d, _al(6)) == STATUS_CODE["MLA_ERR_UNSUPPORTED"]
+    bad = m2_dims()
+    bad.batch = 0
+    assert call(bad, _al(6)) == STATUS_CODE["MLA_ERR_BAD_DIMS"]
+    # the workspace is the one mla_decode_workspace_bytes gives (as for FP8)
+    d = m2_dims()
+    assert L.mla_decode_mxfp4(ctypes.byref(d), *ptrs, _al(6), *rest, _al(10),
+                              M.workspace_bytes(d) - 1, ctypes.c_void_p(0), None) == \
+        STATUS_CODE["MLA_ERR_WORKSPACE"]
+
+
+def test_append_mxfp4_rejects_before_enqueueing():
+    L = M.lib()
+    p = [_al(k + 1) for k in range(6)]
+    assert L.mla_cache_append_mxfp4(ctypes.byref(_append_dims()), *p, None, _al(7), 1 << 30,
+                                    None) == STATUS_CODE["MLA_ERR_NULL_ARG"]
+    assert L.mla_cache_append_mxfp4(ctypes.byref(_append_dims()), *p, ctypes.c_void_p(0x100004),
+                                    _al(7), 1 << 30, None) == STATUS_CODE["MLA_ERR_MISALIGNED"]
+    # whole blocks of 32 latent elements only
+    assert L.mla_cache_append_mxfp4(ctypes.byref(_append_dims(d_c=500)), *p, _al(8), _al(7),
+                                    1 << 30, None) == STATUS_CODE["MLA_ERR_UNSUPPORTED"]
 
 
 def _small_decode_args(B=2, T=None, H=32, d_n=120, d_c=64, d_R=8, d_v=128, P=4, mp=2):

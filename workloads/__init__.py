@@ -141,10 +141,12 @@ def _used_slots(inp, P, ps):
     return used
 
 
-def mxfp4_cache(inp, seed=0, scale_codes=(122, 127), poison=False):
+def mxfp4_cache(inp, seed=0, scale_codes=(124, 126), poison=False):
     """A synthetic MXFP4 cache with the page geometry and k_R of ``inp``: every c_KV element a
     uniformly drawn 4-bit E2M1 code, every block of 32 elements a scale byte (E8M0, 2^(code-127))
-    drawn uniformly from [scale_codes[0], scale_codes[1]] (seeded). Returns (kv4 uint8
+    drawn uniformly from [scale_codes[0], scale_codes[1]] (seeded). The default scales, 2^-3 to
+    2^-1, give c_KV elements of rms about 0.97 (at most 3), the size of the bf16 inputs' N(0, 1)
+    latent. Returns (kv4 uint8
     [P, 64, d_c/2 + 2*d_R] with rows [c_KV codes, two per byte, element 2k in the low nibble |
     k_R bf16 bytes], scales uint8 [P, 64, d_c/32]). With poison=True every slot that is not
     part of a sequence holds 0xFF bytes and NaN scales (255)."""
