@@ -280,3 +280,92 @@ def test_fp8_append_then_decode(M):
     kv_ref = oracle.dequant_fp8_cache(kv8_ref, sc_ref, d_c)
     _decode_vs_oracle(M, inp, kv8, inp["seq_lens"], kv_ref, "fp8 append then decode",
                       kv_scales=sc)
+
+
+# ---- MXFP4 cache (OCP MX: E2M1 codes, an E8M0 scale per token and block of 32 elements)
+
+@pytest.mark.parametrize("shape,lens,T", [("mha2mla", [1, 63, 64, 1000], 3),
+                                          ("deepseek", [62, 64, 500], 2),
+                                          ("wide", [5, 70, 130], 2)])
+def test_mxfp4_append_matches_oracle(M, shape, lens, T):
+    # Per block of 32 latent elements the scale byte is X + 127, X = floor(log2 max|c_KV|) - 2,
+    # and each code is c_KV / 2^X rounded to the nearest even E2M1 value (saturating at 6). The
+    # kernel decides from fp32 sums and the oracle from fp64 ones, so a scale may differ where a
+    # block's maximum sits at a power of two, and a code where a value sits within summation
+    # noise of a rounding midpoint; everything else must agree exactly, and every other byte of
+    # the pool and its scales stays as it was.
+    inp, x, Wd, Wr, before = _case(shape, lens, T, 46)
+    c = SHAPES[shape]
+    d_c, d_R, nb = c["d_c"], c["d_R"], c["d_c"] // 32
+    kv4_0, sc0 = W.mxfp4_cache(inp, seed=7)
+    kv4, sc = kv4_0.clone().cuda(), sc0.clone().cuda()
+    say("mxfp4 append", shape, "B=%d T=%d" % (len(lens), T))
+    M.cache_append(x.cuda(), Wd.cuda(), Wr.cuda(), kv4, inp["page_table"].cuda(), before.cuda(),
+                   kv_scales=sc)
+    torch.cuda.synchronize()
+    got4, gotsc = kv4.cpu().numpy(), sc.cpu().numpy()
+    codes, scales, kr, where = oracle.cache_append_mxfp4(
+        W.u16(x), W.u16(Wd), W.u16(Wr), inp["page_table"].numpy(), before.numpy())
+    rows, _ = oracle.cache_append(W.u16(x), W.u16(Wd), W.u16(Wr), inp["page_table"].numpy(),
+                                  before.numpy())
+    written = np.zeros(got4.shape[:2], dtype=bool)
+    n_codes = n_diff = n_edge = 0
+    for b in range(len(lens)):
+        for i in range(T):
+            page, slot = where[b, i]
+            written[page, slot] = True
+            g_codes = oracle.unpack_fp4(got4[page, slot, :d_c // 2]).astype(np.int64)
+            for k in range(nb):
+                blk = rows[b, i, 32 * k:32 * k + 32]
+                sg, sr = int(gotsc[page, slot, k]), int(scales[b, i, k])
+                if sg != sr:  # only at a power-of-two edge of the block's maximum
+                    amax = np.max(np.abs(blk))
+                    ratio = amax / 2.0 ** (max(sg, sr) - 127 + 2)
+                    assert abs(ratio - 1) < 1e-5, (b, i, k, sg, sr, amax)
+                    n_edge += 1
+                    continue
+                g = g_codes[32 * k:32 * k + 32]
+                r = codes[b, i, 32 * k:32 * k + 32].astype(np.int64)
+                diff = g != r
+                n_codes += g.size
+                n_diff += int(diff.sum())
+                # a differing code is the other neighbour of a value at a rounding midpoint
+                s = 2.0 ** (sg - 127)
+                a = np.minimum(np.abs(blk[diff]) / s, 6.0)
+                vg = np.abs(oracle.fp4_e2m1_value(g[diff]))
+                vr = np.abs(oracle.fp4_e2m1_value(r[diff]))
+                assert np.all(np.abs(np.abs(vg - a) - np.abs(vr - a)) <= 1e-5 * (1 + a)), (b, i, k)
+            # k_R: bf16 within half an ulp of the fp64 rotation
+            krg = got4[page, slot, d_c // 2:].view(np.uint16).astype(np.uint32) << 16
+            krg = krg.view(np.float32).astype(np.float64)
+            assert np.all(np.abs(krg - kr[b, i]) <= 2.0 ** -8 * np.abs(kr[b, i]) + 1e-5), (b, i)
+    say("  codes compared %d, differing %d, scales at an edge %d" % (n_codes, n_diff, n_edge))
+    assert n_diff <= max(2, n_codes // 200), (n_diff, n_codes)
+    assert np.array_equal(got4[~written], kv4_0.numpy()[~written])
+    assert np.array_equal(gotsc[~written], sc0.numpy()[~written])
+
+
+def test_mxfp4_append_then_decode(M):
+    # tokens appended into an MXFP4 cache are read back by mla_decode_mxfp4 (MHA2MLA widths);
+    # the oracle decodes its own MXFP4 cache (the initial pool with its append written in)
+    lens, T = [70, 300, 5], 2
+    inp, x, Wd, Wr, before = _case("mha2mla", lens, T, 47)
+    kv4_0, sc0 = W.mxfp4_cache(inp, seed=8)
+    kv4, sc = kv4_0.clone().cuda(), sc0.clone().cuda()
+    M.cache_append(x.cuda(), Wd.cuda(), Wr.cuda(), kv4, inp["page_table"].cuda(), before.cuda(),
+                   kv_scales=sc)
+    say("mxfp4 append then decode")
+    codes, scales, kr, where = oracle.cache_append_mxfp4(
+        W.u16(x), W.u16(Wd), W.u16(Wr), inp["page_table"].numpy(), before.numpy())
+    d_c = inp["d_c"]
+    kv4_ref, sc_ref = kv4_0.numpy().copy(), sc0.numpy().copy()
+    krb = to_bf16_bits(kr)
+    for b in range(len(lens)):
+        for i in range(T):
+            page, slot = where[b, i]
+            kv4_ref[page, slot, :d_c // 2] = oracle.pack_fp4(codes[b, i])
+            kv4_ref[page, slot, d_c // 2:] = krb[b, i].view(np.uint8)
+            sc_ref[page, slot] = scales[b, i]
+    kv_ref = oracle.dequant_mxfp4_cache(kv4_ref, sc_ref, d_c)
+    _decode_vs_oracle(M, inp, kv4, inp["seq_lens"], kv_ref, "mxfp4 append then decode",
+                      kv_scales=sc)
