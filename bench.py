@@ -24,7 +24,8 @@ decompression it avoids excluded):
   Bytes = sumS (d_c + d_R) 2 + 2 H d_c (d_n + d_v) + 2 B H (d_n + d_R) + 2 B H d_v
           + 4 (B max_pages + B)
 Attention kernel alone (the roofline object): the cache bytes, sumS (d_c + d_R) 2 (1152 B per
-token; 644 B over the FP8 cache), the per-token figure times the tokens. The absorbed queries
+token; 644 B over the FP8 cache; at the MHA2MLA widths 144, 84 over FP8 and 50 over MXFP4), the
+per-token figure times the tokens. The absorbed queries
 it reads (an intermediate the method makes, not an input) are not counted. With several query
 tokens the attention kernel's FLOPs per cache byte pass the MFMA ridge (about 315 FLOP/B, from
 T = 2 on at the DeepSeek widths), and it is priced on MFMA. On the decompressed branch (from
@@ -175,16 +176,23 @@ def run(args):
             inp["q_rope"] = torch.randn(B, T, H, inp["d_R"], generator=g).to(torch.bfloat16)
         return inp
 
-    def with_fp8(inp, seed):  # the FP8 copy of the cache, with per-token scales
+    def with_fp8(inp, seed):  # a quantised cache: the FP8 copy, or a synthetic MXFP4 one
         if args.kv_fp8:
             kv8, sc = W.fp8_cache(inp, seed=seed)
             inp["kv_pages"], inp["kv_scales"] = kv8, sc
+        elif args.kv_mxfp4:
+            kv4, sc = W.mxfp4_cache(inp, seed=seed)
+            inp["kv_pages"], inp["kv_scales"] = kv4, sc
         return inp
 
     fp8_row = cfg["d_c"] + 2 * cfg["d_R"] + 4  # FP8 c_KV + bf16 k_R + fp32 scale
+    mx_row = cfg["d_c"] // 2 + 2 * cfg["d_R"] + cfg["d_c"] // 32  # E2M1 + bf16 k_R + E8M0
+    if args.kv_mxfp4 and cfg["H"] == 128:
+        raise SystemExit("--kv-mxfp4: the MXFP4 cache is read at the MHA2MLA widths "
+                         "(--workload 5)")
     base = with_fp8(with_tokens(W.config_inputs(args.workload), cfg["seed"] + 500),
                     cfg["seed"] + 700)
-    alg = algorithmic(base, T, fp8_row if args.kv_fp8 else None)
+    alg = algorithmic(base, T, fp8_row if args.kv_fp8 else (mx_row if args.kv_mxfp4 else None))
     n_sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / alg["bytes"]))
     sets = []
     for i in range(n_sets):
@@ -203,7 +211,7 @@ def run(args):
     vp = ctypes.c_void_p
 
     names = ("q_nope", "q_rope", "W_UK", "W_UV", "kv_pages") + \
-        (("kv_scales",) if args.kv_fp8 else ()) + ("page_table", "seq_lens")
+        (("kv_scales",) if args.kv_fp8 or args.kv_mxfp4 else ()) + ("page_table", "seq_lens")
 
     def argv(i):
         d = sets[i]
@@ -218,7 +226,8 @@ def run(args):
     ev_arr = [(vp * 6)(*e) for e in ev]
     nullev = ctypes.POINTER(vp)()
 
-    entry = lib.mla_decode_fp8 if args.kv_fp8 else lib.mla_decode_timed
+    entry = (lib.mla_decode_fp8 if args.kv_fp8 else
+             lib.mla_decode_mxfp4 if args.kv_mxfp4 else lib.mla_decode_timed)
 
     def step(i, events=nullev):
         rc = entry(dref, *call_args[i % n_sets], events)
@@ -249,7 +258,8 @@ def run(args):
     attn_s = stage_ms[1] * 1e-3
     decompressed = T >= (args.prefill_threshold or (256 if cfg["H"] == 128 else 1 << 30))
     # the counter records were taken on the one-token decode's attention kernel
-    record = cfg["name"] + ("_fp8" if args.kv_fp8 else "") if T == 1 else None
+    record = cfg["name"] + ("_fp8" if args.kv_fp8 else "_mxfp4" if args.kv_mxfp4 else "") \
+        if T == 1 else None
     traffic = measured_traffic(record) if record else None
     if decompressed:
         # the middle stage brackets the whole branch: W_UV transpose, then per group of
@@ -290,7 +300,10 @@ def run(args):
                    "query_tokens_per_seq": T,
                    "branch": "decompressed" if decompressed else "absorbed",
                    "kv_cache": ("fp8_e4m3 c_KV + bf16 k_R + fp32 scale per token, %d B"
-                                % fp8_row) if args.kv_fp8 else "bf16"},
+                                % fp8_row) if args.kv_fp8 else
+                               ("mxfp4 (E2M1) c_KV + bf16 k_R + E8M0 scale per 32 elements, "
+                                "%d B per token, synthetic codes" % mx_row)
+                               if args.kv_mxfp4 else "bf16"},
         "tflops": round(alg["flops"] / sec / 1e12, 2),
         "gbps": round(alg["bytes"] / sec / 1e9, 1),
         "roofline_frac_call": round(call_frac, 4),
@@ -307,7 +320,7 @@ def run(args):
     util = measured_mfma_util(record) if record else None
     if util is not None:
         res["roofline"]["mfma_util"] = util
-    if not args.no_cpu and T == 1 and not args.kv_fp8:
+    if not args.no_cpu and T == 1 and not args.kv_fp8 and not args.kv_mxfp4:
         res["cpu_baseline"] = cpu_baseline(base, alg, gpu_out=outs[0].float().cpu().numpy())
     else:
         res["cpu_baseline"] = None
@@ -341,8 +354,9 @@ def run_out(args):
     d0 = sets[0]
     dims = M.make_dims(d0["q_nope"], d0["q_rope"], d0["W_UK"], d0["W_UV"], d0["kv_pages"],
                        d0["page_table"])
-    if args.kv_fp8:
-        raise SystemExit("--kv-fp8 does not apply to --out-proj (its decode reads a bf16 cache)")
+    if args.kv_fp8 or args.kv_mxfp4:
+        raise SystemExit("--kv-fp8 and --kv-mxfp4 do not apply to --out-proj (its decode reads "
+                         "a bf16 cache)")
     ws_bytes = M.workspace_bytes(dims)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     outs = [torch.empty((d["B"], hidden), dtype=torch.bfloat16, device=dev) for d in sets]
@@ -398,6 +412,9 @@ def run_append(args):
     if args.kv_fp8:  # append into an FP8 copy of the cache
         kv8, sc8 = W.fp8_cache(inp, seed=cfg["seed"] + 8)
         kv, sc = kv8.to(dev), sc8.to(dev)
+    elif args.kv_mxfp4:  # append into an MXFP4 cache of the workload's geometry
+        kv4, sc4 = W.mxfp4_cache(inp, seed=cfg["seed"] + 8)
+        kv, sc = kv4.to(dev), sc4.to(dev)
     else:
         kv = inp["kv_pages"].to(dev)
     pt = inp["page_table"].to(dev)
@@ -418,7 +435,8 @@ def run_append(args):
     call = [ctypes.byref(d)] + [vp(t.data_ptr()) for t in (x, Wd, Wr, pt, before, kv)] + \
         ([vp(sc.data_ptr())] if sc is not None else []) + \
         [vp(ws.data_ptr()), ctypes.c_size_t(wsb), vp(stream.cuda_stream)]
-    entry = lib.mla_cache_append_fp8 if sc is not None else lib.mla_cache_append
+    entry = (lib.mla_cache_append_fp8 if args.kv_fp8 else
+             lib.mla_cache_append_mxfp4 if args.kv_mxfp4 else lib.mla_cache_append)
     for _ in range(args.warmup):
         entry(*call)
     hip = Hip()
@@ -432,14 +450,16 @@ def run_append(args):
     hip.L.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     us = hip.ms(e0, e1) * 1e3 / args.steps
-    row = (d_c + 2 * d_R + 4) if sc is not None else 2 * (d_c + d_R)
+    row = ((d_c + 2 * d_R + 4) if args.kv_fp8 else
+           (d_c // 2 + 2 * d_R + d_c // 32) if args.kv_mxfp4 else 2 * (d_c + d_R))
     nbytes = 2 * (d_c + d_R) * hidden + 2 * B * T * hidden + B * T * row
     return {"metric": "MLA cache append (c_KV = x W_DKV, RoPE(x W_KR)) per call",
             "value": round(us, 3), "unit": "us", "higher_is_better": False,
             "steps": args.steps, "warmup": args.warmup,
             "config": {"workload": cfg["name"], "batch": B, "new_tokens_per_seq": T,
                        "hidden": hidden, "d_latent": d_c, "d_rope": d_R,
-                       "kv_cache": "fp8" if sc is not None else "bf16"},
+                       "kv_cache": "fp8" if args.kv_fp8 else "mxfp4" if args.kv_mxfp4
+                       else "bf16"},
             "gbps": round(nbytes / us / 1e3, 1),
             "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -500,6 +520,9 @@ def main():
                     "instead of the decode")
     ap.add_argument("--kv-fp8", action="store_true", help="decode over an FP8 copy of the "
                     "cache with per-token scales")
+    ap.add_argument("--kv-mxfp4", action="store_true", help="decode over a synthetic MXFP4 "
+                    "cache (E2M1 codes, an E8M0 scale per 32 elements) of the workload's "
+                    "geometry; MHA2MLA widths (--workload 5)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all-workloads", action="store_true", help="one JSON line for each of "
                     "the five workloads instead of one for --workload")
