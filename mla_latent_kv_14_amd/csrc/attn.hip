@@ -723,7 +723,6 @@ constexpr int H = 32, DC = 64, DR = 8, DK = DC + DR, ROWB = DK * 2;
 constexpr int NBUF = 4;
 constexpr int TT = kPage;  // tokens per tile: one page
 using Tile = PagedTile<TT, ROWB>;
-constexpr int IPW = Tile::INSTR;  // the wave issues the whole tile
 constexpr float kRescale = 64.f;  // log2 headroom before the running max must move
 // FP8 cache: a token row is [c_KV as FP8 e4m3 (64 bytes) | k_R bf16 (16 bytes)], 80 bytes,
 // and each token has an fp32 power-of-two scale in a separate array of the same page geometry.
@@ -796,6 +795,9 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
   constexpr int IPW = TileL::INSTR + (FP8 || MX ? 1 : 0);   // load instructions per tile
   // MXFP4: the ring, then the bf16 copy of the current tile's latent part
   constexpr int WAVE_LDS = NB * LB + (MX ? Tile::BYTES : 0);
+  // the plan for a quantised cache counts two work groups per CU (160 KiB of LDS)
+  static_assert(FMT == kKvBf16 || kGroupsPerCuFp8 * kAttnWavesMha2Mla * WAVE_LDS <= 160 * 1024,
+                "two work groups of a quantised cache must fit one CU's LDS");
   __shared__ __attribute__((aligned(1024))) char lds_tiles[kAttnWavesMha2Mla][WAVE_LDS];
   const float* sc8 = reinterpret_cast<const float*>(kv_scales);
   const unsigned char* sc4 = reinterpret_cast<const unsigned char*>(kv_scales);
