@@ -14,6 +14,12 @@ import workloads as W
 REL_L2 = 5e-3
 MAX_ABS = 2e-2
 LSE_ABS = 1e-2  # natural-log LSE, fp32 output
+# Beside those: the worst (b, h) row and the worst element against the output's own scale. The
+# output is bf16 (2^-9 relative rounding) and the path rounds q_abs, the softmax weights and the
+# split partials to bf16 on the way; the worst row measured 7.6e-3 and the worst element
+# 5.8e-3 of the largest |output| over the parity cases, so these hold with a margin of 2.5x.
+ROW_REL = 2e-2
+MAX_SHARE = 1.5e-2
 
 
 def need_gpu():
@@ -45,6 +51,23 @@ def errors(gpu, ref):
     return rel, mx
 
 
+def row_errors(gpu, ref):
+    """Per (b, h) row (the last axis is d_v): the worst row's relative L2 error (rows whose
+    reference norm is below 1e-3 of the median row norm are left out: their relative error is
+    not informative) and the worst element error as a share of the largest |reference|."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if not g.size:
+        return 0.0, 0.0
+    d = g.shape[-1]
+    g2, r2 = g.reshape(-1, d), r.reshape(-1, d)
+    rn = np.linalg.norm(r2, axis=1)
+    keep = rn > 1e-3 * max(np.median(rn), 1e-300)
+    row = np.linalg.norm(g2 - r2, axis=1)[keep] / rn[keep]
+    worst_row = float(row.max()) if row.size else 0.0
+    return worst_row, float(np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-300))
+
+
 def to_bf16_bits(a):
     """fp64 array -> uint16 bf16 bit patterns, rounded to nearest (for building the oracle's
     own copy of a cache from its fp64 rows)."""
@@ -71,8 +94,11 @@ def check_against_oracle(M, inp, pairs=None, units=0, label=""):
         lse = lse[idx[:, 0], idx[:, 1]]
     rel, mx = errors(out, ref)
     lerr = float(np.max(np.abs(lse - ref_lse)))
-    say(label, "rel_l2=%.3e max_abs=%.3e lse_err=%.3e" % (rel, mx, lerr))
+    worst_row, mx_share = row_errors(out, ref)
+    say(label, "rel_l2=%.3e max_abs=%.3e lse_err=%.3e worst (b,h) rel_l2=%.3e "
+        "max_abs/max|ref|=%.3e" % (rel, mx, lerr, worst_row, mx_share))
     assert np.all(np.isfinite(out))
+    assert worst_row <= ROW_REL and mx_share <= MAX_SHARE, (label, worst_row, mx_share)
     assert rel <= REL_L2, (label, rel)
     assert mx <= MAX_ABS, (label, mx)
     assert lerr <= LSE_ABS, (label, lerr)

@@ -2,8 +2,8 @@
 
 Small cases span several tiles, ragged tails (lengths around the 32- and 64-token tile edges)
 and many split plans; the five workloads run at full size in the launch configuration the
-benchmark times (num_units = 0), with every (b, h) compared except for the 1M-token
-workload, which compares a seeded sample of (b, h) pairs.
+benchmark times (num_units = 0), with every (b, h) compared. Each check also reports the worst
+(b, h) row's relative error and the worst element error against the largest output.
 """
 import numpy as np
 import pytest
@@ -102,12 +102,10 @@ def test_empty_sequence_gives_zero_and_neg_inf(M):
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_workload_full_size(M, cfg):
+    # every (b, h) of each workload, the 1M-token one included (a few seconds of the oracle on
+    # the host's cores)
     inp = W.config_inputs(cfg)
-    pairs = None
-    if cfg == 4:  # 1M tokens: a seeded sample of (b, h), every sequence, spread over heads
-        rng = np.random.default_rng(4)
-        pairs = [(b, int(h)) for b in range(inp["B"]) for h in rng.choice(inp["H"], 8, False)]
-    check_against_oracle(M, inp, pairs=pairs, label="workload %d %s" % (cfg, W.CONFIGS[cfg]["name"]))
+    check_against_oracle(M, inp, label="workload %d %s" % (cfg, W.CONFIGS[cfg]["name"]))
 
 
 # ---- several query tokens per sequence (the T newest tokens, causal among themselves)
