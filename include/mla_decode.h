@@ -38,8 +38,12 @@
  *   - with MLA_CHECK=1 in the environment, every decode entry point first validates
  *     seq_lens, the page-table entries the sequences use and (FP8 or MXFP4 cache) the scales
  *     of the slots they use on the device, synchronises the stream, and returns
- *     MLA_ERR_DEVICE_CHECK (with nothing else enqueued) when one is out of range. This
- *     debugging mode is the only case in which the library synchronises.
+ *     MLA_ERR_DEVICE_CHECK (with nothing else enqueued) when one is out of range.
+ *   - with MLA_LOG=1 in the environment, every decode entry point prints its work plan on
+ *     stderr: the split of the tile stream over plan units, copied back from the workspace
+ *     right after the plan is built (the stream is synchronised there), or, for the
+ *     decompressed branch, its grouping of sequences. These two debugging modes are the only
+ *     cases in which the library synchronises.
  *   - page-table entries at or past ceil(S_b / 64) and cache slots at or past S_b are never
  *     read into the result (they may hold anything, including NaN).
  */

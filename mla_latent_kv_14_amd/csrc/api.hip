@@ -104,6 +104,17 @@ bool check_mode() {
   return e && e[0] == '1' && e[1] == 0;
 }
 
+// MLA_LOG=1 in the environment: print each decode's work plan on stderr.
+bool log_mode() {
+  const char* e = getenv("MLA_LOG");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+const char* format_name(int kv_format) {
+  return kv_format == mla::kKvFp8 ? "fp8" : (kv_format == mla::kKvMxfp4 ? "mxfp4" : "bf16");
+}
+
+
 struct Layout {
   size_t plan, q_abs, part_lse, part_o, total;
 };
@@ -147,6 +158,31 @@ mla_status_t hip_status(hipError_t e) {
   if (e == hipSuccess) return MLA_OK;
   snprintf(g_hip_err, sizeof g_hip_err, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
   return MLA_ERR_HIP;
+}
+
+// The plan the absorb kernel wrote into the workspace, copied back (the stream is synchronised)
+// and printed: the tile stream, each (virtual) sequence's first tile, and every unit's start.
+mla_status_t log_plan(const char* plan, int R, int T, int G, int TT, int kv_format,
+                      hipStream_t hs) {
+  std::vector<char> host(mla::plan_bytes(R, G));
+  mla_status_t st = hip_status(hipMemcpyAsync(host.data(), plan, host.size(),
+                                              hipMemcpyDeviceToHost, hs));
+  if (st == MLA_OK) st = hip_status(hipStreamSynchronize(hs));
+  if (st != MLA_OK) return st;
+  const mla::Plan* p = reinterpret_cast<const mla::Plan*>(host.data());
+  const int32_t* off = reinterpret_cast<const int32_t*>(p + 1);
+  const mla::UnitStart* u =
+      reinterpret_cast<const mla::UnitStart*>(host.data() + mla::plan_units_offset(R));
+  fprintf(stderr,
+          "mla_decode plan: %d sequences x %d query tokens, %d tiles of %d tokens, %d units "
+          "of up to %d tiles, %s cache\n",
+          R / T, T, p->total, TT, p->groups, p->per, format_name(kv_format));
+  for (int v = 0; v < R; ++v)
+    fprintf(stderr, "  row %d: tiles %d..%d\n", v, off[v], (v + 1 < R ? off[v + 1] : p->total) - 1);
+  for (int g = 0; g < G; ++g)
+    fprintf(stderr, "  unit %d: row %d tile %d of %d (length %d, page %d), %d tiles\n", g, u[g].b,
+            u[g].j, u[g].nj, u[g].S, u[g].page, u[g].n);
+  return MLA_OK;
 }
 
 }  // namespace
@@ -225,6 +261,10 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
                                                 : 1.0f / sqrtf((float)(s.DN + s.DR));
   const float scale_log2 = scale * mla::kLog2e;
   if (prefill) {
+    if (log_mode())
+      fprintf(stderr,
+              "mla_decode: decompressed branch, %d sequences x %d query tokens, groups of %d "
+              "sequences\n", B, T, PL.group);
     // stage events: 0/1 and 4/5 mark one point each (no absorb or combine kernel), 2/3 bracket
     // the branch's kernels
     auto record = [&](int k) -> mla_status_t {
@@ -256,6 +296,8 @@ mla_status_t decode_call(const mla_dims_t* dims, int hidden, const void* q_nope,
   st = hip_status(mla::launch_absorb(s.shape, q_nope, W_UK, ws + L.q_abs, R, s.H, seq_lens,
                                      page_table, mp, T, G, ws + L.plan, ctx(0)));
   if (st != MLA_OK) return st;
+  if (log_mode() && (st = log_plan(ws + L.plan, R, T, G, s.TT, kv_format, hs)) != MLA_OK)
+    return st;
   st = hip_status(mla::launch_attention(s.shape, ws + L.q_abs, q_rope, kv_pages, page_table,
                                         seq_lens, R, mp, T, dims->num_pages, ws + L.plan, G,
                                         scale_log2, ws + L.part_o, (float*)(ws + L.part_lse),

@@ -143,3 +143,44 @@ def test_timed_entry_point(M, dims):
     assert hip.ms(ev[2], ev[3]) > 0
     for e in ev:
         hip.destroy(e)
+
+
+def test_log_mode_prints_the_plan(M):
+    # MLA_LOG=1: the plan the absorb kernel built, copied back and printed on stderr. Lengths
+    # 100, 5 and 300 make 4 + 1 + 10 = 15 tiles of 32 tokens; five units take 3 tiles each,
+    # unit g starting at tile 3g, across sequence boundaries
+    import os
+    import re
+    import tempfile
+    inp = W.make_inputs(3, 128, 128, 512, 64, 128, [100, 5, 300], 61)
+    d = to_dev(inp)
+    say("MLA_LOG plan print")
+    os.environ["MLA_LOG"] = "1"
+    with tempfile.TemporaryFile() as f:
+        saved = os.dup(2)
+        os.dup2(f.fileno(), 2)
+        try:
+            M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], d["kv_pages"],
+                     d["page_table"], d["seq_lens"], num_units=5)
+            torch.cuda.synchronize()
+        finally:
+            os.dup2(saved, 2)
+            os.close(saved)
+            del os.environ["MLA_LOG"]
+        f.seek(0)
+        text = f.read().decode()
+    head = re.search(r"mla_decode plan: (\d+) sequences x (\d+) query tokens, (\d+) tiles of "
+                     r"(\d+) tokens, (\d+) units of up to (\d+) tiles, bf16 cache", text)
+    assert head, text[:500]
+    assert [int(x) for x in head.groups()] == [3, 1, 15, 32, 5, 3]
+    rows = [tuple(map(int, m)) for m in re.findall(r"row (\d+): tiles (-?\d+)\.\.(-?\d+)", text)]
+    assert rows == [(0, 0, 3), (1, 4, 4), (2, 5, 14)]
+    units = [tuple(map(int, m)) for m in re.findall(
+        r"unit (\d+): row (\d+) tile (\d+) of (\d+) \(length (\d+), page (-?\d+)\), (\d+) tiles",
+        text)]
+    assert len(units) == 5
+    first = {r: a for r, a, _ in rows}
+    for g, row, j, nj, S, page, n in units:
+        assert first[row] + j == 3 * g and n == 3, units
+        assert S == [100, 5, 300][row] and nj == -(-S // 32)
+        assert page == int(inp["page_table"][row, j * 32 // 64])
