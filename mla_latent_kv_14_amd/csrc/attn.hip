@@ -620,7 +620,7 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
           // Normalise and write this wave's block of the segment's partial, staged in the
           // bytes of tile r that only this wave read (its 128 FP8 columns of each 640-byte row,
           // 4 KiB): 32 heads x 64 columns per pass, head 32mb + t of the pass in row t, then
-          // written as whole 128-byte rows. Within a row the 8-byte unit u (four columns) sits
+          // written as whole 128-byte rows (device scope). Within a row the 8-byte unit u sits
           // at u ^ 2((t >> 1) & 7): the 64 lanes of a write hit every bank twice, and 16-byte
           // pieces stay whole for the read-back.
           MLA_LDS char* stg = tiles + (r % NBUF) * LB + 128 * vw;
@@ -649,17 +649,18 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
               for (int q4 = 0; q4 < 4; ++q4) {  // 32 rows x 8 pieces of 16 bytes
                 const int q = q4 * 64 + lane_e, row = q >> 3, piece = q & 7;
                 const int rsw = 2 * ((row >> 1) & 7);
-                *reinterpret_cast<u32x4*>(po + (size_t)(32 * mb + row) * DC + 64 * half +
-                                          piece * 8) =
+                store_16_device_scope(
+                    po, 2 * ((32 * mb + row) * DC + 64 * half + piece * 8),
                     *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * ROWB8 +
-                                                            8 * ((2 * piece) ^ rsw));
+                                                            8 * ((2 * piece) ^ rsw)));
               }
             }
           }
         } else if (k == seg - 1) {
           // Normalise and write this wave's block of the segment's partial. It is staged, 32
           // heads at a time, in the bytes of tile r that only this wave read (256 bytes at
-          // 256vw of each 1152-byte row), then written as whole 256-byte rows.
+          // 256vw of each 1152-byte row), then written as whole 256-byte rows at device scope
+          // (the combine reads them from other XCDs).
           MLA_LDS char* stg = tiles + (r % NBUF) * LB + 256 * vw;
           // (the slot and lane pass through empty asm so that the store addresses are formed
           // here, not kept in registers through the whole segment)
@@ -690,9 +691,9 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
             for (int q8 = 0; q8 < 8; ++q8) {  // 32 rows x 16 pieces of 16 bytes
               const int q = q8 * 64 + lane_e, row = q >> 4, piece = q & 15;
               const int rsw = 2 * ((row >> 1) & 7);
-              *reinterpret_cast<u32x4*>(po + (size_t)(32 * mb + row) * DC + piece * 8) =
-                  *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * ROWB +
-                                                          8 * ((2 * piece) ^ rsw));
+              store_16_device_scope(po, 2 * ((32 * mb + row) * DC + piece * 8),
+                                    *reinterpret_cast<const MLA_LDS u32x4*>(
+                                        stg + row * ROWB + 8 * ((2 * piece) ^ rsw)));
             }
           }
         }
@@ -1049,7 +1050,8 @@ attn_mha2mla_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restri
         const float ih = __shfl(il, h, 64);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          po[(size_t)h * DC + 32 * nb + t32] = bf16_bits((__bf16)(acc[nb][r] * ih));
+          store_2_device_scope(po, 2 * (h * DC + 32 * nb + t32),
+                               bf16_bits((__bf16)(acc[nb][r] * ih)));
       }
       seg_start = true;
     }

@@ -68,6 +68,24 @@ __device__ __forceinline__ void load_lds_4(const void* base, uint32_t off, MLA_L
   asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 
+// 16-byte store at device scope (cache policy SC1): the line goes through this XCD's L2 to
+// memory as it is stored instead of staying dirty there until the write-back that ends the
+// kernel. Meant for a buffer that only the next kernel reads, from other XCDs (the split
+// partials): the producer no longer ends on a burst of write-backs. base + byte_off is the
+// address; the range check of the buffer descriptor is left wide open (2^31 - 1 bytes).
+constexpr int kCacheSc1 = 16;  // the SC1 bit of a buffer instruction's cache-policy operand
+__device__ __forceinline__ void store_16_device_scope(void* base, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      v, __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000), (int)byte_off, 0,
+      kCacheSc1);
+}
+// The same for one 16-bit element (the coalescing of a wave's 64 lanes is unchanged).
+__device__ __forceinline__ void store_2_device_scope(void* base, uint32_t byte_off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(
+      v, __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000), (int)byte_off, 0,
+      kCacheSc1);
+}
+
 // Work-group barrier for LDS traffic only: waits for this wave's LDS operations, not for its
 // outstanding global loads (the prefetched tiles stay in flight across the barrier).
 __device__ __forceinline__ void block_sync() {

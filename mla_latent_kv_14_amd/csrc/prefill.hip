@@ -208,13 +208,16 @@ decompress_kernel(const char* __restrict__ kv, const int32_t* __restrict__ page_
   }
   uint16_t* const dst = (part == 0 ? kbuf : vbuf) + ((size_t)sl * H + h) * smax * width;
   const int cl = lane & 7;  // 16-byte chunk of the row: columns mw + 8cl .. +8
+  // Written non-temporally: the attention kernel reads each row once, later, and streaming
+  // stores leave the cache to the latent tiles still being decompressed.
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = 8 * i + (lane >> 3);
     const int t = t0 + nw + row;
     const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(stg + row * 128 + 16 * (cl ^ (row & 7)));
     if (t < S && mw + 8 * cl + 8 <= width)
-      *reinterpret_cast<u32x4*>(dst + (size_t)t * width + mw + 8 * cl) = v;
+      __builtin_nontemporal_store(v,
+                                  reinterpret_cast<u32x4*>(dst + (size_t)t * width + mw + 8 * cl));
   }
 }
 
