@@ -128,6 +128,64 @@ __device__ __forceinline__ void wait_tiles(int after) {
   else wait_vmcnt<S>();
 }
 
+// The absorbed query of one head as hi + lo, two FP8 (e4m3) parts for the block-scaled MFMA.
+// raw holds this lane's 128 bf16 elements (chunk j, piece p: elements 128j + 32g4 + 8p .. +8);
+// the head's other elements sit in lanes hl + 16, hl + 32 and hl + 48. The hi scale 2^X puts
+// the head's largest |q| in [128, 256) (X = floor(log2 max) - 7); hi = RNE(q / 2^X), and lo =
+// RNE((q / 2^X - hi) * 16) at scale 2^(X - 4). A bf16 q has 8 significant bits and each part
+// keeps 4, so hi + lo is q exactly unless q / 2^X lies below the e4m3 normal range (q below
+// about 2^-13 of the head's largest). Codes: qsc[0] for hi, qsc[1] for lo.
+__device__ __forceinline__ void split_query_fp8(const u32x4 (&raw)[4][4], i32x8 (&qh)[4],
+                                                i32x8 (&ql)[4], int (&qsc)[2]) {
+  float am = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = raw[j][p][e];
+        am = fmaxf(am, fmaxf(fabsf(__builtin_bit_cast(float, w << 16)),
+                             fabsf(__builtin_bit_cast(float, w & 0xffff0000u))));
+      }
+  am = rows4_max(am);
+  int ex = 0;
+  (void)frexpf(am, &ex);  // am = f 2^ex, f in [0.5, 1): floor(log2 am) = ex - 1
+  const int chi = am > 0.f ? min(max(ex + 119, 0), 247) : 127;  // X + 127, X = ex - 8
+  const int clo = max(chi - 4, 0);
+  const float inv = __builtin_bit_cast(float, (uint32_t)(254 - chi) << 23);        // 2^-X
+  const float lmul = __builtin_bit_cast(float, (uint32_t)(127 + chi - clo) << 23);  // 2^(chi-clo)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int hw[8] = {0, 0, 0, 0, 0, 0, 0, 0}, lw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // elements 8p + 2e and 8p + 2e + 1 (raw word e of piece p) become bytes 2(e & 1) and
+    // 2(e & 1) + 1 of word 2p + e/2
+    auto split2 = [&](uint32_t w, int& h, int& l, auto sel) {
+      const float x0 = __builtin_bit_cast(float, w << 16) * inv;
+      const float x1 = __builtin_bit_cast(float, w & 0xffff0000u) * inv;
+      h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, h, decltype(sel)::value);
+      const f32x2 hv = __builtin_amdgcn_cvt_pk_f32_fp8(h, decltype(sel)::value);
+      l = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - hv[0]) * lmul, (x1 - hv[1]) * lmul, l,
+                                          decltype(sel)::value);
+    };
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int k = 2 * p + e2;
+        split2(raw[j][p][2 * e2], hw[k], lw[k], std::false_type());
+        split2(raw[j][p][2 * e2 + 1], hw[k], lw[k], std::true_type());
+      }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      qh[j][k] = hw[k];
+      ql[j][k] = lw[k];
+    }
+  }
+  qsc[0] = chi;
+  qsc[1] = clo;
+}
+
 // FP8 e4m3 -> bf16, 8 values from two words (bytes 0..7 in order), times 2^(exponent of sc)
 __device__ __forceinline__ bf16x8 cvt_fp8x8(uint32_t w0, uint32_t w1, float sc) {
   const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
@@ -181,17 +239,17 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
     // score operand (16x16x32, A = tile rows): token row 16tb + hl, chunk 4s + g4 of step s;
     // with the row swizzle, step s sits at ko[tb][s & 1] + 128 * (s >> 1) (RoPE steps included)
     uint32_t ko[2][2];
-    // FP8: latent step s reads the 8 bytes at ko8[tb][s & 3] + 128 * (s >> 2) (bytes 32s + 8g4
-    // of the row), RoPE step 16 + q the 16 bytes at kr8[tb][q]
-    uint32_t ko8[2][4], kr8[2][2];
+    // FP8: the operand of the block-scaled 16x16x128 MFMA over latent chunk j (A = tile rows:
+    // token row 16tb + hl, bytes 128j + 32g4 .. +32 of its latent) is the two 16-byte pieces
+    // at ka8[tb][0..1] + 128j; RoPE step 16 + q reads the 16 bytes at kr8[tb][q]
+    uint32_t ka8[2][2], kr8[2][2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       const int r = 16 * tb + hl;
       if constexpr (FP8) {
         const int sw = Tile8::swz(r);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          ko8[tb][q] = r * ROWB8 + 16 * ((2 * q + (g4 >> 1)) ^ sw) + 8 * (g4 & 1);
+        for (int p = 0; p < 2; ++p) ka8[tb][p] = r * ROWB8 + 16 * ((2 * g4 + p) ^ sw);
 #pragma unroll
         for (int q = 0; q < 2; ++q) kr8[tb][q] = r * ROWB8 + DC + 16 * ((4 * q + g4) ^ sw);
       } else {
@@ -201,15 +259,36 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
       }
     }
     bf16x8 qf[KST];
+    // FP8: the absorbed query of head hl as qh + ql, two FP8 (e4m3) parts with one E8M0 scale
+    // each (codes qsc[0], qsc[1]), in the B-operand layout of the block-scaled MFMA (lane: head
+    // hl, bytes 32g4 .. +32 of each 128-wide chunk j); the RoPE steps stay bf16 in qf[16..17]
+    i32x8 qh[4], ql[4];
+    int qsc[2];
     auto load_queries = [&](int b) {  // this wave's 16 queries, loads completed here
-      const uint16_t* qa = q_abs + ((size_t)b * H + head) * DC + 8 * g4;
-      const uint16_t* qr = q_rope + ((size_t)b * H + head) * DR + 8 * g4;
+      if constexpr (FP8) {
+        const uint16_t* qa = q_abs + ((size_t)b * H + head) * DC + 32 * g4;
+        const uint16_t* qr = q_rope + ((size_t)b * H + head) * DR + 8 * g4;
+        u32x4 raw[4][4];  // chunk j, piece p: elements 128j + 32g4 + 8p .. +8
 #pragma unroll
-      for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qa + 32 * s);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) qf[16 + s] = *reinterpret_cast<const bf16x8*>(qr + 32 * s);
+          for (int p = 0; p < 4; ++p)
+            raw[j][p] = *reinterpret_cast<const u32x4*>(qa + 128 * j + 8 * p);
 #pragma unroll
-      for (int s = 0; s < KST; ++s) settle(qf[s]);
+        for (int s = 0; s < 2; ++s) qf[16 + s] = *reinterpret_cast<const bf16x8*>(qr + 32 * s);
+        split_query_fp8(raw, qh, ql, qsc);
+#pragma unroll
+        for (int s = 16; s < KST; ++s) settle(qf[s]);
+      } else {
+        const uint16_t* qa = q_abs + ((size_t)b * H + head) * DC + 8 * g4;
+        const uint16_t* qr = q_rope + ((size_t)b * H + head) * DR + 8 * g4;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qa + 32 * s);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) qf[16 + s] = *reinterpret_cast<const bf16x8*>(qr + 32 * s);
+#pragma unroll
+        for (int s = 0; s < KST; ++s) settle(qf[s]);
+      }
     };
     load_queries(c0.b);
     block_sync_tagged<0>();  // tile 0 landed
@@ -227,51 +306,65 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
         // steps). Operand reads run one half-block (9 steps) ahead of the MFMAs, and on tiles
         // whose reference max is already set the weights of block 0 are formed while block 1's
         // MFMAs run (scheduling fences and groups keep that order).
-        // bf16: the operands as read. FP8: latent steps keep their 8 bytes in words 0 and 1
-        // (converted right before their MFMA, with the token's scale), RoPE steps are bf16.
-        using KOp = typename std::conditional<FP8, u32x4, bf16x8>::type;
-        KOp kop[2][9];
-        // FP8: the scale of this lane's operand token per block (sct), and the scales of its
-        // weight tokens 16tb + 4g4 + e (scw), read first so that their latency is spent here.
-        // They multiply bf16 values exactly: a scale is a power of two by the cache's contract.
-        float sct[2] = {1.f, 1.f};
+        // bf16: the operands as read, nine steps of 16x16x32 per half-block. FP8: half h of a
+        // block is latent chunks 2h and 2h+1 (32 bytes a lane each), which feed the
+        // block-scaled 16x16x128 MFMA as stored, once against qh and once against ql, and
+        // RoPE step h (bf16).
+        struct Op8 {
+          i32x8 a[2];
+          u32x4 r;
+        };
+        using KOp = typename std::conditional<FP8, Op8, bf16x8>::type;
+        KOp kop[2][FP8 ? 1 : 9];
+        // FP8: the scale of this lane's operand token per block (sct) as an E8M0 code (tokc:
+        // its exponent field), and the scales of its weight tokens 16tb + 4g4 + e (scw), read
+        // first so that their latency is spent here. They multiply exactly: a scale is a power
+        // of two by the cache's contract.
+        int tokc[2] = {127, 127};
         f32x4 scw[2];
         if constexpr (FP8) {
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
-            sct[tb] = *reinterpret_cast<const MLA_LDS float*>(kb + Tile8::BYTES +
-                                                              4 * (16 * tb + hl));
+            const float sct = *reinterpret_cast<const MLA_LDS float*>(kb + Tile8::BYTES +
+                                                                      4 * (16 * tb + hl));
+            tokc[tb] = (int)((__builtin_bit_cast(uint32_t, sct) >> 23) & 0xff);
             scw[tb] = *reinterpret_cast<const MLA_LDS f32x4*>(kb + Tile8::BYTES +
                                                               4 * (16 * tb + 4 * g4));
           }
         }
         auto read_half = [&](KOp* dst, int tb, int s0) {
+          if constexpr (FP8) {
+            const int h = s0 / 9;
 #pragma unroll
-          for (int i = 0; i < 9; ++i) {
-            const int s = s0 + i;
-            if constexpr (FP8) {
-              if (s < 16) {
-                const u32x2 w = *reinterpret_cast<const MLA_LDS u32x2*>(
-                    kb + ko8[tb][s & 3] + 128 * (s >> 2));
-                dst[i][0] = w[0];
-                dst[i][1] = w[1];
-              } else {
-                dst[i] = *reinterpret_cast<const MLA_LDS u32x4*>(kb + kr8[tb][s - 16]);
-              }
-            } else {
+            for (int i = 0; i < 2; ++i) {
+              const uint32_t o = 128 * (2 * h + i);
+              const u32x4 p0 = *reinterpret_cast<const MLA_LDS u32x4*>(kb + ka8[tb][0] + o);
+              const u32x4 p1 = *reinterpret_cast<const MLA_LDS u32x4*>(kb + ka8[tb][1] + o);
+              dst[0].a[i] =
+                  __builtin_bit_cast(i32x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            dst[0].r = *reinterpret_cast<const MLA_LDS u32x4*>(kb + kr8[tb][h]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 9; ++i) {
+              const int s = s0 + i;
               dst[i] = lds_read_b128(kb, ko[tb][s & 1] + 128 * (s >> 1));
             }
           }
         };
         auto mfma_half = [&](f32x4* c, const KOp* src, int s0, int tb) {
+          if constexpr (FP8) {
+            const int h = s0 / 9;
 #pragma unroll
-          for (int i = 0; i < 9; ++i) {
-            const int s = s0 + i;
-            if constexpr (FP8) {
-              const bf16x8 op = s < 16 ? cvt_fp8x8(src[i][0], src[i][1], sct[tb])
-                                       : __builtin_bit_cast(bf16x8, src[i]);
-              c[s & 1] = mfma_16x16x32(op, qf[s], c[s & 1]);
-            } else {
+            for (int i = 0; i < 2; ++i) {
+              c[0] = mfma_scale_16x16x128_fp8(src[0].a[i], qh[2 * h + i], c[0], tokc[tb], qsc[0]);
+              c[1] = mfma_scale_16x16x128_fp8(src[0].a[i], ql[2 * h + i], c[1], tokc[tb], qsc[1]);
+            }
+            c[h] = mfma_16x16x32(__builtin_bit_cast(bf16x8, src[0].r), qf[16 + h], c[h]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 9; ++i) {
+              const int s = s0 + i;
               c[s & 1] = mfma_16x16x32(src[i], qf[s], c[s & 1]);
             }
           }
@@ -320,10 +413,11 @@ attn_deepseek_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restr
           scale_block(0, c0);
           weights_block(0);
           mfma_half(c1, kop[1], 9, 1);
+          constexpr int HALF_MFMA = FP8 ? 5 : 9, VALU_PER = FP8 ? 7 : 4;
 #pragma unroll
-          for (int i = 0; i < 9; ++i) {  // one MFMA, then a few VALU instructions of block 0
+          for (int i = 0; i < HALF_MFMA; ++i) {  // one MFMA, then some VALU work of block 0
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
           scale_block(1, c1);

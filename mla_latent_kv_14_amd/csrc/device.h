@@ -14,6 +14,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #define MLA_LDS __attribute__((address_space(3)))
 
@@ -30,6 +32,14 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 // 16x16x32: lane l holds A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16] (j < 8) and
 //           D[4*(l/16) + r][l%16] (r < 4).
+// Block-scaled 16x16x128 MFMA with FP8 (e4m3) A and B. A lane holds 32 bytes of row (A) or
+// column (B) lane % 16, in the same order for both; the result is as for mfma_16x16x32 (lane:
+// column lane % 16, rows 4(lane / 16) .. +4). sa and sb are E8M0 codes (operand times
+// 2^(code - 127)), the same in the four lanes of a row or column.
+__device__ __forceinline__ f32x4 mfma_scale_16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c, int sa,
+                                                          int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -207,7 +217,6 @@ __device__ __forceinline__ UnitStart* plan_units(Plan* p, int B) {
 // The unit record through the scalar path (written by an earlier kernel, read-only here), as
 // one 32-byte load: no field waits for a second round trip, whatever branches on which field.
 __device__ __forceinline__ UnitStart load_unit(const Plan* p, int B, int g) {
-  typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
   const i32x8 w = ld_uniform(reinterpret_cast<const i32x8*>(plan_units(p, B) + g));
   UnitStart u;
   u.b = w[0];

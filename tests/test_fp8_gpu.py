@@ -13,6 +13,14 @@ from tests.gpu_helpers import LSE_ABS, MAX_ABS, REL_L2, errors, need_gpu, say, t
 
 pytestmark = pytest.mark.gpu
 
+# DeepSeek widths, FP8 against the bf16 path on the same values: the scores differ by the
+# block-scaled FP8 MFMA's own accumulation (measured on the device: up to 8.4e-5 of the sum of
+# |products| of one 16x16x128 instruction, where fp32 summation would give about 1e-7). On the
+# case below that moved the outputs by 7-8e-4 (rel-L2) and the lse by 4.7e-4; the bounds leave
+# 2.5x and 4x of that, still below the oracle bounds the two paths each meet
+FP8_VS_BF16_REL = 2e-3
+FP8_VS_BF16_LSE = 2e-3
+
 M2 = dict(H=32, d_n=120, d_c=64, d_R=8, d_v=128)
 DS = dict(H=128, d_n=128, d_c=512, d_R=64, d_v=128)
 
@@ -170,9 +178,10 @@ def test_fp8_deepseek_query_tokens(M):
     check_fp8(M, inp, label="fp8 deepseek 2 query tokens")
 
 
-def test_fp8_deepseek_equals_bf16_on_the_same_values(M):
-    # the score operand is converted with the token's scale and the value operand unscaled with
-    # the scale moved into the weight: every product equals the bf16 path's, bit for bit
+def test_fp8_deepseek_close_to_bf16_on_the_same_values(M):
+    # the scores come from the block-scaled FP8 MFMA (cache bytes as stored, the token's scale as
+    # the block scale, the query split exactly into two FP8 parts), the values as in the bf16
+    # path: against the bf16 path on the dequantised values only the scores' rounding differs
     inp = _inp([300, 64, 1000, 33], 85, DS)
     kv8, sc = W.fp8_cache(inp, seed=3)
     deq = oracle.dequant_fp8_cache(kv8.numpy(), sc.numpy(), inp["d_c"])
@@ -185,7 +194,11 @@ def test_fp8_deepseek_equals_bf16_on_the_same_values(M):
         b, lb = M.decode(d["q_nope"], d["q_rope"], d["W_UK"], d["W_UV"], d["kv_pages"],
                          d["page_table"], d["seq_lens"], num_units=units, return_lse=True)
         torch.cuda.synchronize()
-        assert torch.equal(a, b) and torch.equal(la, lb), units
+        rel, mx = errors(a.float().cpu().numpy(), b.float().cpu().numpy())
+        lerr = (la - lb).abs().max().item()
+        say("fp8 deepseek vs bf16 path, units=%d: rel_l2=%.3e max_abs=%.3e lse=%.3e"
+            % (units, rel, mx, lerr))
+        assert rel <= FP8_VS_BF16_REL and lerr <= FP8_VS_BF16_LSE, (units, rel, lerr)
 
 
 def test_fp8_deepseek_empty_sequence_gives_zero_and_neg_inf(M):

@@ -12,8 +12,11 @@ This test compiles every HIP source to assembly with the library's own flags and
 MFMA's successors over fall-through and taken branches. An access to the MFMA's destination
 that is reached across a branch or a label must be at least as far from the MFMA as the
 compiler keeps the same kind of access (by MFMA opcode: a VALU or memory read, a write, an MFMA
-operand A/B) inside a block in the same compile. The scanner is itself checked on a planted
-case of the failing shape and on its padded form.
+operand A/B) inside a block in the same compile. Where the compiler marks a register
+`implicit-def` on a path (its value is undefined there, so nothing computed from a read of it
+on that path can matter), reads of that register on that path are not counted; writes still
+are (an MFMA result landing after them would overwrite them). The scanner is itself checked on
+a planted case of the failing shape, on its padded form, and on the implicit-def rule.
 """
 import concurrent.futures
 import os
@@ -41,10 +44,18 @@ def _regs(tok):
     return {int(m.group(1))} if m else set()
 
 
+_IMPLICIT = re.compile(r";\s*implicit-def:\s*\$vgpr(\d+)\s*$")
+
+
 def parse(text):
-    """Instructions as (opcode, operands); labels as ("LABEL", name); functions as ("FUNC",)."""
+    """Instructions as (opcode, operands); labels as ("LABEL", name); functions as ("FUNC",);
+    the compiler's `implicit-def: $vgprN` notes as ("UNDEF", ["vN"])."""
     ins, labels = [], {}
     for ln in text.split("\n"):
+        m = _IMPLICIT.search(ln)
+        if m and not ln.split(";")[0].strip():
+            ins.append(("UNDEF", ["v" + m.group(1)]))
+            continue
         s = ln.split(";")[0].strip()
         if not s:
             continue
@@ -83,8 +94,18 @@ def _kind(op, args, dst):
     return None
 
 
+def _read_regs(op, args):
+    """The VGPRs an instruction reads (an MFMA: its A and B operands)."""
+    if op.startswith("v_mfma"):
+        return set().union(set(), *[_regs(x) for x in args[1:3]])
+    vr = [_regs(x) for x in args]
+    if not vr:
+        return set()
+    return set().union(*vr) if _STORE.match(op) else set().union(set(), *vr[1:])
+
+
 def _ws(op, args):
-    if op in ("LABEL", "FUNC"):
+    if op in ("LABEL", "FUNC", "UNDEF"):
         return 0
     if op == "s_nop":
         return int(args[0], 0) + 1
@@ -107,6 +128,8 @@ def in_block_minima(ins):
             if o in ("LABEL", "FUNC") or o.startswith("s_cbranch") or o in ("s_branch",
                                                                              "s_endpgm"):
                 break
+            if o == "UNDEF":
+                continue
             k = _kind(o, a, dst)
             if k is not None:
                 key = (op, k)
@@ -123,22 +146,28 @@ def cross_branch_violations(ins, labels, mins):
     for i, (op, args) in enumerate(ins):
         if not op.startswith("v_mfma"):
             continue
-        dst = _regs(args[0])
         bound = {k: mins.get((op, k), FALLBACK[_shape(op)]) for k in ("read", "write", "mfma")}
         horizon = max(bound.values())
-        stack, seen = [(i + 1, 0, False)], set()
+        dst = _regs(args[0])
+        # (position, wait states so far, crossed a branch or label, registers undefined here)
+        stack, seen = [(i + 1, 0, False, frozenset())], set()
         while stack:
-            j, w, crossed = stack.pop()
-            if j >= len(ins) or w >= horizon or (j, w, crossed) in seen:
+            j, w, crossed, und = stack.pop()
+            if j >= len(ins) or w >= horizon or (j, w, crossed, und) in seen:
                 continue
-            seen.add((j, w, crossed))
+            seen.add((j, w, crossed, und))
             o, a = ins[j]
             if o in ("FUNC", "s_endpgm"):
                 continue
             if o == "LABEL":
-                stack.append((j + 1, w, True))
+                stack.append((j + 1, w, True, und))
+                continue
+            if o == "UNDEF":
+                stack.append((j + 1, w, crossed, und | (_regs(a[0]) & dst)))
                 continue
             k = _kind(o, a, dst)
+            if k in ("read", "mfma") and not ((_read_regs(o, a) & dst) - und):
+                k = None  # it reads only registers undefined on this path
             if k is not None:
                 # MFMA chains that take the destination back as srcC exactly are not accesses
                 if crossed and w < bound[k]:
@@ -147,11 +176,11 @@ def cross_branch_violations(ins, labels, mins):
             nw = w + _ws(o, a)
             if o.startswith("s_cbranch") or o == "s_branch":
                 if a and a[0] in labels:
-                    stack.append((labels[a[0]], nw, True))
+                    stack.append((labels[a[0]], nw, True, und))
                 if o != "s_branch":
-                    stack.append((j + 1, nw, True))
+                    stack.append((j + 1, nw, True, und))
                 continue
-            stack.append((j + 1, nw, crossed))
+            stack.append((j + 1, nw, crossed, und))
     return bad
 
 
@@ -212,6 +241,22 @@ def test_scanner_counts_the_mask_path():
     # edge is reported (moving the target past the mask would leave no violation)
     no_branch = PLANTED.replace("  s_cbranch_scc1 .LBB1_170\n", "")
     assert scan(no_branch) == []
+
+
+def test_scanner_drops_registers_undefined_on_the_path():
+    # the compiler's note that the accumulator's registers are undefined on the taken path ends
+    # the check for them there; a register the note leaves out is still checked
+    read = PLANTED.replace("  v_add_f32_e32 v74, v74, v78\n", "  v_add_f32_e32 v40, v74, v78\n")
+    assert len(scan(read)) == 1
+    undef = read.replace("  s_cbranch_scc1 .LBB1_170\n",
+                         "  ; implicit-def: $vgpr74\n  s_cbranch_scc1 .LBB1_170\n")
+    assert scan(undef) == []
+    other = read.replace("  s_cbranch_scc1 .LBB1_170\n",
+                         "  ; implicit-def: $vgpr75\n  s_cbranch_scc1 .LBB1_170\n")
+    assert len(scan(other)) == 1
+    # a write to an undefined register still has to wait for the MFMA's result
+    write = undef.replace("  v_add_f32_e32 v40, v74, v78\n", "  v_mov_b32_e32 v74, 0\n")
+    assert len(scan(write)) == 1
 
 
 @pytest.mark.skipif(HIPCC is None, reason="hipcc not found")
