@@ -192,9 +192,15 @@ mla_status_t mla_decode_timed(const mla_dims_t* dims, const void* q_nope, const 
  *              -126 <= e <= 127 (exponent-only, as in the microscaling formats). Other values
  *              are not reinterpreted: the result is then unspecified, and the MLA_CHECK mode
  *              reports them (MLA_ERR_DEVICE_CHECK). Slots no sequence uses may hold anything.
- * Each dequantised c_KV element (an E4M3 value times a power of two) is a bf16 value, formed
- * exactly, and the decode then runs as in mla_decode: the result is that of mla_decode on the
- * bf16 cache holding those values. Slots at or past S_b (bytes and scales) are never read
+ * Each dequantised c_KV element (an E4M3 value times a power of two) is a bf16 value. At the
+ * MHA2MLA widths the decode forms those values exactly and runs as in mla_decode: the result
+ * is that of mla_decode on the bf16 cache holding them, bit for bit. At the DeepSeek widths the
+ * latent part of each score is taken by the block-scaled FP8 matrix instruction straight from
+ * the bytes, with the token's scale as the block scale and the absorbed query split exactly
+ * into two E4M3 parts; that instruction's sum differs from an fp32 sum by up to about 1e-4 of
+ * the sum of |products|, so the result is mla_decode's on those values up to that rounding
+ * (within 1e-3 relative on the tested workloads), not bit for bit. Slots at or past S_b (bytes
+ * and scales) are never read
  * into the result. kv_scales must be 16-byte aligned and non-NULL; everything else, including
  * q_len, the workspace size and stage_events (NULL or six events, as for mla_decode_timed),
  * is as for mla_decode_timed.
