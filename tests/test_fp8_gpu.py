@@ -170,6 +170,24 @@ def test_fp8_deepseek_long_sequences_few_units(M, units):
               label="fp8 deepseek long")
 
 
+def test_fp8_deepseek_query_split_scales(M):
+    # the absorbed query is split into two FP8 parts with a per-head E8M0 scale chosen from the
+    # head's largest element (the split does not depend on the scale elsewhere): an all-zero
+    # query (no scale to take), queries scaled by 2^-60 and by 2^-122 (largest |q_abs| below
+    # 2^-120, where the hi scale clamps to its smallest code), and one left as drawn
+    inp = _inp([300, 200, 129, 64], 87, DS)
+    qn = inp["q_nope"].float()
+    qn[0] = 0.0
+    qn[1] *= 2.0 ** -60
+    qn[2] *= 2.0 ** -122
+    inp["q_nope"] = qn.to(torch.bfloat16)
+    qa = np.einsum("bhd,hdc->bhc", inp["q_nope"].float().numpy(), inp["W_UK"].float().numpy())
+    say("fp8 deepseek split scales: largest |q_abs| per sequence %s"
+        % ", ".join("%.1e" % float(np.abs(qa[b]).max()) for b in range(4)))
+    assert np.abs(qa[2]).max() < 2.0 ** -120  # the clamped case is the one exercised
+    check_fp8(M, inp, label="fp8 deepseek split scales")
+
+
 def test_fp8_deepseek_query_tokens(M):
     inp = _inp([70, 2, 200, 64 * 3 + 1], 83, DS)
     g = torch.Generator().manual_seed(84)
